@@ -1,0 +1,32 @@
+"""CPU oracle for the decoder-only transformer prefill (test infrastructure only).
+
+This package is the reference that the HIP library is checked against. It is NOT
+part of the product: only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import it. The library never calls it and must
+fail loudly rather than fall back to it.
+
+Every operation follows the plain definition given on the source pages, written
+out in numpy with float64 arithmetic on float32 tensors and one rounding to
+float32 at each operation's output (the "float64-accumulated f32" reference of
+the metalgemm page, Theorem 1 proof). Matrix products use numpy's matmul as a
+library primitive; nothing is blocked, fused or reordered beyond that.
+
+Parity pins: every function here is pinned by closed forms, invariants or brute
+force in tests/test_oracle_pins.py. End-to-end values on synthetic weights have
+no external fixture: beyond those invariants the whole-forward values are
+"parity unpinned" (the pages' printed end-to-end numbers need trained weights).
+"""
+from .forward import (  # noqa: F401
+    argmax,
+    attention,
+    attention_probs,
+    embed,
+    embed_scale,
+    forward,
+    gemm,
+    rmsnorm,
+    rope,
+    silu,
+    softcap,
+    swiglu,
+)

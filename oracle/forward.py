@@ -1,0 +1,265 @@
+"""Plain float64 reference of the prefill forward pass (test infrastructure only).
+
+Sources (page title, then the passage):
+  [fp]  "N7 · model/forward-parity" — intro (the op list: embedding lookup, decoder
+        stack of RMSNorm, RoPE, causal GQA attention, SwiGLU, residuals and
+        topology-selected norm placement, final norm, tied LM head, per-layer hidden
+        states, per-position logits) and Theorem 1 (hidden slots, argmax, logits).
+  [pi]  "pegainfer issue #878" — Description and Proposed Plan (scaled embedding,
+        layer map of local/global layers, final-logit softcap, id bounds check,
+        bf16-rounded embedding scale, non-finite values fail).
+  [mg]  "N9 · metalgemm" — Theorem 1 (Y = X·Wᵀ with W[out, in]; reference GEMM is a
+        float64-accumulated f32 triple loop; err/scale error model).
+
+Every function takes float32 arrays, computes in float64 and returns float32.
+Readings of points the pages leave open are listed in DESIGN.md ("Readings").
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+_ROW_CHUNK = 8192  # output rows of W widened to float64 at a time (bounds memory only)
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def _f32(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64).astype(np.float32)
+
+
+# ---------------------------------------------------------------- projections
+def gemm(X, W) -> np.ndarray:
+    """Y[p, o] = sum_i X[p, i] * W[o, i] — [mg] Theorem 1 (row-major W[out, in]).
+
+    Accumulated in float64 (numpy matmul), rounded once to float32. Output columns
+    are produced in independent chunks of W's rows; no sum is split.
+    """
+    X64 = _f64(X)
+    W = np.asarray(W)
+    out = np.empty(X64.shape[:-1] + (W.shape[0],), dtype=np.float32)
+    for o0 in range(0, W.shape[0], _ROW_CHUNK):
+        Wc = _f64(W[o0:o0 + _ROW_CHUNK])
+        out[..., o0:o0 + Wc.shape[0]] = _f32(X64 @ Wc.T)
+    return out
+
+
+# ---------------------------------------------------------------- embedding
+def embed_scale(mode: str, hidden: int) -> float:
+    """Embedding multiplier — [pi] Proposed Plan / Acceptance Criteria.
+
+    "bf16_sqrt_hidden": sqrt(hidden) rounded to the nearest bf16 value (ties to
+    even), the recorded bf16-rounded scale the issue asserts against. "none": 1.
+    """
+    if mode == "none":
+        return 1.0
+    if mode != "bf16_sqrt_hidden":
+        raise ValueError(f"embed_scale_mode {mode!r}")
+    r = math.sqrt(hidden)
+    m, e = math.frexp(r)              # r = m * 2**e, 0.5 <= m < 1
+    ulp = 2.0 ** (e - 8)              # bf16 keeps 8 significant bits
+    q = r / ulp
+    lo = math.floor(q)
+    frac = q - lo
+    if frac > 0.5 or (frac == 0.5 and lo % 2 == 1):
+        lo += 1
+    return lo * ulp
+
+
+def embed(E, ids, scale: float) -> np.ndarray:
+    """x0[b, t, :] = E[ids[b, t], :] * scale — [fp] intro (embedding lookup), [pi] Plan.
+
+    ids are bounds-checked against the embedding's rows first ([pi] Proposed Plan).
+    """
+    ids = np.asarray(ids)
+    V = np.asarray(E).shape[0]
+    if ids.size and (ids.min() < 0 or ids.max() >= V):
+        raise ValueError("token id outside [0, vocab)")
+    return _f32(_f64(np.asarray(E)[ids]) * scale)
+
+
+# ---------------------------------------------------------------- normalisation
+def rmsnorm(x, w, eps: float) -> np.ndarray:
+    """y_i = x_i * w_i / sqrt(mean_j x_j^2 + eps) over the last axis — [fp] intro, [mg] intro."""
+    x64 = _f64(x)
+    ms = np.mean(x64 * x64, axis=-1, keepdims=True)
+    return _f32(x64 / np.sqrt(ms + eps) * _f64(w))
+
+
+# ---------------------------------------------------------------- rotary embedding
+def rope(x, positions, theta: float) -> np.ndarray:
+    """Rotary position embedding of x[..., S, nheads, D] — [fp] intro (RoPE).
+
+    Rotate-half pairing (the HF convention the forward-parity oracle exports): for
+    k in [0, D/2) the pair (x_k, x_{k+D/2}) at position p turns by the angle
+    p * theta^(-2k/D).
+    """
+    x64 = _f64(x)
+    D = x64.shape[-1]
+    half = D // 2
+    k = np.arange(half, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * k / D)
+    ang = _f64(positions)[:, None] * inv_freq[None, :]          # [S, D/2]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    a, b = x64[..., :half], x64[..., half:]
+    return _f32(np.concatenate([a * c - b * s, a * s + b * c], axis=-1))
+
+
+# ---------------------------------------------------------------- attention
+def _visible(S: int, window: int) -> np.ndarray:
+    """mask[i, j]: key j visible from query i — causal, and i - j < window if window > 0.
+
+    [fp] intro (causal attention); [pi] Description: a 1024-token prompt is "exactly
+    the sliding window" and evicts nothing, so a window of W keeps keys with i - j < W.
+    """
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    m = j <= i
+    if window > 0:
+        m &= (i - j) < window
+    return m
+
+
+def attention_probs(q, k, window: int = 0) -> np.ndarray:
+    """Softmax weights p[b, h, i, j] (float64) of causal grouped-query attention.
+
+    q [B, S, Hq, D], k [B, S, Hkv, D]; query head h reads KV head h // (Hq / Hkv)
+    ([fp] intro: GQA). Scores are q·k / sqrt(D), softmax over visible keys.
+    """
+    q64, k64 = _f64(q), _f64(k)
+    B, S, Hq, D = q64.shape
+    Hkv = k64.shape[2]
+    if Hq % Hkv:
+        raise ValueError("n_heads must be a multiple of n_kv_heads")
+    group = Hq // Hkv
+    mask = _visible(S, window)
+    p = np.empty((B, Hq, S, S), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            s = (q64[b, :, h, :] @ k64[b, :, g, :].T) / math.sqrt(D)
+            s = np.where(mask, s, -np.inf)
+            m = np.max(s, axis=-1, keepdims=True)
+            e = np.where(mask, np.exp(s - m), 0.0)
+            p[b, h] = e / np.sum(e, axis=-1, keepdims=True)
+    return p
+
+
+def attention(q, k, v, window: int = 0) -> np.ndarray:
+    """o[b, i, h, :] = sum_j p[b, h, i, j] * v[b, j, h // group, :] — [fp] intro, [mg] Theorem 1.
+
+    Sequences of a batch never attend to each other. Returns float32 [B, S, Hq, D].
+    """
+    v64 = _f64(v)
+    B, S, Hkv, D = v64.shape
+    Hq = np.asarray(q).shape[2]
+    group = Hq // Hkv
+    out = np.empty((B, S, Hq, D), dtype=np.float32)
+    for b in range(B):
+        p = attention_probs(np.asarray(q)[b:b + 1], np.asarray(k)[b:b + 1], window)[0]
+        for h in range(Hq):
+            out[b, :, h, :] = _f32(p[h] @ v64[b, :, h // group, :])
+    return out
+
+
+# ---------------------------------------------------------------- feed-forward
+def silu(z) -> np.ndarray:
+    """silu(z) = z / (1 + e^-z), float64 in and out."""
+    z64 = _f64(z)
+    with np.errstate(over="ignore"):
+        return z64 / (1.0 + np.exp(-z64))
+
+
+def swiglu(g, u) -> np.ndarray:
+    """a = silu(g) * u — [fp] intro (SwiGLU FFN), [mg] intro."""
+    return _f32(silu(g) * _f64(u))
+
+
+# ---------------------------------------------------------------- head
+def softcap(z, cap: float) -> np.ndarray:
+    """z <- cap * tanh(z / cap) when cap > 0 — [pi] Description (final-logit softcap)."""
+    if cap == 0.0:
+        return np.asarray(z, dtype=np.float32)
+    if not (cap > 0.0):
+        raise ValueError("final_logit_softcap must be positive or 0 (off)")
+    return _f32(cap * np.tanh(_f64(z) / cap))
+
+
+def argmax(z) -> np.ndarray:
+    """Per-position argmax over the last axis, lowest index on ties ([fp] Theorem 1).
+
+    Non-finite values fail outright ([pi] Acceptance Criteria).
+    """
+    z = np.asarray(z)
+    if not np.all(np.isfinite(z)):
+        raise FloatingPointError("non-finite logits")
+    return np.argmax(z, axis=-1).astype(np.int32)
+
+
+# ---------------------------------------------------------------- whole forward
+def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = True):
+    """The prefill forward pass over a batch of prompts.
+
+    cfg: an object with the geometry fields n_layers, hidden, n_heads, n_kv_heads,
+    head_dim, ffn, vocab, rms_eps, rope_theta, embed_scale_mode,
+    final_logit_softcap, sliding_window, norm_placement and a kinds() method giving
+    "local"/"global" per layer (the parsed layer map, [pi] Proposed Plan).
+    weights: mapping name -> float32 array (names as documented on the workloads).
+    ids: int [B, S]; every row is an independent sequence at positions 0..S-1.
+
+    Returns dict(logits [B,S,V] f32, hidden [L+2,B,S,H] f32, argmax [B,S] i32).
+    Slots ([fp] Theorem 1): 0 = embedding, l+1 = after layer l, L+1 = final norm.
+    """
+    ids = np.asarray(ids)
+    B, S = ids.shape
+    H, Hq, Hkv, D = cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    L = cfg.n_layers
+    eps = cfg.rms_eps
+    sandwich = cfg.norm_placement == "sandwich"
+    if cfg.norm_placement not in ("pre", "sandwich"):
+        raise ValueError("norm_placement")
+    kinds = cfg.kinds()
+    positions = np.arange(S)
+
+    E = weights["embed"]
+    x = embed(E, ids, embed_scale(cfg.embed_scale_mode, H))            # [B, S, H]
+    hidden = np.empty((L + 2, B, S, H), dtype=np.float32) if want_hidden else None
+    if want_hidden:
+        hidden[0] = x
+
+    for l in range(L):
+        p = f"layers.{l}."
+        window = cfg.sliding_window if kinds[l] == "local" else 0
+        # attention sublayer
+        n = rmsnorm(x, weights[p + "attn_norm"], eps)
+        q = gemm(n, weights[p + "wq"]).reshape(B, S, Hq, D)
+        k = gemm(n, weights[p + "wk"]).reshape(B, S, Hkv, D)
+        v = gemm(n, weights[p + "wv"]).reshape(B, S, Hkv, D)
+        q = np.stack([rope(q[b], positions, cfg.rope_theta) for b in range(B)])
+        k = np.stack([rope(k[b], positions, cfg.rope_theta) for b in range(B)])
+        o = attention(q, k, v, window).reshape(B, S, Hq * D)
+        u = gemm(o, weights[p + "wo"])
+        if sandwich:
+            u = rmsnorm(u, weights[p + "post_attn_norm"], eps)
+        x = _f32(_f64(x) + _f64(u))
+        # feed-forward sublayer
+        n = rmsnorm(x, weights[p + "ffn_norm"], eps)
+        a = swiglu(gemm(n, weights[p + "w_gate"]), gemm(n, weights[p + "w_up"]))
+        d = gemm(a, weights[p + "w_down"])
+        if sandwich:
+            d = rmsnorm(d, weights[p + "post_ffn_norm"], eps)
+        x = _f32(_f64(x) + _f64(d))
+        if want_hidden:
+            hidden[l + 1] = x
+
+    h = rmsnorm(x, weights["final_norm"], eps)
+    if want_hidden:
+        hidden[L + 1] = h
+    z = softcap(gemm(h, E), cfg.final_logit_softcap)                    # tied head
+    out = {"argmax": argmax(z), "hidden": hidden}
+    out["logits"] = z if want_logits else None
+    return out

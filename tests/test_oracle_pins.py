@@ -1,0 +1,397 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test is chosen so that a plausible mistake in the oracle (a dropped term, a
+wrong sign or index, a transposed operand, a wrong pairing) fails it. None of them
+re-types the oracle's own formula: they use closed forms, exact rational
+arithmetic, invariants and special cases that reduce to something simpler.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import workloads as wl
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_values.json")))
+rng = np.random.default_rng(1234)
+
+
+# ------------------------------------------------------------------ GEMM
+def _exact_gemm(X, W):
+    P, K = X.shape
+    N = W.shape[0]
+    Y = np.empty((P, N), dtype=np.float64)
+    for p in range(P):
+        for o in range(N):
+            s = Fraction(0)
+            for i in range(K):
+                s += Fraction(float(X[p, i])) * Fraction(float(W[o, i]))
+            Y[p, o] = float(s)
+    return Y
+
+
+@pytest.mark.parametrize("P,K,N", [(1, 1, 1), (3, 5, 2), (8, 8, 8), (2, 7, 5)])
+def test_gemm_matches_exact_rational_sum(P, K, N):
+    X = rng.standard_normal((P, K)).astype(np.float32)
+    W = rng.standard_normal((N, K)).astype(np.float32)
+    exact = _exact_gemm(X, W)
+    got = oracle.gemm(X, W).astype(np.float64)
+    # one float32 rounding of the exact sum (plus at most a double-rounding ulp)
+    ulp = np.spacing(np.abs(exact).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= ulp)
+
+
+def test_gemm_integer_inputs_are_exact_and_not_transposed():
+    X = rng.integers(-4, 5, size=(3, 6)).astype(np.float32)
+    W = rng.integers(-4, 5, size=(4, 6)).astype(np.float32)
+    exact = _exact_gemm(X, W)
+    assert np.array_equal(oracle.gemm(X, W), exact.astype(np.float32))
+    assert oracle.gemm(X, W).shape == (3, 4)
+
+
+def test_gemm_identity_and_one_hot():
+    X = rng.standard_normal((5, 7)).astype(np.float32)
+    assert np.array_equal(oracle.gemm(X, np.eye(7, dtype=np.float32)), X)
+    W = rng.standard_normal((6, 7)).astype(np.float32)
+    onehot = np.zeros((1, 7), dtype=np.float32)
+    onehot[0, 3] = 1.0
+    assert np.array_equal(oracle.gemm(onehot, W)[0], W[:, 3])
+
+
+def test_gemm_err_over_scale_gate_on_page_shapes():
+    # the page's error model: err/scale = max|d| / max|ref| against a float64 product
+    bound = GOLD["gemm_err_over_scale_max"]["value"]
+    for P, K, N in GOLD["gemm_shapes_P_in_out"]["value"]:
+        X = rng.standard_normal((P, K)).astype(np.float32)
+        W = rng.standard_normal((N, K)).astype(np.float32)
+        ref = X.astype(np.float64) @ W.astype(np.float64).T
+        err = np.max(np.abs(oracle.gemm(X, W) - ref)) / np.max(np.abs(ref))
+        assert err < 1e-6 < bound
+
+
+# ------------------------------------------------------------------ RMSNorm
+def test_rmsnorm_hand_example_uses_mean_not_sum():
+    y = oracle.rmsnorm(np.array([[3.0, 4.0]], np.float32), np.ones(2, np.float32), 0.0)
+    ms = (9.0 + 16.0) / 2.0
+    assert np.allclose(y, [[3 / math.sqrt(ms), 4 / math.sqrt(ms)]], rtol=1e-7)
+
+
+def test_rmsnorm_constant_vector_closed_form():
+    c, eps, H = 3.0, 1e-5, 64
+    y = oracle.rmsnorm(np.full((2, H), c, np.float32), np.ones(H, np.float32), eps)
+    assert np.allclose(y, c / math.sqrt(c * c + eps), rtol=1e-7)
+    ms = c * c
+    assert math.isclose(float(np.mean(y.astype(np.float64) ** 2)), ms / (ms + eps), rel_tol=1e-6)
+
+
+def test_rmsnorm_gain_is_elementwise_and_scale_invariant():
+    x = rng.standard_normal((4, 32)).astype(np.float32)
+    w = rng.standard_normal(32).astype(np.float32)
+    one = oracle.rmsnorm(x, np.ones(32, np.float32), 1e-5)
+    assert np.allclose(oracle.rmsnorm(x, w, 1e-5), one * w, rtol=1e-6, atol=1e-7)
+    one0 = oracle.rmsnorm(x, np.ones(32, np.float32), 0.0)
+    assert np.allclose(oracle.rmsnorm(x * 1000.0, np.ones(32, np.float32), 0.0), one0, rtol=1e-6)
+    # with eps > 0 the output shrinks by sqrt(ms / (ms + eps)) per row
+    ms = np.mean(x.astype(np.float64) ** 2, -1, keepdims=True)
+    assert np.allclose(one, one0 * np.sqrt(ms / (ms + 1e-5)), rtol=1e-6)
+    # eps matters when the row is tiny: y -> x / sqrt(eps)
+    tiny = np.full((1, 8), 1e-6, np.float32)
+    assert np.allclose(oracle.rmsnorm(tiny, np.ones(8, np.float32), 1.0), 1e-6, rtol=1e-6)
+
+
+# ------------------------------------------------------------------ RoPE
+def test_rope_d2_turns_by_position_radians():
+    x = np.array([[[1.0, 0.0]]] * 4, np.float32)          # [S=4, heads=1, D=2]
+    y = oracle.rope(x, np.arange(4), 10000.0)
+    for p in range(4):
+        assert np.allclose(y[p, 0], [math.cos(p), math.sin(p)], atol=1e-7)
+
+
+def test_rope_rotate_half_pairing_and_frequency():
+    # D = 4: dim 1 pairs with dim 3 and turns at theta^(-2/4) = 1/100 rad per position
+    x = np.zeros((4, 1, 4), np.float32)
+    x[:, 0, 1] = 1.0
+    y = oracle.rope(x, np.arange(4), 10000.0)
+    p = 3
+    assert np.allclose(y[p, 0], [0.0, math.cos(0.03), 0.0, math.sin(0.03)], atol=1e-7)
+    # dim 0 pairs with dim 2 and turns at 1 rad per position
+    x = np.zeros((4, 1, 4), np.float32)
+    x[:, 0, 0] = 1.0
+    y = oracle.rope(x, np.arange(4), 10000.0)
+    assert np.allclose(y[2, 0], [math.cos(2), 0.0, math.sin(2), 0.0], atol=1e-7)
+
+
+def test_rope_preserves_pair_norms_and_is_identity_at_zero():
+    D = 64
+    x = rng.standard_normal((9, 3, D)).astype(np.float32)
+    y = oracle.rope(x, np.arange(9), 500000.0)
+    n_in = x[..., :32] ** 2 + x[..., 32:] ** 2
+    n_out = y[..., :32].astype(np.float64) ** 2 + y[..., 32:].astype(np.float64) ** 2
+    assert np.allclose(n_in, n_out, rtol=1e-5)
+    assert np.array_equal(y[0], x[0])
+
+
+def test_rope_scores_depend_only_on_relative_position():
+    D = 16
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    k = rng.standard_normal((1, 1, D)).astype(np.float32)
+
+    def at(v, p):
+        return oracle.rope(v, np.array([p]), 10000.0)[0, 0].astype(np.float64)
+
+    for m, n in [(5, 2), (9, 6), (3, 0), (40, 37)]:
+        assert math.isclose(at(q, m) @ at(k, n), at(q, m - n) @ k[0, 0].astype(np.float64), rel_tol=1e-5)
+
+
+# ------------------------------------------------------------------ attention
+def _qkv(B, S, Hq, Hkv, D):
+    q = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    return q, k, v
+
+
+def test_attention_first_position_returns_its_value_row():
+    q, k, v = _qkv(2, 7, 4, 2, 8)
+    o = oracle.attention(q, k, v)
+    for h in range(4):
+        assert np.allclose(o[:, 0, h], v[:, 0, h // 2], rtol=1e-6)
+    q1, k1, v1 = q[:, :1], k[:, :1], v[:, :1]
+    assert np.allclose(oracle.attention(q1, k1, v1)[:, 0, 3], v1[:, 0, 1], rtol=1e-6)
+
+
+def test_attention_two_key_closed_form_pins_the_scale():
+    D = 4
+    q = np.zeros((1, 2, 1, D), np.float32)
+    k = np.zeros((1, 2, 1, D), np.float32)
+    v = np.zeros((1, 2, 1, D), np.float32)
+    k[0, 1, 0, 0] = 1.0                       # k0 = 0, k1 = e0
+    q[0, 1, 0, 0] = 2.0 * math.log(3.0)       # s10 = 0, s11 = 2 ln3 / sqrt(4) = ln 3
+    v[0, 0, 0] = [1, 0, 0, 0]
+    v[0, 1, 0] = [0, 1, 0, 0]
+    o = oracle.attention(q, k, v)
+    assert np.allclose(o[0, 1, 0], [0.25, 0.75, 0, 0], atol=1e-7)
+
+
+def test_attention_probabilities_causal_rows_sum_to_one():
+    q, k, _ = _qkv(1, 11, 4, 2, 8)
+    p = oracle.attention_probs(q, k)
+    assert np.allclose(p.sum(-1), 1.0, atol=1e-12)
+    iu = np.triu_indices(11, 1)
+    assert np.all(p[0, :, iu[0], iu[1]] == 0.0)
+    pw = oracle.attention_probs(q, k, window=3)
+    assert np.allclose(pw.sum(-1), 1.0, atol=1e-12)
+    i, j = np.meshgrid(np.arange(11), np.arange(11), indexing="ij")
+    assert np.all(pw[0][:, (i - j) >= 3] == 0.0)
+    assert np.all(pw[0][:, (i - j < 3) & (j <= i)] > 0.0)
+
+
+def test_attention_zero_query_averages_visible_values():
+    _, k, v = _qkv(1, 6, 2, 1, 4)
+    q = np.zeros((1, 6, 2, 4), np.float32)
+    o = oracle.attention(q, k, v)
+    for i in range(6):
+        assert np.allclose(o[0, i, 1], v[0, :i + 1, 0].mean(0), rtol=1e-6)
+    ow = oracle.attention(q, k, v, window=2)
+    for i in range(1, 6):
+        assert np.allclose(ow[0, i, 0], v[0, i - 1:i + 1, 0].mean(0), rtol=1e-6)
+
+
+def test_attention_window_special_cases():
+    q, k, v = _qkv(1, 9, 2, 2, 8)
+    full = oracle.attention(q, k, v)
+    assert np.array_equal(oracle.attention(q, k, v, window=9), full)
+    assert np.array_equal(oracle.attention(q, k, v, window=100), full)
+    assert np.allclose(oracle.attention(q, k, v, window=1), v, rtol=1e-6)
+    assert not np.allclose(oracle.attention(q, k, v, window=4)[0, 8], full[0, 8])
+
+
+def test_attention_gqa_equals_mha_with_repeated_kv_heads():
+    q, k, v = _qkv(2, 8, 6, 2, 8)
+    gqa = oracle.attention(q, k, v)
+    mha = oracle.attention(q, np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2))
+    assert np.allclose(gqa, mha, rtol=1e-6, atol=1e-7)
+
+
+def test_attention_batch_rows_do_not_mix():
+    q, k, v = _qkv(3, 5, 2, 1, 4)
+    o = oracle.attention(q, k, v)
+    o1 = oracle.attention(q[1:2], k[1:2], v[1:2])
+    assert np.array_equal(o[1:2], o1)
+
+
+# ------------------------------------------------------------------ SwiGLU
+def test_silu_closed_forms():
+    s = oracle.silu(np.array([0.0, 1.0, -1.0, 40.0, -40.0]))
+    assert s[0] == 0.0
+    assert math.isclose(s[1], 1.0 / (1.0 + math.exp(-1.0)), rel_tol=1e-15)
+    assert math.isclose(s[2], -1.0 / (1.0 + math.exp(1.0)), rel_tol=1e-15)
+    assert math.isclose(s[3], 40.0, rel_tol=1e-15)
+    assert abs(s[4]) < 1e-15
+
+
+def test_swiglu_gate_and_up_are_not_interchangeable():
+    a = oracle.swiglu(np.array([1.0, 2.0, 0.0], np.float32), np.array([2.0, 1.0, 5.0], np.float32))
+    assert np.allclose(a, [2.0 / (1.0 + math.exp(-1.0)), 2.0 / (1.0 + math.exp(-2.0)), 0.0], rtol=1e-7)
+
+
+# ------------------------------------------------------------------ softcap / argmax
+def test_softcap_bounds_monotone_and_small_signal():
+    z = np.linspace(-200, 200, 4001).astype(np.float32)
+    c = oracle.softcap(z, 30.0)
+    assert np.all(np.abs(c) <= 30.0) and np.all(np.diff(c) >= 0)
+    small = np.array([1e-3, -2e-2, 0.5], np.float32)
+    assert np.all(np.abs(oracle.softcap(small, 30.0) - small) <= np.abs(small) ** 3 / (3 * 900) + 1e-8)
+    assert math.isclose(float(oracle.softcap(np.float32(30.0 * math.atanh(0.5)), 30.0)), 15.0, rel_tol=1e-6)
+    assert np.array_equal(oracle.softcap(z, 0.0), z)
+    with pytest.raises(ValueError):
+        oracle.softcap(z, -1.0)
+    with pytest.raises(ValueError):
+        oracle.softcap(z, float("nan"))
+
+
+def test_argmax_lowest_index_on_ties_and_nonfinite_fails():
+    z = np.array([[1.0, 3.0, 3.0, 2.0], [5.0, 5.0, 5.0, 5.0]], np.float32)
+    assert list(oracle.argmax(z)) == [1, 0]
+    with pytest.raises(FloatingPointError):
+        oracle.argmax(np.array([[1.0, np.nan]], np.float32))
+    with pytest.raises(FloatingPointError):
+        oracle.argmax(np.array([[1.0, np.inf]], np.float32))
+
+
+# ------------------------------------------------------------------ embedding
+def test_embed_scale_is_bf16_rounded_sqrt():
+    assert oracle.embed_scale("bf16_sqrt_hidden", 3840) == 62.0      # sqrt = 61.9677...
+    assert math.sqrt(3840) != 62.0
+    assert oracle.embed_scale("bf16_sqrt_hidden", 576) == 24.0       # exact square
+    assert oracle.embed_scale("bf16_sqrt_hidden", 257 ** 2) == 256.0  # tie -> even mantissa
+    assert oracle.embed_scale("bf16_sqrt_hidden", 259 ** 2) == 260.0  # tie -> even mantissa
+    assert oracle.embed_scale("bf16_sqrt_hidden", 2) == 1.4140625     # 1.41421... -> 1 + 53/128
+    assert oracle.embed_scale("none", 3840) == 1.0
+
+
+def test_embed_gathers_rows_scales_exactly_and_checks_ids():
+    E = rng.standard_normal((10, 6)).astype(np.float32)
+    E = (E.view(np.uint32) & 0xFFFF0000).view(np.float32)   # bf16-representable
+    ids = np.array([[3, 0, 9]])
+    x = oracle.embed(E, ids, 62.0)
+    assert np.array_equal(x[0], E[[3, 0, 9]] * np.float32(62.0))
+    for bad in ([[10]], [[-1]]):
+        with pytest.raises(ValueError):
+            oracle.embed(E, np.array(bad), 1.0)
+
+
+# ------------------------------------------------------------------ whole forward
+TINY = wl.TINY_F32
+
+
+def _weights(cfg, seed=7):
+    return {n: wl.LazyWeights(cfg, seed)[n] for n in wl.weight_shapes(cfg)}
+
+
+def test_forward_shapes_and_slot_convention():
+    w = _weights(TINY)
+    ids = wl.draw_ids(TINY)
+    out = oracle.forward(TINY, w, ids)
+    L, H, V = TINY.n_layers, TINY.hidden, TINY.vocab
+    assert out["hidden"].shape == (L + 2, 1, 16, H)
+    assert out["logits"].shape == (1, 16, V)
+    assert np.array_equal(out["hidden"][0], w["embed"][ids])
+    assert np.allclose(out["hidden"][L + 1], oracle.rmsnorm(out["hidden"][L], w["final_norm"], TINY.rms_eps))
+    assert np.array_equal(out["argmax"], np.argmax(out["logits"], -1))
+
+
+def test_forward_causal_prefix_invariance():
+    w = _weights(TINY)
+    ids = wl.draw_ids(TINY)
+    full = oracle.forward(TINY, w, ids)
+    for s in (1, 5, 11):
+        pre = oracle.forward(TINY, w, ids[:, :s])
+        assert np.allclose(pre["logits"], full["logits"][:, :s], rtol=1e-6, atol=1e-7)
+        assert np.allclose(pre["hidden"], full["hidden"][:, :, :s], rtol=1e-6, atol=1e-7)
+
+
+def test_forward_batch_rows_are_independent():
+    cfg = TINY.replace(batch=3)
+    w = _weights(cfg)
+    ids = wl.draw_ids(cfg)
+    full = oracle.forward(cfg, w, ids)
+    one = oracle.forward(cfg, w, ids[2:3])
+    assert np.allclose(one["logits"][0], full["logits"][2], rtol=1e-6, atol=1e-7)
+
+
+def test_forward_zero_layers_argmax_is_the_input_token():
+    cfg = TINY.replace(n_layers=0)
+    w = _weights(cfg)
+    ids = wl.draw_ids(cfg)
+    out = oracle.forward(cfg, w, ids)
+    # self-dot H*rms(e) ~ 1.28 dominates cross terms ~ N(0, 0.16^2) over 512 rows
+    assert np.array_equal(out["argmax"], ids)
+
+
+def test_forward_residual_passthrough_when_branches_vanish():
+    w = _weights(TINY)
+    for l in range(TINY.n_layers):
+        w[f"layers.{l}.wo"] = np.zeros_like(w[f"layers.{l}.wo"])
+        w[f"layers.{l}.w_down"] = np.zeros_like(w[f"layers.{l}.w_down"])
+    out = oracle.forward(TINY, w, wl.draw_ids(TINY))
+    for s in range(1, TINY.n_layers + 1):
+        assert np.array_equal(out["hidden"][s], out["hidden"][0])
+
+
+def test_forward_single_token_ignores_query_and_key_weights():
+    cfg = TINY.replace(seq=1)
+    w = _weights(cfg)
+    ids = wl.draw_ids(cfg)
+    a = oracle.forward(cfg, w, ids)
+    w2 = dict(w)
+    for l in range(cfg.n_layers):
+        w2[f"layers.{l}.wq"] = w[f"layers.{l}.wq"] * -3.0
+        w2[f"layers.{l}.wk"] = rng.standard_normal(w[f"layers.{l}.wk"].shape).astype(np.float32)
+    b = oracle.forward(cfg, w2, ids)
+    assert np.array_equal(a["logits"], b["logits"])
+
+
+def test_forward_sandwich_norm_cancels_branch_scale():
+    base = TINY.replace(rms_eps=1e-12)
+    sand = base.replace(norm_placement="sandwich")
+    ids = wl.draw_ids(base)
+    for cfg, invariant in ((sand, True), (base, False)):
+        w = _weights(cfg)
+        a = oracle.forward(cfg, w, ids)["logits"]
+        for l in range(cfg.n_layers):
+            w[f"layers.{l}.wo"] = w[f"layers.{l}.wo"] * 7.0
+            w[f"layers.{l}.w_down"] = w[f"layers.{l}.w_down"] * 7.0
+        b = oracle.forward(cfg, w, ids)["logits"]
+        assert np.allclose(a, b, rtol=1e-4, atol=1e-6) == invariant
+
+
+def test_forward_layer_map_and_window():
+    ids = wl.draw_ids(TINY)
+    w = _weights(TINY)
+    ref = oracle.forward(TINY, w, ids)["logits"]
+    glob = TINY.replace(sliding_window=4, layer_kind=("global", "global"))
+    assert np.array_equal(oracle.forward(glob, w, ids)["logits"], ref)
+    wide = TINY.replace(sliding_window=16, layer_kind=("local", "local"))
+    assert np.array_equal(oracle.forward(wide, w, ids)["logits"], ref)
+    narrow = TINY.replace(sliding_window=4, layer_kind=("local", "global"))
+    out = oracle.forward(narrow, w, ids)["logits"]
+    assert np.array_equal(out[:, :4], ref[:, :4])          # first W positions see everything
+    assert not np.allclose(out[:, 4:], ref[:, 4:])
+
+
+def test_forward_softcap_and_embed_scale_compose():
+    capped = TINY.replace(final_logit_softcap=2.0, embed_scale_mode="bf16_sqrt_hidden")
+    plain = TINY.replace(embed_scale_mode="bf16_sqrt_hidden")
+    w = _weights(TINY)
+    ids = wl.draw_ids(TINY)
+    a = oracle.forward(capped, w, ids)
+    b = oracle.forward(plain, w, ids)
+    assert np.array_equal(a["hidden"][0], w["embed"][ids] * np.float32(8.0))   # bf16(sqrt 64) = 8
+    assert np.allclose(a["logits"], 2.0 * np.tanh(b["logits"].astype(np.float64) / 2.0), rtol=1e-6, atol=1e-7)
+    assert np.all(np.abs(a["logits"]) < 2.0)
+    assert np.array_equal(a["argmax"], b["argmax"])
