@@ -1,0 +1,78 @@
+// Shared device helpers for the gfx950 kernels: element types, vector types,
+// conversions, wavefront reductions and the MFMA wrappers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fwdk {
+
+typedef uint16_t bf16_t;  // bf16 storage: the upper 16 bits of an IEEE binary32
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Round to nearest, ties to even (inputs here are finite or +-inf; a NaN input
+// stays a NaN because its payload bits keep the exponent all ones).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// Element type traits: load/store one value through fp32.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// Wavefront-wide reductions (64 lanes) through cross-lane shuffles.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// exp2 on the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// 1/x and 1/sqrt(x) on the hardware units (v_rcp_f32, v_rsq_f32).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// MFMA wrappers (CDNA4): D = A * B + C with fp32 accumulation.
+__device__ __forceinline__ floatx16_t mfma_32x32x16_bf16(const bf16x8_t& a, const bf16x8_t& b,
+                                                         const floatx16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4_t mfma_16x16x32_bf16(const bf16x8_t& a, const bf16x8_t& b,
+                                                        const floatx4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+}  // namespace fwdk

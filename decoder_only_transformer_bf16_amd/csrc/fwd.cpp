@@ -1,0 +1,509 @@
+// C-ABI implementation of libfwd.so: configuration checks, weight packing into
+// library-owned HBM, workspace, and the launch sequence of the prefill forward.
+// See include/fwd.h for the contract of every entry point.
+#include "fwd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using fwdk::DType;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                              \
+  do {                                                                                             \
+    hipError_t e_ = (expr);                                                                        \
+    if (e_ != hipSuccess) return fail(FWD_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// sqrt(hidden) rounded to 8 significant bits, ties to even ("pegainfer issue #878":
+// the embedding scale is the bf16-rounded value).
+float bf16_sqrt(int hidden) {
+  const double r = std::sqrt((double)hidden);
+  int e = 0;
+  const double m = std::frexp(r, &e);                    // r = m * 2^e, m in [0.5, 1)
+  const double q = std::nearbyint(std::ldexp(m, 8));    // default rounding: nearest, ties to even
+  return (float)std::ldexp(q, e - 8);
+}
+
+int check_config(const fwd_config* c) {
+  if (!c) return fail(FWD_E_ARG, "config is NULL");
+  if (c->n_layers < 0 || c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->ffn <= 0 || c->vocab <= 0)
+    return fail(FWD_E_CONFIG, "geometry fields must be positive (n_layers >= 0)");
+  if (c->n_heads % c->n_kv_heads) return fail(FWD_E_CONFIG, "n_heads must be a multiple of n_kv_heads");
+  if (c->dtype != FWD_DTYPE_BF16 && c->dtype != FWD_DTYPE_F32) return fail(FWD_E_CONFIG, "dtype");
+  const DType dt = DType(c->dtype);
+  if (!fwdk::attention_supported(dt, c->head_dim))
+    return fail(FWD_E_CONFIG, dt == DType::BF16 ? "bf16 head_dim must be 64, 128 or 256"
+                                                : "f32 head_dim must be 16, 32 or 64");
+  const int vec = dt == DType::BF16 ? 8 : 4;
+  if (c->hidden % vec || c->ffn % vec || (c->n_heads * c->head_dim) % vec)
+    return fail(FWD_E_CONFIG, "hidden, ffn and n_heads*head_dim must be multiples of 8 (bf16) / 4 (f32)");
+  if (dt == DType::BF16 && (c->ffn % 32 || (c->n_heads * c->head_dim) % 32 || (c->n_kv_heads * c->head_dim) % 32))
+    return fail(FWD_E_CONFIG, "bf16 needs ffn and head widths that are multiples of 32");
+  if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return fail(FWD_E_CONFIG, "rms_eps must be positive");
+  if (!(c->rope_theta > 1.0) || !std::isfinite(c->rope_theta)) return fail(FWD_E_CONFIG, "rope_theta must be > 1");
+  if (std::isnan(c->final_logit_softcap) || c->final_logit_softcap < 0.f || std::isinf(c->final_logit_softcap))
+    return fail(FWD_E_CONFIG, "final_logit_softcap must be positive, or 0 for off");
+  if (c->embed_scale_mode != FWD_EMBED_SCALE_NONE && c->embed_scale_mode != FWD_EMBED_SCALE_BF16_SQRT_HIDDEN)
+    return fail(FWD_E_CONFIG, "embed_scale_mode");
+  if (c->norm_placement != FWD_NORM_PRE && c->norm_placement != FWD_NORM_SANDWICH)
+    return fail(FWD_E_CONFIG, "norm_placement");
+  if (c->sliding_window < 0) return fail(FWD_E_CONFIG, "sliding_window must be >= 0");
+  if (c->layer_kind)
+    for (int l = 0; l < c->n_layers; ++l)
+      if (c->layer_kind[l] != FWD_LAYER_GLOBAL && c->layer_kind[l] != FWD_LAYER_LOCAL)
+        return fail(FWD_E_CONFIG, "layer_kind entries must be FWD_LAYER_GLOBAL or FWD_LAYER_LOCAL");
+  if (c->max_tokens <= 0) return fail(FWD_E_CONFIG, "max_tokens must be positive");
+  return FWD_OK;
+}
+
+struct Geometry {
+  int64_t esize, H, Hq, Hkv, D, F, V, L, T, qkv_rows, logit_chunk;
+  int64_t weight_bytes() const {
+    const int64_t per_layer = (qkv_rows * H + H * Hq * D + 2 * F * H + H * F) * esize + 4 * H * 4;
+    return V * H * esize + H * 4 + L * per_layer;
+  }
+  // Workspace (bytes, each buffer rounded to 256) for up to T tokens.
+  int64_t workspace_bytes(bool sandwich) const {
+    auto r = [](int64_t b) { return round_up(b, 256); };
+    int64_t w = 2 * r(T * H * 4);                       // residual stream, mid-layer copy
+    w += r(T * H * esize);                              // normalised activations
+    w += r(T * (Hq + Hkv) * D * esize);                 // rotated q | k
+    w += r(8 * T * Hkv * D * esize);                    // transposed v, padded keys
+    w += r(T * Hq * D * esize);                         // attention output
+    w += r(T * F * esize);                              // SwiGLU output
+    if (sandwich) w += r(T * H * 4);                    // sublayer output before its norm
+    w += r(T * 4) + r(T * 4) + 256;                     // ids, argmax, flag
+    w += r(logit_chunk * V * 4);                        // logits when the caller wants none
+    w += r(T * (D / 2) * 8);                            // RoPE cos/sin table
+    return w;
+  }
+};
+
+Geometry geometry(const fwd_config* c) {
+  Geometry g;
+  g.esize = c->dtype == FWD_DTYPE_BF16 ? 2 : 4;
+  g.H = c->hidden;
+  g.Hq = c->n_heads;
+  g.Hkv = c->n_kv_heads;
+  g.D = c->head_dim;
+  g.F = c->ffn;
+  g.V = c->vocab;
+  g.L = c->n_layers;
+  g.T = c->max_tokens;
+  g.qkv_rows = (g.Hq + 2 * g.Hkv) * g.D;
+  g.logit_chunk = std::min<int64_t>(g.T, 1024);
+  return g;
+}
+
+}  // namespace
+
+struct fwd_model {
+  fwd_config cfg{};
+  std::vector<int32_t> kinds;
+  DType dt = DType::BF16;
+  Geometry g{};
+  hipStream_t stream = nullptr;
+  float embed_scale = 1.f;
+  std::vector<void*> allocs;
+
+  void* embed = nullptr;
+  float* final_norm = nullptr;
+  struct Layer {
+    float *attn_norm, *ffn_norm, *post_attn, *post_ffn;
+    void *wqkv, *wo, *wgu, *wdown;
+  };
+  std::vector<Layer> layers;
+
+  float* x = nullptr;   // residual stream (updated in place when no hidden slots are requested)
+  float* xb = nullptr;  // mid-layer residual when slots are requested
+  void* n = nullptr;
+  void* qk = nullptr;
+  void* vt = nullptr;
+  void* o = nullptr;
+  void* a = nullptr;
+  float* u = nullptr;
+  int32_t* ids = nullptr;
+  int32_t* amax = nullptr;
+  int* flag = nullptr;
+  float* logits_ws = nullptr;
+  float2* rope_cs = nullptr;
+
+  int alloc(void** p, int64_t bytes) {
+    *p = nullptr;
+    if (bytes <= 0) return FWD_OK;
+    HIP_TRY(hipMalloc(p, (size_t)round_up(bytes, 256)));
+    allocs.push_back(*p);
+    return FWD_OK;
+  }
+  ~fwd_model() {
+    if (stream) (void)hipStreamSynchronize(stream);
+    else (void)hipDeviceSynchronize();
+    for (void* p : allocs) (void)hipFree(p);
+  }
+};
+
+namespace {
+
+// Packed row order of a q or k projection: within each head, the rotate-half pair
+// (k, k + D/2) is placed C rows apart in the same 2C-row group, so the GEMM
+// epilogue receives both members of a pair together (C = fwdk::pair_chunk).
+std::vector<int32_t> rope_row_map(int heads, int D, int C, int offset) {
+  std::vector<int32_t> map((size_t)heads * D);
+  const int half = D / 2;
+  for (int h = 0; h < heads; ++h)
+    for (int d = 0; d < D; ++d) {
+      const int k = d < half ? d : d - half, second = d < half ? 0 : 1;
+      const int packed = (2 * (k / C) + second) * C + (k % C);
+      map[(size_t)h * D + d] = offset + h * D + packed;
+    }
+  return map;
+}
+
+// Gate row f and up row f land C rows apart in the same 2C-row group.
+std::vector<int32_t> glu_row_map(int F, int C, int second) {
+  std::vector<int32_t> map(F);
+  for (int f = 0; f < F; ++f) map[f] = (2 * (f / C) + second) * C + (f % C);
+  return map;
+}
+
+std::vector<int32_t> identity_map(int rows, int offset) {
+  std::vector<int32_t> map(rows);
+  for (int r = 0; r < rows; ++r) map[r] = offset + r;
+  return map;
+}
+
+bool device_is_gfx950() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) return false;
+  return std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fwd_available(void) { return device_is_gfx950() ? 1 : 0; }
+
+const char* fwd_last_error(void) { return g_err.c_str(); }
+
+int fwd_output_sizes(const fwd_config* cfg, int32_t B, int32_t S, fwd_sizes* out) {
+  if (int rc = check_config(cfg)) return rc;
+  if (!out || B < 0 || S < 0) return fail(FWD_E_ARG, "bad B, S or NULL output");
+  const Geometry g = geometry(cfg);
+  const int64_t T = (int64_t)B * S;
+  out->logits_elems = T * g.V;
+  out->hidden_elems = (g.L + 2) * T * g.H;
+  out->argmax_elems = T;
+  out->weight_bytes = g.weight_bytes();
+  out->workspace_bytes = g.workspace_bytes(cfg->norm_placement == FWD_NORM_SANDWICH);
+  return FWD_OK;
+}
+
+int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fwd_model** out) {
+  if (!out) return fail(FWD_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (int rc = check_config(cfg)) return rc;
+  if (!w || !w->embed || !w->final_norm || (cfg->n_layers > 0 && !w->layers))
+    return fail(FWD_E_WEIGHTS, "embed, final_norm and layers are required");
+  const bool sandwich = cfg->norm_placement == FWD_NORM_SANDWICH;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const fwd_layer_weights& L = w->layers[l];
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.ffn_norm || !L.w_gate || !L.w_up || !L.w_down ||
+        (sandwich && (!L.post_attn_norm || !L.post_ffn_norm)))
+      return fail(FWD_E_WEIGHTS, "layer " + std::to_string(l) + " is missing a weight pointer");
+  }
+  if (!device_is_gfx950()) return fail(FWD_E_UNAVAILABLE, "no gfx950 device is available");
+
+  fwd_model* m = new fwd_model();
+  m->cfg = *cfg;
+  m->kinds.assign(cfg->n_layers, FWD_LAYER_GLOBAL);
+  if (cfg->layer_kind) m->kinds.assign(cfg->layer_kind, cfg->layer_kind + cfg->n_layers);
+  m->cfg.layer_kind = nullptr;
+  m->dt = DType(cfg->dtype);
+  m->g = geometry(cfg);
+  m->stream = (hipStream_t)hip_stream;
+  m->embed_scale = cfg->embed_scale_mode == FWD_EMBED_SCALE_BF16_SQRT_HIDDEN ? bf16_sqrt(cfg->hidden) : 1.f;
+  const Geometry& g = m->g;
+  hipStream_t s = m->stream;
+  const int C = fwdk::pair_chunk(m->dt);
+
+  auto run = [&]() -> int {
+    // ---- weights ----
+    if (int rc = m->alloc(&m->embed, g.V * g.H * g.esize)) return rc;
+    HIP_TRY(hipMemcpyAsync(m->embed, w->embed, g.V * g.H * g.esize, hipMemcpyDeviceToDevice, s));
+    if (int rc = m->alloc((void**)&m->final_norm, g.H * 4)) return rc;
+    HIP_TRY(fwdk::gains_to_f32(m->dt, w->final_norm, m->final_norm, (int)g.H, s));
+
+    // row maps, uploaded once
+    std::vector<int32_t> maps;
+    auto append = [&](const std::vector<int32_t>& v) {
+      const size_t off = maps.size();
+      maps.insert(maps.end(), v.begin(), v.end());
+      return off;
+    };
+    const size_t mq = append(rope_row_map((int)g.Hq, (int)g.D, C, 0));
+    const size_t mk = append(rope_row_map((int)g.Hkv, (int)g.D, C, (int)(g.Hq * g.D)));
+    const size_t mv = append(identity_map((int)(g.Hkv * g.D), (int)((g.Hq + g.Hkv) * g.D)));
+    const size_t mg = append(glu_row_map((int)g.F, C, 0));
+    const size_t mu = append(glu_row_map((int)g.F, C, 1));
+    int32_t* dmaps = nullptr;
+    HIP_TRY(hipMalloc((void**)&dmaps, maps.size() * 4));
+    struct Free {
+      int32_t* p;
+      ~Free() { (void)hipFree(p); }
+    } free_maps{dmaps};
+    HIP_TRY(hipMemcpyAsync(dmaps, maps.data(), maps.size() * 4, hipMemcpyHostToDevice, s));
+
+    const int64_t rowH = g.H * g.esize;
+    m->layers.resize(g.L);
+    for (int l = 0; l < g.L; ++l) {
+      const fwd_layer_weights& W = w->layers[l];
+      fwd_model::Layer& L = m->layers[l];
+      L = fwd_model::Layer{};
+      if (int rc = m->alloc((void**)&L.attn_norm, g.H * 4)) return rc;
+      if (int rc = m->alloc((void**)&L.ffn_norm, g.H * 4)) return rc;
+      HIP_TRY(fwdk::gains_to_f32(m->dt, W.attn_norm, L.attn_norm, (int)g.H, s));
+      HIP_TRY(fwdk::gains_to_f32(m->dt, W.ffn_norm, L.ffn_norm, (int)g.H, s));
+      if (sandwich) {
+        if (int rc = m->alloc((void**)&L.post_attn, g.H * 4)) return rc;
+        if (int rc = m->alloc((void**)&L.post_ffn, g.H * 4)) return rc;
+        HIP_TRY(fwdk::gains_to_f32(m->dt, W.post_attn_norm, L.post_attn, (int)g.H, s));
+        HIP_TRY(fwdk::gains_to_f32(m->dt, W.post_ffn_norm, L.post_ffn, (int)g.H, s));
+      }
+      if (int rc = m->alloc(&L.wqkv, g.qkv_rows * rowH)) return rc;
+      HIP_TRY(fwdk::copy_rows(L.wqkv, W.wq, dmaps + mq, (int)(g.Hq * g.D), rowH, s));
+      HIP_TRY(fwdk::copy_rows(L.wqkv, W.wk, dmaps + mk, (int)(g.Hkv * g.D), rowH, s));
+      HIP_TRY(fwdk::copy_rows(L.wqkv, W.wv, dmaps + mv, (int)(g.Hkv * g.D), rowH, s));
+      if (int rc = m->alloc(&L.wgu, 2 * g.F * rowH)) return rc;
+      HIP_TRY(fwdk::copy_rows(L.wgu, W.w_gate, dmaps + mg, (int)g.F, rowH, s));
+      HIP_TRY(fwdk::copy_rows(L.wgu, W.w_up, dmaps + mu, (int)g.F, rowH, s));
+      if (int rc = m->alloc(&L.wo, g.H * g.Hq * g.D * g.esize)) return rc;
+      HIP_TRY(hipMemcpyAsync(L.wo, W.wo, g.H * g.Hq * g.D * g.esize, hipMemcpyDeviceToDevice, s));
+      if (int rc = m->alloc(&L.wdown, g.H * g.F * g.esize)) return rc;
+      HIP_TRY(hipMemcpyAsync(L.wdown, W.w_down, g.H * g.F * g.esize, hipMemcpyDeviceToDevice, s));
+    }
+
+    // ---- RoPE table: angle(t, k) = t * theta^(-2k/D), computed in double ----
+    {
+      std::vector<float2> cs((size_t)g.T * (g.D / 2));
+      for (int64_t t = 0; t < g.T; ++t)
+        for (int64_t k = 0; k < g.D / 2; ++k) {
+          const double ang = (double)t * std::pow(cfg->rope_theta, -2.0 * (double)k / (double)g.D);
+          cs[(size_t)t * (g.D / 2) + k] = float2{(float)std::cos(ang), (float)std::sin(ang)};
+        }
+      if (int rc = m->alloc((void**)&m->rope_cs, (int64_t)cs.size() * 8)) return rc;
+      HIP_TRY(hipMemcpyAsync(m->rope_cs, cs.data(), cs.size() * 8, hipMemcpyHostToDevice, s));
+      HIP_TRY(hipStreamSynchronize(s));  // host staging buffers die at scope end
+    }
+
+    // ---- workspace ----
+    const int64_t T = g.T;
+    if (int rc = m->alloc((void**)&m->x, T * g.H * 4)) return rc;
+    if (int rc = m->alloc((void**)&m->xb, T * g.H * 4)) return rc;
+    if (int rc = m->alloc(&m->n, T * g.H * g.esize)) return rc;
+    if (int rc = m->alloc(&m->qk, T * (g.Hq + g.Hkv) * g.D * g.esize)) return rc;
+    if (int rc = m->alloc(&m->vt, 8 * T * g.Hkv * g.D * g.esize)) return rc;
+    if (int rc = m->alloc(&m->o, T * g.Hq * g.D * g.esize)) return rc;
+    if (int rc = m->alloc(&m->a, T * g.F * g.esize)) return rc;
+    if (sandwich)
+      if (int rc = m->alloc((void**)&m->u, T * g.H * 4)) return rc;
+    if (int rc = m->alloc((void**)&m->ids, T * 4)) return rc;
+    if (int rc = m->alloc((void**)&m->amax, T * 4)) return rc;
+    if (int rc = m->alloc((void**)&m->flag, 256)) return rc;
+    if (int rc = m->alloc((void**)&m->logits_ws, g.logit_chunk * g.V * 4)) return rc;
+    HIP_TRY(hipStreamSynchronize(s));
+    return FWD_OK;
+  };
+  const int rc = run();
+  if (rc != FWD_OK) {
+    delete m;
+    return rc;
+  }
+  *out = m;
+  return FWD_OK;
+}
+
+int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, const fwd_outputs* out) {
+  if (!m) return fail(FWD_E_ARG, "model is NULL");
+  if (B < 0 || S < 0) return fail(FWD_E_ARG, "B and S must be >= 0");
+  const int64_t T = (int64_t)B * S;
+  if (T == 0) return FWD_OK;
+  if (!ids_host) return fail(FWD_E_ARG, "ids is NULL");
+  if (T > m->g.T) return fail(FWD_E_TOO_LARGE, "B*S = " + std::to_string(T) + " exceeds max_tokens " +
+                                                   std::to_string(m->g.T));
+  const int V = (int)m->g.V;
+  for (int64_t i = 0; i < T; ++i)
+    if (ids_host[i] < 0 || ids_host[i] >= V)
+      return fail(FWD_E_TOKEN_RANGE, "token id " + std::to_string(ids_host[i]) + " at index " + std::to_string(i) +
+                                         " is outside [0, " + std::to_string(V) + ")");
+  const fwd_outputs none{nullptr, nullptr, nullptr};
+  const fwd_outputs& o = out ? *out : none;
+
+  const Geometry& g = m->g;
+  const DType dt = m->dt;
+  hipStream_t s = m->stream;
+  const int H = (int)g.H, Hq = (int)g.Hq, Hkv = (int)g.Hkv, D = (int)g.D, F = (int)g.F, L = (int)g.L;
+  const int M = (int)T;
+  const float eps = m->cfg.rms_eps;
+  const bool sandwich = m->cfg.norm_placement == FWD_NORM_SANDWICH;
+  const int64_t TH = T * H;
+  float* hidden = o.hidden;
+
+  HIP_TRY(hipMemcpyAsync(m->ids, ids_host, T * 4, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipMemsetAsync(m->flag, 0, 4, s));
+
+  float* cur = hidden ? hidden : m->x;
+  HIP_TRY(fwdk::embed(dt, m->ids, m->embed, cur, M, H, m->embed_scale, s));
+  // first layer's input norm; every later sublayer input norm is fused below
+  if (L > 0) HIP_TRY(fwdk::rmsnorm(dt, cur, m->layers[0].attn_norm, m->n, nullptr, M, H, eps, s));
+
+  const int ldvt = (int)round_up(S, 8);
+  char* qk = (char*)m->qk;
+  for (int l = 0; l < L; ++l) {
+    const fwd_model::Layer& w = m->layers[l];
+    float* xin = cur;
+    float* xmid = hidden ? m->xb : m->x;
+    float* xout = hidden ? hidden + (int64_t)(l + 1) * TH : m->x;
+    const bool last = l + 1 == L;
+    const float* next_norm = last ? m->final_norm : m->layers[l + 1].attn_norm;
+
+    // attention sublayer (its input norm is already in m->n)
+    fwdk::RopeArgs ra{m->qk, m->vt, m->rope_cs, Hq, Hkv, D, S, ldvt};
+    HIP_TRY(fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, s));
+    fwdk::AttnArgs aa{};
+    aa.q = qk;
+    aa.k = qk + (int64_t)Hq * D * g.esize;
+    aa.vt = m->vt;
+    aa.o = m->o;
+    aa.ldq = aa.ldk = (int64_t)(Hq + Hkv) * D;
+    aa.ldo = (int64_t)Hq * D;
+    aa.ldvt = ldvt;
+    aa.B = B;
+    aa.S = S;
+    aa.Hq = Hq;
+    aa.Hkv = Hkv;
+    aa.D = D;
+    aa.window = m->kinds[l] == FWD_LAYER_LOCAL ? m->cfg.sliding_window : 0;
+    HIP_TRY(fwdk::attention(dt, aa, s));
+    if (!sandwich) {
+      HIP_TRY(fwdk::gemm_residual(dt, m->o, w.wo, xin, xmid, M, H, Hq * D, s));
+      HIP_TRY(fwdk::rmsnorm(dt, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, s));
+    } else {
+      HIP_TRY(fwdk::gemm_store(dt, m->o, w.wo, m->u, H, M, H, Hq * D, 0.f, s));
+      HIP_TRY(fwdk::add_norm(dt, xin, m->u, w.post_attn, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, s));
+    }
+
+    // feed-forward sublayer
+    HIP_TRY(fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, s));
+    float* final32 = (last && hidden) ? hidden + (int64_t)(L + 1) * TH : nullptr;
+    if (!sandwich) {
+      HIP_TRY(fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, s));
+      HIP_TRY(fwdk::rmsnorm(dt, xout, next_norm, m->n, final32, M, H, eps, s));
+    } else {
+      HIP_TRY(fwdk::gemm_store(dt, m->a, w.wdown, m->u, H, M, H, F, 0.f, s));
+      HIP_TRY(fwdk::add_norm(dt, xmid, m->u, w.post_ffn, xout, next_norm, m->n, final32, M, H, eps, s));
+    }
+    cur = xout;
+  }
+  if (L == 0) {
+    float* final32 = hidden ? hidden + TH : nullptr;
+    HIP_TRY(fwdk::rmsnorm(dt, cur, m->final_norm, m->n, final32, M, H, eps, s));
+  }
+
+  // tied LM head (+ softcap) and argmax
+  const float cap = m->cfg.final_logit_softcap;
+  int32_t* am = o.argmax ? o.argmax : m->amax;
+  if (o.logits) {
+    HIP_TRY(fwdk::gemm_store(dt, m->n, m->embed, o.logits, V, M, V, H, cap, s));
+    HIP_TRY(fwdk::argmax_rows(o.logits, V, M, V, am, m->flag, s));
+  } else {
+    const int64_t chunk = g.logit_chunk;
+    for (int64_t r0 = 0; r0 < T; r0 += chunk) {
+      const int rows = (int)std::min<int64_t>(chunk, T - r0);
+      const char* nrow = (const char*)m->n + r0 * H * g.esize;
+      HIP_TRY(fwdk::gemm_store(dt, nrow, m->embed, m->logits_ws, V, rows, V, H, cap, s));
+      HIP_TRY(fwdk::argmax_rows(m->logits_ws, V, rows, V, am + r0, m->flag, s));
+    }
+  }
+  int flag = 0;
+  HIP_TRY(hipMemcpyAsync(&flag, m->flag, 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  if (flag) return fail(FWD_E_NONFINITE, "non-finite logits");
+  return FWD_OK;
+}
+
+int fwd_gemm(const void* X, const void* W, float* Y, int32_t P, int32_t in, int32_t out, int32_t dtype,
+             void* hip_stream) {
+  if (dtype != FWD_DTYPE_BF16 && dtype != FWD_DTYPE_F32) return fail(FWD_E_ARG, "dtype");
+  if (P < 0 || in <= 0 || out < 0) return fail(FWD_E_ARG, "sizes must be P >= 0, in > 0, out >= 0");
+  if (in % (dtype == FWD_DTYPE_BF16 ? 8 : 4)) return fail(FWD_E_ARG, "in must be a multiple of 8 (bf16) / 4 (f32)");
+  if ((int64_t)P * out == 0) return FWD_OK;
+  if (!X || !W || !Y) return fail(FWD_E_ARG, "NULL buffer");
+  if (!device_is_gfx950()) return fail(FWD_E_UNAVAILABLE, "no gfx950 device is available");
+  HIP_TRY(fwdk::gemm_store(DType(dtype), X, W, Y, out, P, out, in, 0.f, (hipStream_t)hip_stream));
+  return FWD_OK;
+}
+
+int fwd_attention(const void* q, const void* k, const void* v_t, void* o, int32_t B, int32_t S, int32_t n_heads,
+                  int32_t n_kv_heads, int32_t head_dim, int32_t window, int32_t dtype, void* hip_stream) {
+  if (dtype != FWD_DTYPE_BF16 && dtype != FWD_DTYPE_F32) return fail(FWD_E_ARG, "dtype");
+  if (B < 0 || S < 0 || n_heads <= 0 || n_kv_heads <= 0 || window < 0) return fail(FWD_E_ARG, "bad sizes");
+  if (n_heads % n_kv_heads) return fail(FWD_E_CONFIG, "n_heads must be a multiple of n_kv_heads");
+  if (!fwdk::attention_supported(DType(dtype), head_dim)) return fail(FWD_E_CONFIG, "unsupported head_dim");
+  if ((int64_t)B * S == 0) return FWD_OK;
+  if (!q || !k || !v_t || !o) return fail(FWD_E_ARG, "NULL buffer");
+  if (!device_is_gfx950()) return fail(FWD_E_UNAVAILABLE, "no gfx950 device is available");
+  fwdk::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.vt = v_t;
+  a.o = o;
+  a.ldq = a.ldo = (int64_t)n_heads * head_dim;
+  a.ldk = (int64_t)n_kv_heads * head_dim;
+  a.ldvt = (int)round_up(S, 8);
+  a.B = B;
+  a.S = S;
+  a.Hq = n_heads;
+  a.Hkv = n_kv_heads;
+  a.D = head_dim;
+  a.window = window;
+  HIP_TRY(fwdk::attention(DType(dtype), a, (hipStream_t)hip_stream));
+  return FWD_OK;
+}
+
+int fwd_rmsnorm(const float* x, const void* w, void* y, int32_t rows, int32_t hidden, float eps, int32_t dtype,
+                void* hip_stream) {
+  if (dtype != FWD_DTYPE_BF16 && dtype != FWD_DTYPE_F32) return fail(FWD_E_ARG, "dtype");
+  if (rows < 0 || hidden <= 0 || hidden % 4) return fail(FWD_E_ARG, "rows >= 0 and hidden a positive multiple of 4");
+  if (rows == 0) return FWD_OK;
+  if (!x || !w || !y) return fail(FWD_E_ARG, "NULL buffer");
+  if (!device_is_gfx950()) return fail(FWD_E_UNAVAILABLE, "no gfx950 device is available");
+  HIP_TRY(fwdk::rmsnorm(DType(dtype), x, (const float*)w, y, nullptr, rows, hidden, eps, (hipStream_t)hip_stream));
+  return FWD_OK;
+}
+
+void fwd_destroy(fwd_model* m) { delete m; }
+
+}  // extern "C"

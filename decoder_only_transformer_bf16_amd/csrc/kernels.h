@@ -1,0 +1,69 @@
+// Host-side launchers of the gfx950 kernels. Every launcher only enqueues work on
+// `stream` and returns the launch status; shapes are validated by the caller
+// (the C-ABI layer) before any launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fwdk {
+
+enum class DType { F32 = 0, BF16 = 1 };
+
+// Pair distance of the fused pair epilogues (RoPE, SwiGLU): the two members of a
+// pair sit `pair_chunk(dt)` packed columns apart. The weight packing of the runtime
+// and the GEMM epilogues both follow it.
+inline int pair_chunk(DType dt) { return dt == DType::BF16 ? 32 : 1; }
+
+// ---- projections Y = X·Wᵀ (X [M, K], W [N, K], both row-major) ----
+// Y fp32 [M, N] (ldy), optional softcap (0 = off).
+hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K,
+                      float softcap, hipStream_t s);
+// xout[M, N] = xin + X·Wᵀ (fp32 residual stream, row stride N; xin may equal xout).
+hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xin, float* xout, int M, int N,
+                         int K, hipStream_t s);
+// a[M, F] = silu(g) * u with W packed as interleaved gate/up chunks (N = 2F).
+hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, hipStream_t s);
+// QKV projection with RoPE on q and k; N = (Hq + 2 Hkv) D with packed q/k rows.
+// Writes qk [M, (Hq + Hkv) D] (rotated, natural dim order) and
+// vt [B, Hkv, D, ldvt] (values transposed). Rows are b * S + t.
+struct RopeArgs {
+  void* qk;
+  void* vt;
+  const float2* cs;  // [S_max, D / 2] (cos, sin)
+  int Hq, Hkv, D, S, ldvt;
+};
+hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, hipStream_t s);
+
+// ---- attention ----
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* vt;
+  void* o;
+  int64_t ldq, ldk, ldo;  // elements between consecutive tokens
+  int ldvt;               // elements between consecutive dims of vt (>= S, multiple of 8)
+  int B, S, Hq, Hkv, D, window;
+};
+hipError_t attention(DType dt, const AttnArgs& a, hipStream_t s);
+bool attention_supported(DType dt, int D);
+
+// ---- row kernels ----
+// y = RMSNorm(x; w) (w fp32 gains); y of dtype dt; optional fp32 copy y32.
+hipError_t rmsnorm(DType dt, const float* x, const float* w, void* y, float* y32, int rows, int H, float eps,
+                   hipStream_t s);
+// xout = xin + RMSNorm(u; wpost); y = RMSNorm(xout; wnext) (dtype dt), y32 optional fp32 copy of y.
+hipError_t add_norm(DType dt, const float* xin, const float* u, const float* wpost, float* xout, const float* wnext,
+                    void* y, float* y32, int rows, int H, float eps, hipStream_t s);
+// x[t, :] = E[ids[t], :] * scale (fp32 out).
+hipError_t embed(DType dt, const int32_t* ids, const void* E, float* x, int rows, int H, float scale,
+                 hipStream_t s);
+// out[r] = argmax_v z[r, v] (lowest index on ties); *flag = 1 if any z is not finite.
+hipError_t argmax_rows(const float* z, int64_t ldz, int rows, int V, int32_t* out, int* flag, hipStream_t s);
+
+// ---- packing ----
+// dst[map[r], :] = src[r, :] for r < rows; rows of `row_bytes` bytes (multiple of 4).
+hipError_t copy_rows(void* dst, const void* src, const int32_t* map, int rows, int64_t row_bytes, hipStream_t s);
+// dst[i] = float(src[i]) for a gain vector of dtype dt.
+hipError_t gains_to_f32(DType dt, const void* src, float* dst, int n, hipStream_t s);
+
+}  // namespace fwdk

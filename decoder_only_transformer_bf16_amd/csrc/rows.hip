@@ -1,0 +1,246 @@
+// Row-wise, HBM-bound kernels of the forward pass: scaled embedding gather,
+// RMSNorm (plain, and the sandwich variant fused with the residual add), the
+// per-position argmax with the non-finite check, and weight packing copies.
+// One 64-lane wavefront per row, 16-byte vector accesses along the row.
+#include "common.h"
+#include "kernels.h"
+
+namespace fwdk {
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // 4 wavefronts of 64 lanes
+
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ void store(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+  static __device__ __forceinline__ float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+};
+template <> struct Vec4<bf16_t> {
+  static __device__ __forceinline__ void store(bf16_t* p, float4 v) {
+    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+  }
+  static __device__ __forceinline__ float4 load(const bf16_t* p) {
+    const u32x2_t u = *reinterpret_cast<const u32x2_t*>(p);
+    return float4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xFFFF0000u), __uint_as_float(u[1] << 16),
+                  __uint_as_float(u[1] & 0xFFFF0000u)};
+  }
+};
+
+__device__ __forceinline__ float sumsq4(float4 v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
+__device__ __forceinline__ float4 mul4(float4 a, float4 b, float s) {
+  return float4{a.x * b.x * s, a.y * b.y * s, a.z * b.z * s, a.w * b.w * s};
+}
+
+// y = x * w / sqrt(mean(x^2) + eps)  ("N7 · model/forward-parity", intro: RMSNorm)
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ w,
+                                                     T* __restrict__ y, float* __restrict__ y32, int rows, int H,
+                                                     float eps) {
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* xr = x + (int64_t)row * H;
+  float ss = 0.f;
+  for (int i = lane * 4; i < H; i += 256) ss += sumsq4(Vec4<float>::load(xr + i));
+  ss = wave_sum(ss);
+  const float r = fast_rsqrt(ss / (float)H + eps);
+  for (int i = lane * 4; i < H; i += 256) {
+    const float4 v = mul4(Vec4<float>::load(xr + i), Vec4<float>::load(w + i), r);
+    Vec4<T>::store(y + (int64_t)row * H + i, v);
+    if (y32) Vec4<float>::store(y32 + (int64_t)row * H + i, v);
+  }
+}
+
+// Sandwich placement ("N7 · model/forward-parity", intro: topology-selected norm
+// placement): xout = xin + RMSNorm(u; wpost), then y = RMSNorm(xout; wnext), the
+// input of the next sublayer.
+template <typename T>
+__global__ __launch_bounds__(256) void add_norm_kernel(const float* __restrict__ xin, const float* __restrict__ u,
+                                                      const float* __restrict__ wpost, float* __restrict__ xout,
+                                                      const float* __restrict__ wnext, T* __restrict__ y,
+                                                      float* __restrict__ y32, int rows, int H, float eps) {
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t off = (int64_t)row * H;
+  float ss = 0.f;
+  for (int i = lane * 4; i < H; i += 256) ss += sumsq4(Vec4<float>::load(u + off + i));
+  ss = wave_sum(ss);
+  const float ru = fast_rsqrt(ss / (float)H + eps);
+  float sx = 0.f;
+  for (int i = lane * 4; i < H; i += 256) {
+    const float4 n = mul4(Vec4<float>::load(u + off + i), Vec4<float>::load(wpost + i), ru);
+    const float4 xi = Vec4<float>::load(xin + off + i);
+    const float4 xo = float4{xi.x + n.x, xi.y + n.y, xi.z + n.z, xi.w + n.w};
+    Vec4<float>::store(xout + off + i, xo);
+    sx += sumsq4(xo);
+  }
+  sx = wave_sum(sx);
+  const float rx = fast_rsqrt(sx / (float)H + eps);
+  for (int i = lane * 4; i < H; i += 256) {
+    // each lane re-reads only what it wrote itself
+    const float4 v = mul4(Vec4<float>::load(xout + off + i), Vec4<float>::load(wnext + i), rx);
+    Vec4<T>::store(y + off + i, v);
+    if (y32) Vec4<float>::store(y32 + off + i, v);
+  }
+}
+
+// x[t] = E[ids[t]] * scale ("pegainfer issue #878", Proposed Plan: scaled embedding)
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids, const T* __restrict__ E,
+                                                   float* __restrict__ x, int rows, int H, float scale) {
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const T* e = E + (int64_t)ids[row] * H;
+  for (int i = lane * 4; i < H; i += 256) {
+    const float4 v = Vec4<T>::load(e + i);
+    Vec4<float>::store(x + (int64_t)row * H + i, float4{v.x * scale, v.y * scale, v.z * scale, v.w * scale});
+  }
+}
+
+// argmax over a row, lowest index on ties ("N7 · model/forward-parity", Theorem 1:
+// per-position argmax); any non-finite value raises the flag ("pegainfer issue
+// #878", Acceptance Criteria). 256 threads per row.
+__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ z, int64_t ldz, int V,
+                                                    int32_t* __restrict__ out, int* __restrict__ flag) {
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const float* zr = z + (int64_t)row * ldz;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  bool bad = false;
+  const bool vec = (V % 4 == 0) && ((ldz % 4) == 0);
+  if (vec) {
+    for (int i = tid * 4; i < V; i += 1024) {
+      const float4 v = *reinterpret_cast<const float4*>(zr + i);
+      bad |= !(isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w));
+      better(bv, bi, v.x, i);
+      better(bv, bi, v.y, i + 1);
+      better(bv, bi, v.z, i + 2);
+      better(bv, bi, v.w, i + 3);
+    }
+  } else {
+    for (int i = tid; i < V; i += 256) {
+      const float v = zr[i];
+      bad |= !isfinite(v);
+      better(bv, bi, v, i);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    better(bv, bi, ov, oi);
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  __shared__ int sbad[4];
+  const int wave = tid >> 6;
+  const bool wbad = __any(bad);
+  if ((tid & 63) == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+    sbad[wave] = wbad;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float v = sv[0];
+    int i = si[0];
+    int anybad = sbad[0];
+    for (int w = 1; w < 4; ++w) {
+      better(v, i, sv[w], si[w]);
+      anybad |= sbad[w];
+    }
+    if (out) out[row] = i;
+    if (anybad) *flag = 1;
+  }
+}
+
+// Packing copy: dst row map[r] <- src row r.
+__global__ __launch_bounds__(256) void copy_rows_kernel(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
+                                                       const int32_t* __restrict__ map, int64_t row_bytes) {
+  const int r = blockIdx.x;
+  const uint8_t* s = src + (int64_t)r * row_bytes;
+  uint8_t* d = dst + (int64_t)map[r] * row_bytes;
+  if (row_bytes % 16 == 0) {
+    for (int64_t i = threadIdx.x * 16; i < row_bytes; i += 256 * 16)
+      *reinterpret_cast<u32x4_t*>(d + i) = *reinterpret_cast<const u32x4_t*>(s + i);
+  } else {
+    for (int64_t i = threadIdx.x * 4; i < row_bytes; i += 256 * 4)
+      *reinterpret_cast<uint32_t*>(d + i) = *reinterpret_cast<const uint32_t*>(s + i);
+  }
+}
+
+template <typename T>
+__global__ void gains_kernel(const T* __restrict__ src, float* __restrict__ dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = Elem<T>::load(src + i);
+}
+
+inline int row_blocks(int rows) { return (rows + kRowsPerBlock - 1) / kRowsPerBlock; }
+
+}  // namespace
+
+hipError_t rmsnorm(DType dt, const float* x, const float* w, void* y, float* y32, int rows, int H, float eps,
+                   hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (dt == DType::BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, x, w, (bf16_t*)y, y32,
+                       rows, H, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(row_blocks(rows)), dim3(256), 0, s, x, w, (float*)y, y32, rows,
+                       H, eps);
+  return hipGetLastError();
+}
+
+hipError_t add_norm(DType dt, const float* xin, const float* u, const float* wpost, float* xout, const float* wnext,
+                    void* y, float* y32, int rows, int H, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (dt == DType::BF16)
+    hipLaunchKernelGGL(add_norm_kernel<bf16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, xin, u, wpost, xout,
+                       wnext, (bf16_t*)y, y32, rows, H, eps);
+  else
+    hipLaunchKernelGGL(add_norm_kernel<float>, dim3(row_blocks(rows)), dim3(256), 0, s, xin, u, wpost, xout, wnext,
+                       (float*)y, y32, rows, H, eps);
+  return hipGetLastError();
+}
+
+hipError_t embed(DType dt, const int32_t* ids, const void* E, float* x, int rows, int H, float scale,
+                 hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (dt == DType::BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, ids, (const bf16_t*)E, x,
+                       rows, H, scale);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(row_blocks(rows)), dim3(256), 0, s, ids, (const float*)E, x, rows,
+                       H, scale);
+  return hipGetLastError();
+}
+
+hipError_t argmax_rows(const float* z, int64_t ldz, int rows, int V, int32_t* out, int* flag, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(256), 0, s, z, ldz, V, out, flag);
+  return hipGetLastError();
+}
+
+hipError_t copy_rows(void* dst, const void* src, const int32_t* map, int rows, int64_t row_bytes, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(rows), dim3(256), 0, s, (uint8_t*)dst, (const uint8_t*)src, map,
+                     row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t gains_to_f32(DType dt, const void* src, float* dst, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (dt == DType::BF16)
+    hipLaunchKernelGGL(gains_kernel<bf16_t>, dim3((n + 255) / 256), dim3(256), 0, s, (const bf16_t*)src, dst, n);
+  else
+    hipLaunchKernelGGL(gains_kernel<float>, dim3((n + 255) / 256), dim3(256), 0, s, (const float*)src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace fwdk

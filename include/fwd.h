@@ -1,0 +1,226 @@
+/*
+ * fwd.h — C ABI of the MI355X (gfx950) prefill forward library, libfwd.so.
+ *
+ * The library computes the forward pass of a decoder-only transformer over a
+ * batch of prompts ("N7 · model/forward-parity", introduction and Theorem 1):
+ * scaled embedding lookup, then per layer RMSNorm, the Q/K/V/O projections,
+ * RoPE, causal grouped-query attention with an optional sliding window, the
+ * SwiGLU feed-forward and the residual adds, with pre-norm or sandwich-norm
+ * placement; then the final norm, the tied LM head with an optional final-logit
+ * softcap ("pegainfer issue #878", Description and Proposed Plan), and the
+ * per-position argmax. Projections are Y = X·Wᵀ with W stored [out, in]
+ * ("N9 · metalgemm", Theorem 1).
+ *
+ * Conventions for every entry point:
+ *  - Plain C types only. Pointers documented as "device" point to HIP device
+ *    memory; "host" pointers to ordinary host memory.
+ *  - All GPU work is enqueued on the hip stream passed in (NULL = the null
+ *    stream). Functions return once the work is enqueued, except where stated.
+ *  - Return value: FWD_OK (0) or a negative FWD_E_* code; the message of the
+ *    last failure on the calling thread is available from fwd_last_error().
+ *  - Nothing aborts and nothing falls back to a CPU computation: with no usable
+ *    gfx950 device every compute entry point returns FWD_E_UNAVAILABLE.
+ *  - bf16 means the 16-bit brain floating-point format (upper half of an IEEE
+ *    binary32); all accumulation is in fp32.
+ */
+#ifndef FWD_H_
+#define FWD_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define FWD_OK 0
+#define FWD_E_CONFIG (-1)      /* invalid or unsupported geometry / numerics        */
+#define FWD_E_WEIGHTS (-2)     /* a required weight pointer is NULL                 */
+#define FWD_E_TOKEN_RANGE (-3) /* a token id lies outside [0, vocab)                */
+#define FWD_E_TOO_LARGE (-4)   /* B*S exceeds the model's max_tokens                */
+#define FWD_E_NONFINITE (-5)   /* a logit came out NaN or infinite                  */
+#define FWD_E_HIP (-6)         /* a HIP runtime call failed (message has details)   */
+#define FWD_E_UNAVAILABLE (-7) /* no usable gfx950 device                           */
+#define FWD_E_ARG (-8)         /* bad argument (NULL handle, negative size, ...)    */
+
+/* ---- enumerations ---- */
+#define FWD_DTYPE_F32 0
+#define FWD_DTYPE_BF16 1
+#define FWD_EMBED_SCALE_NONE 0
+#define FWD_EMBED_SCALE_BF16_SQRT_HIDDEN 1 /* sqrt(hidden) rounded to bf16 (issue #878) */
+#define FWD_NORM_PRE 0
+#define FWD_NORM_SANDWICH 1 /* RMSNorm on the sublayer input and on its output */
+#define FWD_LAYER_GLOBAL 0
+#define FWD_LAYER_LOCAL 1   /* sliding-window attention layer                 */
+
+/*
+ * Model description ("pegainfer issue #878", Proposed Plan: one typed config,
+ * geometry derived from it, softcap validated positive at parse).
+ *  n_layers, hidden (H), n_heads (Hq), n_kv_heads (Hkv, divides Hq),
+ *  head_dim (D, even), ffn (F), vocab (V)
+ *  rms_eps              RMSNorm epsilon (> 0)
+ *  rope_theta           RoPE base (> 1); rotate-half pairs (k, k + D/2)
+ *  embed_scale_mode     FWD_EMBED_SCALE_*
+ *  final_logit_softcap  0 = off; otherwise z <- c * tanh(z / c); c < 0 or NaN is FWD_E_CONFIG
+ *  sliding_window       W > 0: a local layer's query i sees keys j with 0 <= i - j < W
+ *  layer_kind           host array of n_layers FWD_LAYER_* values, read during
+ *                       fwd_create only; NULL = every layer global
+ *  norm_placement       FWD_NORM_*
+ *  dtype                FWD_DTYPE_BF16 (weights and GEMM operands bf16) or
+ *                       FWD_DTYPE_F32 (everything fp32)
+ *  max_tokens           largest B*S a later fwd_prefill may request; sizes the
+ *                       workspace that fwd_create allocates
+ * Supported: bf16 needs head_dim in {64, 128, 256}; f32 needs head_dim <= 64;
+ * hidden, Hq*D, Hkv*D and ffn multiples of 8 (bf16) or 4 (f32); bf16 additionally
+ * needs Hq*D, Hkv*D and ffn multiples of 32.
+ */
+typedef struct fwd_config {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rms_eps;
+  float final_logit_softcap;
+  double rope_theta;
+  int32_t embed_scale_mode;
+  int32_t sliding_window;
+  const int32_t* layer_kind;
+  int32_t norm_placement;
+  int32_t dtype;
+  int32_t max_tokens;
+} fwd_config;
+
+/*
+ * Weights of one layer: device pointers, row-major W[out, in], element type
+ * bf16 or f32 according to fwd_config.dtype (norm gains too).
+ *  wq [Hq*D, H], wk [Hkv*D, H], wv [Hkv*D, H], wo [H, Hq*D],
+ *  w_gate [F, H], w_up [F, H], w_down [H, F], *_norm [H].
+ *  post_attn_norm / post_ffn_norm are read only for FWD_NORM_SANDWICH.
+ */
+typedef struct fwd_layer_weights {
+  const void* attn_norm;
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* wo;
+  const void* ffn_norm;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* post_attn_norm;
+  const void* post_ffn_norm;
+} fwd_layer_weights;
+
+/* embed [V, H] (also the tied LM head), final_norm [H]: device pointers;
+ * layers: host array of n_layers entries. */
+typedef struct fwd_weights {
+  const void* embed;
+  const void* final_norm;
+  const fwd_layer_weights* layers;
+} fwd_weights;
+
+/*
+ * Caller-owned device output buffers of one fwd_prefill; any may be NULL to skip it.
+ *  logits [B, S, V] fp32 (after the softcap when it is on)
+ *  hidden [L + 2, B, S, H] fp32: slot 0 = scaled embedding, slot l + 1 = the
+ *         residual stream after layer l, slot L + 1 = final-norm output
+ *         ("N7 · model/forward-parity", Theorem 1: one hidden slot per layer)
+ *  argmax [B, S] int32: per-position argmax of the logits, lowest index on ties
+ */
+typedef struct fwd_outputs {
+  float* logits;
+  float* hidden;
+  int32_t* argmax;
+} fwd_outputs;
+
+/* Element counts of the outputs, and bytes the library allocates for a model. */
+typedef struct fwd_sizes {
+  int64_t logits_elems;
+  int64_t hidden_elems;
+  int64_t argmax_elems;
+  int64_t weight_bytes;
+  int64_t workspace_bytes;
+} fwd_sizes;
+
+typedef struct fwd_model fwd_model;
+
+/* 1 if a gfx950 device is visible and usable, else 0 ("N9 · metalgemm",
+ * Theorem 2: Available()). Never fails. */
+int fwd_available(void);
+
+/*
+ * Validate cfg, allocate the model on the current HIP device, and copy the
+ * weights into library-owned HBM in the library's packed layout
+ * ("N9 · metalgemm", Theorem 2: Upload / FwdConfig / FwdLayer / FwdFinalNorm).
+ * The weight buffers are only read during this call (the copies run on
+ * hip_stream and are complete when it returns), so the caller may free them
+ * afterwards. The model keeps hip_stream for later fwd_prefill calls.
+ * On success *out receives the handle (release with fwd_destroy).
+ * Errors: FWD_E_ARG, FWD_E_CONFIG, FWD_E_WEIGHTS, FWD_E_HIP, FWD_E_UNAVAILABLE.
+ */
+int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fwd_model** out);
+
+/*
+ * Sizes of the outputs of a (B, S) prefill and of the model's own allocations
+ * — the one source of truth for buffer sizes ("pegainfer issue #878", Proposed
+ * Plan). Pure host computation; needs no device. Errors: FWD_E_ARG, FWD_E_CONFIG.
+ */
+int fwd_output_sizes(const fwd_config* cfg, int32_t B, int32_t S, fwd_sizes* out);
+
+/*
+ * Forward pass over B independent prompts of S tokens each (positions 0..S-1).
+ * ids_host: host int32 [B, S]. Every id is checked against [0, vocab) on the
+ * host before anything is uploaded ("pegainfer issue #878", Proposed Plan);
+ * a bad id returns FWD_E_TOKEN_RANGE and enqueues nothing. B*S must not exceed
+ * max_tokens (FWD_E_TOO_LARGE). S == 0 or B == 0 is a no-op.
+ * Blocks until the work on the model's stream is finished, then returns
+ * FWD_E_NONFINITE if any logit was NaN or infinite ("pegainfer issue #878",
+ * Acceptance Criteria: non-finite values fail outright); outputs are then
+ * unspecified. Calls on one model must not overlap.
+ */
+int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, const fwd_outputs* out);
+
+/*
+ * Standalone projection Y[p, o] = sum_i X[p, i] * W[o, i] ("N9 · metalgemm",
+ * Theorem 1: Weight.MatMul). X device [P, in], W device [out, in], both of
+ * `dtype` (FWD_DTYPE_BF16 or FWD_DTYPE_F32); Y device fp32 [P, out]. fp32
+ * accumulation. `in` must be a multiple of 8 (bf16) or 4 (f32).
+ * Errors: FWD_E_ARG, FWD_E_UNAVAILABLE, FWD_E_HIP.
+ */
+int fwd_gemm(const void* X, const void* W, float* Y, int32_t P, int32_t in, int32_t out,
+             int32_t dtype, void* hip_stream);
+
+/*
+ * Causal grouped-query attention alone, the operation inside each layer
+ * ("N7 · model/forward-parity", introduction; "N9 · metalgemm", Theorem 1 op
+ * chain): o[b,i,h,:] = sum_j softmax_j(q[b,i,h,:]·k[b,j,g,:] / sqrt(D)) v[b,j,g,:]
+ * over keys j <= i (and i - j < window when window > 0), g = h / (Hq / Hkv).
+ * Device buffers of `dtype`: q [B, S, Hq, D], k [B, S, Hkv, D],
+ * v_t [B, Hkv, D, Sp] with Sp = S rounded up to a multiple of 8 (values
+ * transposed, keys contiguous; entries past S are ignored), o [B, S, Hq, D].
+ * No RoPE is applied here. Errors: FWD_E_ARG, FWD_E_CONFIG, FWD_E_UNAVAILABLE, FWD_E_HIP.
+ */
+int fwd_attention(const void* q, const void* k, const void* v_t, void* o, int32_t B, int32_t S,
+                  int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t window,
+                  int32_t dtype, void* hip_stream);
+
+/*
+ * RMSNorm alone ("N7 · model/forward-parity", introduction):
+ * y[r, i] = x[r, i] * w[i] / sqrt(mean_j x[r, j]^2 + eps).
+ * x device fp32 [rows, H]; w device fp32 [H]; y device [rows, H] of `dtype`.
+ * H must be a multiple of 4.
+ * Errors: FWD_E_ARG, FWD_E_UNAVAILABLE, FWD_E_HIP.
+ */
+int fwd_rmsnorm(const float* x, const void* w, void* y, int32_t rows, int32_t hidden, float eps,
+                int32_t dtype, void* hip_stream);
+
+/* Release a model and everything it allocated (waits for its stream first).
+ * NULL is a no-op ("N9 · metalgemm", Theorem 1: Free / Reset reclaim the table). */
+void fwd_destroy(fwd_model* m);
+
+/* Message of the last failure on the calling thread ("" if none). The pointer
+ * stays valid until the next call into the library on that thread. */
+const char* fwd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FWD_H_ */

@@ -128,6 +128,29 @@ class LazyWeights:
         return arr
 
 
+class HostWeights:
+    """Mapping name -> float32 view of arrays already drawn in storage form
+    (bf16 bit patterns are widened exactly on access)."""
+
+    def __init__(self, raw: Dict[str, np.ndarray]):
+        self.raw = raw
+
+    def __contains__(self, name):
+        return name in self.raw
+
+    def keys(self):
+        return self.raw.keys()
+
+    def __getitem__(self, name):
+        a = self.raw[name]
+        return bf16_bits_to_f32(a) if a.dtype == np.uint16 else a
+
+
+def draw_all(cfg: ModelConfig, seed: int = SEED_WEIGHTS) -> Dict[str, np.ndarray]:
+    """Every weight of cfg in storage form (float32, or uint16 bf16 bits)."""
+    return {n: draw_weight(cfg, n, seed) for n in weight_shapes(cfg)}
+
+
 def draw_ids(cfg: ModelConfig, batch: Optional[int] = None, seq: Optional[int] = None,
              seed: int = SEED_IDS) -> np.ndarray:
     """int32 [B, S] token ids uniform in [0, V). A shorter draw is a prefix of a longer

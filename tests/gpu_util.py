@@ -1,0 +1,61 @@
+"""Helpers shared by the GPU tests and the smoke check: move seeded host arrays to
+the device as torch tensors, and compare results. No step of the forward pass."""
+from __future__ import annotations
+
+import numpy as np
+
+
+def to_device(arr: np.ndarray):
+    """float32 array -> float32 tensor; uint16 (bf16 bits) -> bfloat16 tensor; on cuda."""
+    import torch
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def upload_weights(cfg, host: dict) -> dict:
+    return {n: to_device(a) for n, a in host.items()}
+
+
+def bf16_to_f32(t) -> np.ndarray:
+    """bfloat16 tensor -> float32 numpy (exact widening on the host)."""
+    import torch
+    bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def cosine(a, b) -> float:
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def err_over_scale(got, ref) -> float:
+    """max|got - ref| / max|ref| ("N9 · metalgemm", Theorem 1 error model)."""
+    ref = np.asarray(ref, np.float64)
+    return float(np.max(np.abs(np.asarray(got, np.float64) - ref)) / np.max(np.abs(ref)))
+
+
+def argmax_check(got_ids, ref_logits, got_logits):
+    """Argmax parity under the near-tie reading: where the oracle's top-1 margin exceeds
+    twice the row's max logit error the id must match exactly; otherwise the GPU id must
+    lie within 2 * error of the oracle's max. Returns (n_pinned, n_near_tie, failures)."""
+    ref = np.asarray(ref_logits, np.float64).reshape(-1, ref_logits.shape[-1])
+    got = np.asarray(got_logits, np.float64).reshape(ref.shape)
+    ids = np.asarray(got_ids).ravel()
+    pinned = near = 0
+    fails = []
+    for t in range(ref.shape[0]):
+        eps = float(np.max(np.abs(got[t] - ref[t])))
+        top2 = np.partition(ref[t], -2)[-2:]
+        margin = float(top2[1] - top2[0])
+        best = int(np.argmax(ref[t]))
+        if margin > 2 * eps:
+            pinned += 1
+            if ids[t] != best:
+                fails.append((t, int(ids[t]), best, margin, eps))
+        else:
+            near += 1
+            if ref[t, ids[t]] < ref[t, best] - 2 * eps:
+                fails.append((t, int(ids[t]), best, margin, eps))
+    return pinned, near, fails

@@ -1,0 +1,92 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+entry point include/fwd.h declares, validates configurations, and refuses to run
+compute without a gfx950 device instead of falling back to anything."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from decoder_only_transformer_bf16_amd import fwd
+from synth import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = open(os.path.join(ROOT, "include", "fwd.h")).read()
+
+
+def _declared():
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(fwd_\w+)\s*\(", HEADER, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(fwd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fwd.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_struct_layouts_match_header_order():
+    cfg_fields = re.search(r"typedef struct fwd_config \{(.*?)\} fwd_config;", HEADER, re.S).group(1)
+    names = re.findall(r"(\w+)(?:,|;)", cfg_fields.replace("const int32_t*", ""))
+    assert names == [f for f, _ in fwd.FwdConfig._fields_]
+    assert ctypes.sizeof(fwd.FwdConfig) == 80
+    lw = re.search(r"typedef struct fwd_layer_weights \{(.*?)\}", HEADER, re.S).group(1)
+    assert re.findall(r"\*\s*(\w+);", lw) == [f for f, _ in fwd.FwdLayerWeights._fields_]
+
+
+def test_no_device_here_means_unavailable_not_fallback():
+    if fwd.available():
+        pytest.skip("a gfx950 device is visible")
+    cfg, keep = fwd.make_config(wl.TINY_F32, 16)
+    w = fwd.FwdWeights(embed=1, final_norm=1, layers=None)
+    cfg0, keep0 = fwd.make_config(wl.TINY_F32.replace(n_layers=0), 16)
+    h = fwd.c_vp()
+    assert fwd.lib().fwd_create(ctypes.byref(cfg0), ctypes.byref(w), None, ctypes.byref(h)) == fwd.FWD_E_UNAVAILABLE
+    assert not h.value
+    # non-null (never dereferenced) pointers: the device check comes before any access
+    assert fwd.lib().fwd_gemm(16, 16, 16, 4, 8, 4, fwd.DTYPE["bf16"], None) == fwd.FWD_E_UNAVAILABLE
+    assert b"gfx950" in fwd.lib().fwd_last_error()
+
+
+def _create_rc(cfg, max_tokens=16):
+    c, keep = fwd.make_config(cfg, max_tokens)
+    s = fwd.FwdSizes()
+    return fwd.lib().fwd_output_sizes(ctypes.byref(c), 1, 16, ctypes.byref(s))
+
+
+@pytest.mark.parametrize("bad", [
+    dict(final_logit_softcap=-1.0), dict(final_logit_softcap=float("nan")), dict(final_logit_softcap=float("inf")),
+    dict(n_kv_heads=3), dict(head_dim=24), dict(rms_eps=0.0), dict(rope_theta=1.0), dict(sliding_window=-1),
+    dict(dtype="bf16"),  # tiny geometry is not a supported bf16 shape (head_dim 16)
+])
+def test_bad_configs_are_rejected(bad):
+    assert _create_rc(wl.TINY_F32.replace(**bad)) == fwd.FWD_E_CONFIG
+
+
+def test_output_sizes_are_the_one_source_of_truth():
+    for cfg in wl.MODELS.values():
+        s = fwd.output_sizes(cfg, cfg.batch, cfg.seq)
+        T = cfg.batch * cfg.seq
+        assert s["logits_elems"] == T * cfg.vocab
+        assert s["hidden_elems"] == (cfg.n_layers + 2) * T * cfg.hidden
+        assert s["argmax_elems"] == T
+        n_weights = sum(int(np.prod(shape)) for shape, kind in wl.weight_shapes(cfg).values() if kind == "matrix")
+        esize = 2 if cfg.dtype == "bf16" else 4
+        assert s["weight_bytes"] >= n_weights * esize
+    with pytest.raises(fwd.FwdError) as e:
+        fwd.output_sizes(wl.TINY_F32, -1, 4)
+    assert e.value.code == fwd.FWD_E_ARG
+
+
+def test_null_handle_and_empty_calls():
+    L = fwd.lib()
+    assert L.fwd_prefill(None, None, 1, 1, None) == fwd.FWD_E_ARG
+    L.fwd_destroy(None)
+    # empty problems are no-ops even without a device
+    assert L.fwd_gemm(None, None, None, 0, 8, 4, fwd.DTYPE["bf16"], None) == fwd.FWD_OK
+    assert L.fwd_gemm(None, None, None, 4, 7, 4, fwd.DTYPE["bf16"], None) == fwd.FWD_E_ARG
