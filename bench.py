@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Prefill throughput of the Llama-3-8B-shaped decoder on one MI355X.
+
+One step = one fwd_prefill of the whole forward pass over a batch of 8 x 2048
+synthetic token ids (32 layers, hidden 4096, 32/8 heads, head_dim 128, FFN 14336,
+vocab 128256, bf16 weights N(0, 0.02)), writing fp32 logits, per-position argmax
+and the fp32 hidden slots. Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line with tokens/s, the roofline record of the dominant kernel
+(gate/up projection + SwiGLU, timed with HIP events on the library's stream) and
+the CPU oracle's throughput on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "prefill tokens/s (Llama-3-8B shape, bf16); GEMM MFMA util vs peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_flops(cfg, B, S):
+    """Algorithmic flops of each kernel class for one prefill (multiply-add = 2)."""
+    T = B * S
+    H, Hq, Hkv, D, F, V, L = cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn, cfg.vocab, cfg.n_layers
+    kinds = cfg.kinds()
+    attn = 0
+    for l in range(L):
+        W = cfg.sliding_window if kinds[l] == "local" else 0
+        visible = sum(min(i + 1, W) if W > 0 else i + 1 for i in range(S))
+        attn += 4 * D * Hq * B * visible
+    return {
+        "qkv_rope": L * 2 * T * H * (Hq + 2 * Hkv) * D,
+        "attention": attn,
+        "o_proj": L * 2 * T * Hq * D * H,
+        "gate_up": L * 2 * T * H * 2 * F,
+        "down_proj": L * 2 * T * F * H,
+        "lm_head": 2 * T * H * V,
+    }
+
+
+def cpu_baseline(cfg, S):
+    """The CPU oracle (as it stands) on a bounded sample: one S-token row through
+    the embedding, final norm and LM head with 0 layers, then with 1 layer; the
+    difference prices one layer. Full-model seconds per row = t0 + L * t_layer."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from synth import workloads as wl
+
+    ids = wl.draw_ids(cfg)[:1, :S]
+    times = {}
+    for n in (0, 1):
+        c = cfg.replace(n_layers=n)
+        w = wl.LazyWeights(c, cache=True)
+        for name in wl.weight_shapes(c):
+            w[name]                                   # draw outside the timed region
+        t = time.perf_counter()
+        oracle.forward(c, w, ids, want_logits=True, want_hidden=False)
+        times[n] = time.perf_counter() - t
+        del w
+    t_layer = max(times[1] - times[0], 1e-9)
+    per_row = times[0] + cfg.n_layers * t_layer
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": S / per_row,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"1 row x {S} tokens: embedding+final norm+LM head ({times[0]:.1f} s) and one decoder layer "
+                   f"({t_layer:.1f} s) timed, scaled to {cfg.n_layers} layers; float64 numpy oracle"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hidden", action="store_true", help="skip the hidden-slot output")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the batch rows are independent: more GPUs would each run their own share)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from decoder_only_transformer_bf16_amd import fwd
+    from synth import workloads as wl
+    from tests.gpu_util import to_device
+
+    cfg = wl.LLAMA3_8B
+    B, S = cfg.batch, cfg.seq
+    T = B * S
+    torch.cuda.set_device(0)
+    if not fwd.available():
+        raise SystemExit("libfwd.so sees no gfx950 device")
+
+    t0 = time.time()
+    weights = {}
+    for name in wl.weight_shapes(cfg):
+        weights[name] = to_device(wl.draw_weight(cfg, name))
+    stream = torch.cuda.Stream()
+    model = fwd.Model(cfg, weights, max_tokens=T, stream=stream)
+    del weights
+    torch.cuda.empty_cache()
+    ids = wl.draw_ids(cfg)
+    logits = torch.empty((B, S, cfg.vocab), dtype=torch.float32, device="cuda")
+    argmax = torch.empty((B, S), dtype=torch.int32, device="cuda")
+    hidden = None if args.no_hidden else torch.empty((cfg.n_layers + 2, B, S, cfg.hidden), dtype=torch.float32,
+                                                     device="cuda")
+    log(f"setup {time.time() - t0:.1f} s (weights drawn, uploaded, packed)")
+
+    for i in range(args.warmup):
+        model.prefill_into(ids, logits, hidden, argmax)
+        log(f"warmup {i + 1}/{args.warmup} done")
+    model.set_timing(True)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(args.steps):
+        model.prefill_into(ids, logits, hidden, argmax)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t
+    timing = model.timing()
+    ms_per_step = elapsed * 1000.0 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step")
+
+    flops = kernel_flops(cfg, B, S)
+    total_flops = sum(flops.values())
+    kernels = {}
+    for k, v in timing.items():
+        if not v["launches"]:
+            continue
+        rec = {"ms_per_launch": v["ms"] / v["launches"], "launches_per_step": v["launches"] / args.steps,
+               "ms_per_step": v["ms"] / args.steps}
+        if k in flops:
+            per_launch = flops[k] / (v["launches"] / args.steps)
+            rec["tflops"] = per_launch / (rec["ms_per_launch"] * 1e-3) / 1e12
+            rec["frac_of_bf16_peak"] = rec["tflops"] / PEAK_BF16_TFLOPS
+        kernels[k] = rec
+    dom = kernels["gate_up"]
+    gate_up_flops_per_launch = 2 * T * cfg.hidden * 2 * cfg.ffn
+    achieved = gate_up_flops_per_launch / (dom["ms_per_launch"] * 1e-3) / 1e12
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "gate_up_swiglu_llama3_8b_traffic.json")
+    if os.path.exists(tfile):
+        try:
+            tr = json.load(open(tfile))
+            from decoder_only_transformer_bf16_amd import _build
+            if tr.get("source_digest") == _build.source_digest():
+                traffic = tr["bytes_per_launch"]
+        except Exception as e:  # stale or unreadable record: report none
+            log(f"traffic record ignored: {e}")
+
+    result = {
+        "metric": METRIC,
+        "value": T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, uniform token ids)",
+        "config": {"workload": "llama3-8b-shape prefill: 8 x 2048 tokens, 32 layers, hidden 4096, 32/8 heads x 128, "
+                               "ffn 14336, vocab 128256; outputs fp32 logits, argmax"
+                               + ("" if args.no_hidden else ", fp32 hidden slots"),
+                   "batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "gate_up projection + SwiGLU epilogue [16384, 4096 -> 2 x 14336]",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "end_to_end": {"algorithmic_tflop_per_step": total_flops / 1e12,
+                       "tflops": total_flops / (ms_per_step * 1e-3) / 1e12,
+                       "frac_of_bf16_peak": total_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "kernels": kernels,
+    }
+    model.close()
+    del logits, hidden, argmax
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, S)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

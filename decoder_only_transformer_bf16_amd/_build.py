@@ -50,3 +50,13 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+
+
+def source_digest(files=("gemm.hip", "common.h", "kernels.h")) -> str:
+    """sha256 over the GEMM kernel sources (ties stored counter data to the kernel it measured)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]

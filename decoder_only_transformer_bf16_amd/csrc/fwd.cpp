@@ -23,6 +23,13 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
+#define TIMED(model, kind, expr)              \
+  do {                                        \
+    if (int rc_ = (model)->tick(kind)) return rc_; \
+    HIP_TRY(expr);                            \
+    if (int rc_ = (model)->tock()) return rc_; \
+  } while (0)
+
 #define HIP_TRY(expr)                                                                              \
   do {                                                                                             \
     hipError_t e_ = (expr);                                                                        \
@@ -146,6 +153,48 @@ struct fwd_model {
   float* logits_ws = nullptr;
   float2* rope_cs = nullptr;
 
+  // per-kernel-class event timing (fwd_set_timing)
+  bool timing = false;
+  std::vector<hipEvent_t> events;
+  size_t events_used = 0;
+  std::vector<int> marks;  // kernel class of each (start, stop) event pair
+  double class_ms[FWD_KERNEL_CLASSES] = {};
+  int64_t class_n[FWD_KERNEL_CLASSES] = {};
+
+  // Record the start event of a launch of `kind` (no-op when timing is off).
+  int tick(int kind) {
+    if (!timing) return FWD_OK;
+    if (events_used + 2 > events.size()) {
+      for (int i = 0; i < 2; ++i) {
+        hipEvent_t e;
+        HIP_TRY(hipEventCreate(&e));
+        events.push_back(e);
+      }
+    }
+    marks.push_back(kind);
+    HIP_TRY(hipEventRecord(events[events_used], stream));
+    return FWD_OK;
+  }
+  int tock() {
+    if (!timing) return FWD_OK;
+    HIP_TRY(hipEventRecord(events[events_used + 1], stream));
+    events_used += 2;
+    return FWD_OK;
+  }
+  // After the stream is synchronised: fold the recorded pairs into the totals.
+  int collect() {
+    if (!timing) return FWD_OK;
+    for (size_t i = 0; i < marks.size(); ++i) {
+      float ms = 0.f;
+      HIP_TRY(hipEventElapsedTime(&ms, events[2 * i], events[2 * i + 1]));
+      class_ms[marks[i]] += ms;
+      class_n[marks[i]] += 1;
+    }
+    marks.clear();
+    events_used = 0;
+    return FWD_OK;
+  }
+
   int alloc(void** p, int64_t bytes) {
     *p = nullptr;
     if (bytes <= 0) return FWD_OK;
@@ -157,6 +206,7 @@ struct fwd_model {
     if (stream) (void)hipStreamSynchronize(stream);
     else (void)hipDeviceSynchronize();
     for (void* p : allocs) (void)hipFree(p);
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
   }
 };
 
@@ -371,13 +421,15 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
   const int64_t TH = T * H;
   float* hidden = o.hidden;
 
+  m->marks.clear();
+  m->events_used = 0;
   HIP_TRY(hipMemcpyAsync(m->ids, ids_host, T * 4, hipMemcpyHostToDevice, s));
   HIP_TRY(hipMemsetAsync(m->flag, 0, 4, s));
 
   float* cur = hidden ? hidden : m->x;
-  HIP_TRY(fwdk::embed(dt, m->ids, m->embed, cur, M, H, m->embed_scale, s));
+  TIMED(m, FWD_KERNEL_EMBED, fwdk::embed(dt, m->ids, m->embed, cur, M, H, m->embed_scale, s));
   // first layer's input norm; every later sublayer input norm is fused below
-  if (L > 0) HIP_TRY(fwdk::rmsnorm(dt, cur, m->layers[0].attn_norm, m->n, nullptr, M, H, eps, s));
+  if (L > 0) TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, cur, m->layers[0].attn_norm, m->n, nullptr, M, H, eps, s));
 
   const int ldvt = (int)round_up(S, 8);
   char* qk = (char*)m->qk;
@@ -391,7 +443,7 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
 
     // attention sublayer (its input norm is already in m->n)
     fwdk::RopeArgs ra{m->qk, m->vt, m->rope_cs, Hq, Hkv, D, S, ldvt};
-    HIP_TRY(fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, s));
+    TIMED(m, FWD_KERNEL_QKV_ROPE, fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, s));
     fwdk::AttnArgs aa{};
     aa.q = qk;
     aa.k = qk + (int64_t)Hq * D * g.esize;
@@ -406,50 +458,51 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
     aa.Hkv = Hkv;
     aa.D = D;
     aa.window = m->kinds[l] == FWD_LAYER_LOCAL ? m->cfg.sliding_window : 0;
-    HIP_TRY(fwdk::attention(dt, aa, s));
+    TIMED(m, FWD_KERNEL_ATTENTION, fwdk::attention(dt, aa, s));
     if (!sandwich) {
-      HIP_TRY(fwdk::gemm_residual(dt, m->o, w.wo, xin, xmid, M, H, Hq * D, s));
-      HIP_TRY(fwdk::rmsnorm(dt, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, s));
+      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_residual(dt, m->o, w.wo, xin, xmid, M, H, Hq * D, s));
+      TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, s));
     } else {
-      HIP_TRY(fwdk::gemm_store(dt, m->o, w.wo, m->u, H, M, H, Hq * D, 0.f, s));
-      HIP_TRY(fwdk::add_norm(dt, xin, m->u, w.post_attn, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, s));
+      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_store(dt, m->o, w.wo, m->u, H, M, H, Hq * D, 0.f, s));
+      TIMED(m, FWD_KERNEL_NORM, fwdk::add_norm(dt, xin, m->u, w.post_attn, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, s));
     }
 
     // feed-forward sublayer
-    HIP_TRY(fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, s));
+    TIMED(m, FWD_KERNEL_GATE_UP, fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, s));
     float* final32 = (last && hidden) ? hidden + (int64_t)(L + 1) * TH : nullptr;
     if (!sandwich) {
-      HIP_TRY(fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, s));
-      HIP_TRY(fwdk::rmsnorm(dt, xout, next_norm, m->n, final32, M, H, eps, s));
+      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, s));
+      TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xout, next_norm, m->n, final32, M, H, eps, s));
     } else {
-      HIP_TRY(fwdk::gemm_store(dt, m->a, w.wdown, m->u, H, M, H, F, 0.f, s));
-      HIP_TRY(fwdk::add_norm(dt, xmid, m->u, w.post_ffn, xout, next_norm, m->n, final32, M, H, eps, s));
+      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_store(dt, m->a, w.wdown, m->u, H, M, H, F, 0.f, s));
+      TIMED(m, FWD_KERNEL_NORM, fwdk::add_norm(dt, xmid, m->u, w.post_ffn, xout, next_norm, m->n, final32, M, H, eps, s));
     }
     cur = xout;
   }
   if (L == 0) {
     float* final32 = hidden ? hidden + TH : nullptr;
-    HIP_TRY(fwdk::rmsnorm(dt, cur, m->final_norm, m->n, final32, M, H, eps, s));
+    TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, cur, m->final_norm, m->n, final32, M, H, eps, s));
   }
 
   // tied LM head (+ softcap) and argmax
   const float cap = m->cfg.final_logit_softcap;
   int32_t* am = o.argmax ? o.argmax : m->amax;
   if (o.logits) {
-    HIP_TRY(fwdk::gemm_store(dt, m->n, m->embed, o.logits, V, M, V, H, cap, s));
-    HIP_TRY(fwdk::argmax_rows(o.logits, V, M, V, am, m->flag, s));
+    TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, m->n, m->embed, o.logits, V, M, V, H, cap, s));
+    TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(o.logits, V, M, V, am, m->flag, s));
   } else {
     const int64_t chunk = g.logit_chunk;
     for (int64_t r0 = 0; r0 < T; r0 += chunk) {
       const int rows = (int)std::min<int64_t>(chunk, T - r0);
       const char* nrow = (const char*)m->n + r0 * H * g.esize;
-      HIP_TRY(fwdk::gemm_store(dt, nrow, m->embed, m->logits_ws, V, rows, V, H, cap, s));
-      HIP_TRY(fwdk::argmax_rows(m->logits_ws, V, rows, V, am + r0, m->flag, s));
+      TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, nrow, m->embed, m->logits_ws, V, rows, V, H, cap, s));
+      TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(m->logits_ws, V, rows, V, am + r0, m->flag, s));
     }
   }
   int flag = 0;
   HIP_TRY(hipMemcpyAsync(&flag, m->flag, 4, hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
+  if (int rc = m->collect()) return rc;
   if (flag) return fail(FWD_E_NONFINITE, "non-finite logits");
   return FWD_OK;
 }
@@ -501,6 +554,25 @@ int fwd_rmsnorm(const float* x, const void* w, void* y, int32_t rows, int32_t hi
   if (!x || !w || !y) return fail(FWD_E_ARG, "NULL buffer");
   if (!device_is_gfx950()) return fail(FWD_E_UNAVAILABLE, "no gfx950 device is available");
   HIP_TRY(fwdk::rmsnorm(DType(dtype), x, (const float*)w, y, nullptr, rows, hidden, eps, (hipStream_t)hip_stream));
+  return FWD_OK;
+}
+
+int fwd_set_timing(fwd_model* m, int32_t enable) {
+  if (!m) return fail(FWD_E_ARG, "model is NULL");
+  m->timing = enable != 0;
+  m->marks.clear();
+  m->events_used = 0;
+  for (int k = 0; k < FWD_KERNEL_CLASSES; ++k) {
+    m->class_ms[k] = 0.0;
+    m->class_n[k] = 0;
+  }
+  return FWD_OK;
+}
+
+int fwd_get_timing(const fwd_model* m, int32_t kernel_class, double* total_ms, int64_t* launches) {
+  if (!m || kernel_class < 0 || kernel_class >= FWD_KERNEL_CLASSES) return fail(FWD_E_ARG, "bad model or class");
+  if (total_ms) *total_ms = m->class_ms[kernel_class];
+  if (launches) *launches = m->class_n[kernel_class];
   return FWD_OK;
 }
 

@@ -31,7 +31,8 @@ NORM = {"pre": 0, "sandwich": 1}
 LAYER = {"global": 0, "local": 1}
 
 EXPORTS = ("fwd_available", "fwd_create", "fwd_output_sizes", "fwd_prefill", "fwd_gemm", "fwd_attention",
-           "fwd_rmsnorm", "fwd_destroy", "fwd_last_error")
+           "fwd_rmsnorm", "fwd_set_timing", "fwd_get_timing", "fwd_destroy", "fwd_last_error")
+KERNEL_CLASSES = ("embed", "norm", "qkv_rope", "attention", "o_proj", "gate_up", "down_proj", "lm_head", "argmax")
 
 c_i32, c_i64, c_f32, c_f64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.fwd_attention.restype = c_i32
         L.fwd_rmsnorm.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_f32, c_i32, c_vp]
         L.fwd_rmsnorm.restype = c_i32
+        L.fwd_set_timing.argtypes = [c_vp, c_i32]
+        L.fwd_set_timing.restype = c_i32
+        L.fwd_get_timing.argtypes = [c_vp, c_i32, ctypes.POINTER(c_f64), ctypes.POINTER(c_i64)]
+        L.fwd_get_timing.restype = c_i32
         L.fwd_destroy.argtypes = [c_vp]
         L.fwd_destroy.restype = None
         L.fwd_last_error.restype = ctypes.c_char_p
@@ -172,6 +177,19 @@ class Model:
             self.close()
         except Exception:
             pass
+
+    def set_timing(self, enable: bool) -> None:
+        """Per-kernel-class HIP-event timing of later prefills (clears the totals)."""
+        _check(lib().fwd_set_timing(self._h, 1 if enable else 0))
+
+    def timing(self) -> Dict[str, Dict[str, float]]:
+        """{class: {"ms": total milliseconds, "launches": n}} since set_timing(True)."""
+        out = {}
+        for i, name in enumerate(KERNEL_CLASSES):
+            ms, n = c_f64(), c_i64()
+            _check(lib().fwd_get_timing(self._h, i, ctypes.byref(ms), ctypes.byref(n)))
+            out[name] = {"ms": ms.value, "launches": n.value}
+        return out
 
     def prefill_into(self, ids: np.ndarray, logits=None, hidden=None, argmax=None) -> None:
         """fwd_prefill writing into caller-allocated device tensors (any may be None)."""

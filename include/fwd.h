@@ -211,6 +211,26 @@ int fwd_attention(const void* q, const void* k, const void* v_t, void* o, int32_
 int fwd_rmsnorm(const float* x, const void* w, void* y, int32_t rows, int32_t hidden, float eps,
                 int32_t dtype, void* hip_stream);
 
+/*
+ * Per-kernel timing of fwd_prefill with HIP events recorded on the model's stream
+ * around every launch (off by default). Kernel classes:
+ */
+#define FWD_KERNEL_EMBED 0         /* scaled embedding gather                      */
+#define FWD_KERNEL_NORM 1          /* RMSNorm, and the fused sandwich add + norm   */
+#define FWD_KERNEL_QKV_ROPE 2      /* QKV projection with the RoPE epilogue        */
+#define FWD_KERNEL_ATTENTION 3     /* causal GQA attention                         */
+#define FWD_KERNEL_O_PROJ 4        /* output projection (+ residual add)           */
+#define FWD_KERNEL_GATE_UP 5       /* gate/up projection with the SwiGLU epilogue  */
+#define FWD_KERNEL_DOWN_PROJ 6     /* down projection (+ residual add)             */
+#define FWD_KERNEL_LM_HEAD 7       /* tied LM head (+ softcap)                     */
+#define FWD_KERNEL_ARGMAX 8        /* per-position argmax + non-finite check      */
+#define FWD_KERNEL_CLASSES 9
+/* enable != 0 turns timing on and clears the accumulated totals; 0 turns it off. */
+int fwd_set_timing(fwd_model* m, int32_t enable);
+/* Accumulated milliseconds and launch count of one kernel class since the last
+ * fwd_set_timing(m, 1). Errors: FWD_E_ARG. */
+int fwd_get_timing(const fwd_model* m, int32_t kernel_class, double* total_ms, int64_t* launches);
+
 /* Release a model and everything it allocated (waits for its stream first).
  * NULL is a no-op ("N9 · metalgemm", Theorem 1: Free / Reset reclaim the table). */
 void fwd_destroy(fwd_model* m);
