@@ -27,12 +27,14 @@ constexpr int KB = 32;  // keys per slice
 // g of the transposed score tile ends up owning keys 8 g .. 8 g + 7.
 __device__ __forceinline__ int key_row(int j) { return ((j >> 2) & 1) * 16 + (j >> 3) * 4 + (j & 3); }
 
+// LDS layouts (16-byte chunks XOR-swizzled so that the 16 lanes an LDS read serves
+// together, which read one chunk column of 16 consecutive rows, hit distinct banks).
 template <int D>
-__device__ __forceinline__ int k_off(int row, int chunk) {  // K tile: [32 rows][D], 16-byte chunks
-  return row * D + ((chunk ^ (row & 7)) << 3);
+__device__ __forceinline__ int k_off(int row, int chunk) {  // K tile: [32 rows][D]
+  return row * D + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 3);
 }
 __device__ __forceinline__ int v_off(int d, int chunk) {  // Vᵀ tile: [D rows][32 keys], 4 chunks per row
-  return d * KB + ((chunk ^ ((d >> 1) & 3)) << 3);
+  return d * KB + ((chunk ^ ((d >> 2) & 3)) << 3);
 }
 
 template <int D>
@@ -266,6 +268,43 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, float scale_lo
   }
 }
 
+// 64 tokens x 64 value columns per workgroup through an LDS tile.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ src, int64_t ld, T* __restrict__ vt,
+                                                         int ldvt, int S, int C) {
+  constexpr int kV = 16 / sizeof(T);  // elements per 16-byte access
+  constexpr int kPad = kV;
+  __shared__ T tile[64][64 + kPad];
+  const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64, b = blockIdx.z;
+  for (int q = threadIdx.x; q < 64 * 64 / kV; q += 256) {
+    const int r = q / (64 / kV), cv = (q % (64 / kV)) * kV;
+    const int t = t0 + r, c = c0 + cv;
+    T v[kV];
+    if (t < S && c < C) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src + ((int64_t)b * S + t) * ld + c);
+      __builtin_memcpy(v, &x, 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kV; ++e) v[e] = T(0);
+    }
+#pragma unroll
+    for (int e = 0; e < kV; ++e) tile[r][cv + e] = v[e];
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 64 * 64 / kV; q += 256) {
+    const int ci = q / (64 / kV), tv = (q % (64 / kV)) * kV;
+    const int c = c0 + ci, t = t0 + tv;
+    if (c < C && t < S) {
+      T v[kV];
+#pragma unroll
+      for (int e = 0; e < kV; ++e) v[e] = tile[tv + e][ci];
+      u32x4_t x;
+      __builtin_memcpy(&x, v, 16);
+      *reinterpret_cast<u32x4_t*>(vt + ((int64_t)b * C + c) * ldvt + t) = x;
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
   const float sl = kLog2e / sqrtf((float)D);
@@ -298,6 +337,19 @@ hipError_t launch_f32(const AttnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t transpose_v(DType dt, const void* src, int64_t ld, void* vt, int ldvt, int B, int S, int C,
+                       hipStream_t s) {
+  if (B <= 0 || S <= 0) return hipSuccess;
+  const dim3 grid((S + 63) / 64, (C + 63) / 64, B);
+  if (dt == DType::BF16)
+    hipLaunchKernelGGL(transpose_v_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)src, ld, (bf16_t*)vt, ldvt,
+                       S, C);
+  else
+    hipLaunchKernelGGL(transpose_v_kernel<float>, grid, dim3(256), 0, s, (const float*)src, ld, (float*)vt, ldvt, S,
+                       C);
+  return hipGetLastError();
+}
 
 bool attention_supported(DType dt, int D) {
   if (dt == DType::BF16) return D == 64 || D == 128 || D == 256;

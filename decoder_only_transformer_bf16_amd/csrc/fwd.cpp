@@ -92,7 +92,7 @@ struct Geometry {
     auto r = [](int64_t b) { return round_up(b, 256); };
     int64_t w = 2 * r(T * H * 4);                       // residual stream, mid-layer copy
     w += r(T * H * esize);                              // normalised activations
-    w += r(T * (Hq + Hkv) * D * esize);                 // rotated q | k
+    w += r(T * (Hq + 2 * Hkv) * D * esize);             // rotated q | rotated k | v
     w += r(8 * T * Hkv * D * esize);                    // transposed v, padded keys
     w += r(T * Hq * D * esize);                         // attention output
     w += r(T * F * esize);                              // SwiGLU output
@@ -373,7 +373,7 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     if (int rc = m->alloc((void**)&m->x, T * g.H * 4)) return rc;
     if (int rc = m->alloc((void**)&m->xb, T * g.H * 4)) return rc;
     if (int rc = m->alloc(&m->n, T * g.H * g.esize)) return rc;
-    if (int rc = m->alloc(&m->qk, T * (g.Hq + g.Hkv) * g.D * g.esize)) return rc;
+    if (int rc = m->alloc(&m->qk, T * (g.Hq + 2 * g.Hkv) * g.D * g.esize)) return rc;
     if (int rc = m->alloc(&m->vt, 8 * T * g.Hkv * g.D * g.esize)) return rc;
     if (int rc = m->alloc(&m->o, T * g.Hq * g.D * g.esize)) return rc;
     if (int rc = m->alloc(&m->a, T * g.F * g.esize)) return rc;
@@ -442,14 +442,17 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
     const float* next_norm = last ? m->final_norm : m->layers[l + 1].attn_norm;
 
     // attention sublayer (its input norm is already in m->n)
-    fwdk::RopeArgs ra{m->qk, m->vt, m->rope_cs, Hq, Hkv, D, S, ldvt};
+    fwdk::RopeArgs ra{m->qk, m->rope_cs, Hq, Hkv, D, S};
     TIMED(m, FWD_KERNEL_QKV_ROPE, fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, s));
+    const int64_t ldqkv = (int64_t)(Hq + 2 * Hkv) * D;
+    TIMED(m, FWD_KERNEL_V_TRANSPOSE,
+          fwdk::transpose_v(dt, qk + (int64_t)(Hq + Hkv) * D * g.esize, ldqkv, m->vt, ldvt, B, S, Hkv * D, s));
     fwdk::AttnArgs aa{};
     aa.q = qk;
     aa.k = qk + (int64_t)Hq * D * g.esize;
     aa.vt = m->vt;
     aa.o = m->o;
-    aa.ldq = aa.ldk = (int64_t)(Hq + Hkv) * D;
+    aa.ldq = aa.ldk = ldqkv;
     aa.ldo = (int64_t)Hq * D;
     aa.ldvt = ldvt;
     aa.B = B;

@@ -7,6 +7,8 @@
 // (BM/WM) x (BN/WN) sub-tile, K staged through LDS in 64-wide slices, double
 // buffered, with the next slice's global loads in flight during the MFMAs.
 // f32 path: an LDS-tiled VALU kernel (the fp32 configuration is tiny).
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -66,31 +68,26 @@ struct EpiSwiGLU {
 
 template <int C, typename T>
 struct EpiRope {
-  T* qk;
-  T* vt;
+  T* qkv;  // [M, (Hq + 2 Hkv) D]: rotated q, rotated k, plain v, natural dim order
   const float2* cs;
-  int Hq, Hkv, D, S, ldvt;
+  int Hq, Hkv, D, S;
   __device__ __forceinline__ void pair(int row, int c, float v0, float v1, bool ok0, bool) const {
     if (!ok0) return;
     const int qsz = Hq * D, ksz = Hkv * D;
-    const int b = row / S, t = row - b * S;
+    T* out = qkv + (int64_t)row * (qsz + 2 * ksz);
     if (c < qsz + ksz) {
+      const int t = row % S;
       const int sec = c < qsz ? 0 : qsz;
       const int cc = c - sec;
       const int head = cc / D, pd = cc - head * D;
       const int k = (pd / (2 * C)) * C + (pd % C);  // rotation index in [0, D/2)
       const float2 r = cs[(int64_t)t * (D / 2) + k];
-      const float a = v0 * r.x - v1 * r.y;
-      const float bb = v0 * r.y + v1 * r.x;
-      T* dst = qk + (int64_t)row * (qsz + ksz) + sec + head * D + k;
-      Elem<T>::store(dst, a);
-      Elem<T>::store(dst + D / 2, bb);
-    } else {
-      const int cc = c - qsz - ksz;  // value columns are not permuted
-      const int g = cc / D, d = cc - g * D;
-      T* dst = vt + ((int64_t)(b * Hkv + g) * D + d) * ldvt + t;
-      Elem<T>::store(dst, v0);
-      Elem<T>::store(dst + (int64_t)C * ldvt, v1);
+      T* dst = out + sec + head * D + k;
+      Elem<T>::store(dst, v0 * r.x - v1 * r.y);
+      Elem<T>::store(dst + D / 2, v0 * r.y + v1 * r.x);
+    } else {  // value columns are not permuted
+      Elem<T>::store(out + c, v0);
+      Elem<T>::store(out + c + C, v1);
     }
   }
 };
@@ -114,56 +111,85 @@ __device__ __forceinline__ void tile_coords(int pid, int nTM, int nTN, int& tm, 
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
-constexpr int BK = 64;  // K slice staged in LDS: 8 chunks of 16 bytes per row
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// LDS element offset of 16-byte chunk c of tile row r (XOR swizzle on chunks so
-// that the 32-row fragment reads and the row-wise writes spread over all banks).
-__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+// Physical 16-byte chunk of logical chunk c in row r of a tile whose rows hold BK
+// bf16. gfx950's LDS serves a ds_read_b128 16 lanes (256 bytes, 64 banks) at a
+// time; a fragment read touches one chunk column of 16 consecutive rows, so the
+// swizzle must give those 16 rows distinct (row parity, chunk) bank slots. For
+// 128-byte rows, c ^ (r & 7) ^ ((r >> 3) & 1) does (and 8 consecutive rows still
+// land on 8 distinct chunks).
+template <int BK>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (BK == 64) return c ^ (r & 7) ^ ((r >> 3) & 1);
+  else return c ^ ((r >> 2) & 3);  // 64-byte rows: 16 rows -> (r & 3, chunk) distinct
+}
+template <int BK>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return r * BK + (swz<BK>(r, c) << 3);
+}
 
-template <int ROWS, int NT>
-struct SliceLoader {
-  static constexpr int kPer = ROWS * (BK / 8) / NT;
-  static_assert(kPer * NT == ROWS * (BK / 8), "tile rows must fill the workgroup");
-  u32x4_t v[kPer];
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ base, int64_t ld, int row0, int nrows, int k0,
-                                       int K, int tid) {
-#pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int q = tid + p * NT;
-      const int r = q >> 3, c = q & 7;
-      const int gr = row0 + r, gk = k0 + c * 8;
-      if (gr < nrows && gk < K)
-        v[p] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)gr * ld + gk);
-      else
-        v[p] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
-#pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int q = tid + p * NT;
-      *reinterpret_cast<u32x4_t*>(lds + lds_off(q >> 3, q & 7)) = v[p];
-    }
-  }
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 dword3: 32-bit data
+// format, the value untyped loads require). Loads whose offset lies past `bytes`
+// return zero, which pads the ragged edges of a tile without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// Global -> LDS copy of 1 KiB of a BK-wide K slice of a ROWS-row operand tile with
+// buffer_load_dwordx4 ... lds (no VGPR staging): 64 lanes x 16 bytes. Lane l lands
+// at byte 16 l of block `blk`, i.e. tile row blk * (64 / CH) + l / CH and physical
+// chunk l % CH, so it fetches the logical chunk the swizzled layout keeps there.
+template <int BK>
+__device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, bf16_t* lds, int K, int k0, int blk, int lane) {
+  constexpr int CH = BK / 8, RPB = 64 / CH;  // chunks per row, rows per 1 KiB block
+  const int row = blk * RPB + lane / CH;
+  const int kk = k0 + swz<BK>(row, lane % CH) * 8;  // the swizzle is an involution
+  const uint32_t off = kk < K ? (uint32_t)(row * K + kk) * 2u : 0x80000000u;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + blk * 512), 16, off, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Tile configuration: BM x BN output tile, BK-wide K slices, STAGES LDS buffers,
+// WM x WN wavefronts (each owning a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles).
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = NW * 64;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32, KS = BK / 16;
+  static constexpr int LOADS_A = BM * (BK / 8) / 64 / NW;      // 1 KiB buffer loads per wave per slice
+  static constexpr int LOADS = (BM + BN) * (BK / 8) / 64 / NW;
+  static_assert(LOADS_A * NW * 64 == BM * (BK / 8) && LOADS * NW * 64 == (BM + BN) * (BK / 8), "load split");
+  static constexpr int LDS_BYTES = STAGES * (BM + BN) * BK * 2;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(TN % 2 == 0, "pair epilogues need an even number of 32-column sub-tiles");
+  static_assert(KS % 2 == 0, "fragment register buffers alternate per sub-step");
 };
 
-template <int BM, int BN, int WM, int WN, class Epi>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(const bf16_t* __restrict__ X,
-                                                               const bf16_t* __restrict__ W, int M, int N,
-                                                               int K, Epi epi) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  static_assert(TN % 2 == 0, "pair epilogues need an even number of 32-column sub-tiles");
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][(BM + BN) * BK];
+template <class C, class Epi>
+__global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const bf16_t* __restrict__ X,
+                                                         const bf16_t* __restrict__ W, int M, int N, int K,
+                                                         Epi epi) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::STAGES, NW = C::NW;
+  constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN, KS = C::KS;
+  constexpr int SLICE = (BM + BN) * BK;  // elements per stage
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[ST * SLICE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave / C::WN, wn = wave % C::WN;
   const int nTM = (M + BM - 1) / BM, nTN = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(blockIdx.x, nTM, nTN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(X + (int64_t)m0 * K, (int64_t)min(BM, M - m0) * K * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + (int64_t)n0 * K, (int64_t)min(BN, N - n0) * K * 2);
 
   floatx16_t acc[TM][TN];
 #pragma unroll
@@ -171,43 +197,72 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(const bf16_t* __
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx16_t{};
 
-  SliceLoader<BM, NT> la;
-  SliceLoader<BN, NT> lb;
+  // Software pipeline. STAGES LDS buffers; slice t lives in buffer t % STAGES.
+  // Inside slice t, sub-step kk issues its TM x TN independent MFMAs, each followed
+  // by its share of the fragment reads for sub-step kk + 1. Halfway through the last
+  // sub-step (its fragments are in registers by then) one barrier both frees buffer
+  // t % STAGES and publishes slice t + 1; the second half of the MFMAs then carries
+  // the loads that refill the freed buffer with slice t + STAGES and the reads of
+  // slice t + 1's first fragments.
+  constexpr int MF = TM * TN, FR = TM + TN, H = MF / 2, LA = C::LOADS_A, LT = C::LOADS;
   const int nk = (K + BK - 1) / BK;
-  la.load(X, K, m0, M, 0, K, tid);
-  lb.load(W, K, n0, N, 0, K, tid);
-  la.store(lds[0], tid);
-  lb.store(lds[0] + BM * BK, tid);
-  __syncthreads();
-
+  auto issue_load = [&](int p, bf16_t* buf, int k0) {  // load p of this wave's share of one slice
+    if (p < LA) load_block<BK>(ra, buf, K, k0, wave + p * NW, lane);
+    else load_block<BK>(rb, buf + BM * BK, K, k0, wave + (p - LA) * NW, lane);
+  };
+#pragma unroll
+  for (int q = 0; q < ST; ++q)
+    if (q < nk)
+#pragma unroll
+      for (int p = 0; p < LT; ++p) issue_load(p, lds + q * SLICE, q * BK);
   const int lr = lane & 31, lk = lane >> 5;
+  const int arow = wm * WTM + lr, brow = BM + wn * WTN + lr;  // tile rows this lane reads (+32 i / +32 j)
+  bf16x8_t fa[2][TM], fb[2][TN];
+  auto read_frag = [&](const bf16_t* base, int f, int kk, int buf) {
+    if (f < TM) fa[buf][f] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(base + lds_off<BK>(arow + f * 32, kk * 2 + lk)));
+    else fb[buf][f - TM] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(base + lds_off<BK>(brow + (f - TM) * 32, kk * 2 + lk)));
+  };
+  if (nk > 1) wait_vmcnt<(ST - 1) * LT>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+#pragma unroll
+  for (int f = 0; f < FR; ++f) read_frag(lds, f, 0, 0);
+
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      la.load(X, K, m0, M, (kt + 1) * BK, K, tid);
-      lb.load(W, K, n0, N, (kt + 1) * BK, K, tid);
+    bf16_t* cur = lds + (kt % ST) * SLICE;
+    const bf16_t* nxt = lds + ((kt + 1) % ST) * SLICE;
+    const bool refill = kt + ST < nk;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int rb_ = kk & 1, wb = rb_ ^ 1;  // register buffers: read from rb_, prefetch into wb
+#pragma unroll
+      for (int x = 0; x < MF; ++x) {
+        if (kk == KS - 1 && x == H) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // all of slice kt is in registers
+          if (kt + 1 < nk) {
+            if (kt + ST - 1 < nk) wait_vmcnt<(ST - 2) * LT>();  // slice kt + 1 has landed
+            else wait_vmcnt<0>();
+          }
+          __syncthreads();
+        }
+        const int i = x % TM, j = x / TM;
+        acc[i][j] = mfma_32x32x16_bf16(fa[rb_][i], fb[rb_][j], acc[i][j]);
+        if (kk + 1 < KS) {
+#pragma unroll
+          for (int f = (x * FR) / MF; f < ((x + 1) * FR) / MF; ++f) read_frag(cur, f, kk + 1, wb);
+        } else if (x >= H) {
+          const int y = x - H;
+          // (on the last slice this reads a stale but in-bounds buffer; never used)
+#pragma unroll
+          for (int f = (y * FR) / (MF - H); f < ((y + 1) * FR) / (MF - H); ++f) read_frag(nxt, f, 0, wb);
+          if (refill) {
+#pragma unroll
+            for (int p = (y * LT) / (MF - H); p < ((y + 1) * LT) / (MF - H); ++p) issue_load(p, cur, (kt + ST) * BK);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    const bf16_t* As = lds[cur];
-    const bf16_t* Bs = lds[cur] + BM * BK;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t a[TM], b[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        a[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(As + lds_off(wm * WTM + i * 32 + lr, kk * 2 + lk)));
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        b[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Bs + lds_off(wn * WTN + j * 32 + lr, kk * 2 + lk)));
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16_bf16(a[i], b[j], acc[i][j]);
-    }
-    if (kt + 1 < nk) {
-      la.store(lds[cur ^ 1], tid);
-      lb.store(lds[cur ^ 1] + BM * BK, tid);
-    }
-    __syncthreads();
   }
 
   // Accumulator layout of v_mfma_f32_32x32x16: register r of lane l holds
@@ -225,6 +280,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(const bf16_t* __
       }
     }
 }
+
+template <class C, class Epi>
+hipError_t launch_cfg(const void* X, const void* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
+  const int grid = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<C, Epi>), dim3(grid), dim3(C::NT), 0, s, (const bf16_t*)X, (const bf16_t*)W,
+                     M, N, K, epi);
+  return hipGetLastError();
+}
+
+using CfgBig = Cfg<256, 256, 64, 2, 2, 4>;  // 8 wavefronts: two per SIMD
+using CfgSmall = Cfg<128, 128, 64, 2, 2, 2>;
 
 // ------------------------------------------------------------------ f32 VALU kernel
 // 64x64 output tile, 256 threads, 4x4 outputs per thread, K slices of 16.
@@ -276,16 +342,8 @@ template <class Epi>
 hipError_t launch_bf16(const void* X, const void* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 256) {
-    const int grid = ((M + 255) / 256) * ((N + 255) / 256);
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2, Epi>), dim3(grid), dim3(256), 0, s,
-                       (const bf16_t*)X, (const bf16_t*)W, M, N, K, epi);
-  } else {
-    const int grid = ((M + 127) / 128) * ((N + 127) / 128);
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, Epi>), dim3(grid), dim3(256), 0, s,
-                       (const bf16_t*)X, (const bf16_t*)W, M, N, K, epi);
-  }
-  return hipGetLastError();
+  if (big >= 256) return launch_cfg<CfgBig>(X, W, M, N, K, epi, s);
+  return launch_cfg<CfgSmall>(X, W, M, N, K, epi, s);
 }
 
 template <class Epi>
@@ -319,10 +377,8 @@ hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, i
 hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, hipStream_t s) {
   const int N = (r.Hq + 2 * r.Hkv) * r.D;
   if (dt == DType::BF16)
-    return launch_bf16(X, W, M, N, K,
-                       EpiRope<32, bf16_t>{(bf16_t*)r.qk, (bf16_t*)r.vt, r.cs, r.Hq, r.Hkv, r.D, r.S, r.ldvt}, s);
-  return launch_f32(X, W, M, N, K,
-                    EpiRope<1, float>{(float*)r.qk, (float*)r.vt, r.cs, r.Hq, r.Hkv, r.D, r.S, r.ldvt}, s);
+    return launch_bf16(X, W, M, N, K, EpiRope<32, bf16_t>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S}, s);
+  return launch_f32(X, W, M, N, K, EpiRope<1, float>{(float*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S}, s);
 }
 
 }  // namespace fwdk

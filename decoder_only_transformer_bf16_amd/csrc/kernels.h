@@ -24,13 +24,12 @@ hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xi
 // a[M, F] = silu(g) * u with W packed as interleaved gate/up chunks (N = 2F).
 hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, hipStream_t s);
 // QKV projection with RoPE on q and k; N = (Hq + 2 Hkv) D with packed q/k rows.
-// Writes qk [M, (Hq + Hkv) D] (rotated, natural dim order) and
-// vt [B, Hkv, D, ldvt] (values transposed). Rows are b * S + t.
+// Writes qkv [M, (Hq + 2 Hkv) D]: rotated q heads, rotated k heads, then the value
+// heads, each in natural dim order. Rows are b * S + t (t = position).
 struct RopeArgs {
-  void* qk;
-  void* vt;
+  void* qkv;
   const float2* cs;  // [S_max, D / 2] (cos, sin)
-  int Hq, Hkv, D, S, ldvt;
+  int Hq, Hkv, D, S;
 };
 hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, hipStream_t s);
 
@@ -45,6 +44,10 @@ struct AttnArgs {
   int B, S, Hq, Hkv, D, window;
 };
 hipError_t attention(DType dt, const AttnArgs& a, hipStream_t s);
+// vt[b, c, t] = src[(b * S + t) * ld + c] for c < C = Hkv * D (values transposed so that
+// keys are contiguous); rows of vt are ldvt long (ldvt >= S rounded up to 8).
+hipError_t transpose_v(DType dt, const void* src, int64_t ld, void* vt, int ldvt, int B, int S, int C,
+                       hipStream_t s);
 bool attention_supported(DType dt, int D);
 
 // ---- row kernels ----

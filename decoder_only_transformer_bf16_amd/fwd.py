@@ -32,7 +32,8 @@ LAYER = {"global": 0, "local": 1}
 
 EXPORTS = ("fwd_available", "fwd_create", "fwd_output_sizes", "fwd_prefill", "fwd_gemm", "fwd_attention",
            "fwd_rmsnorm", "fwd_set_timing", "fwd_get_timing", "fwd_destroy", "fwd_last_error")
-KERNEL_CLASSES = ("embed", "norm", "qkv_rope", "attention", "o_proj", "gate_up", "down_proj", "lm_head", "argmax")
+KERNEL_CLASSES = ("embed", "norm", "qkv_rope", "attention", "o_proj", "gate_up", "down_proj", "lm_head", "argmax",
+                  "v_transpose")
 
 c_i32, c_i64, c_f32, c_f64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
