@@ -159,41 +159,58 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, float scale_
           for (int nq = 0; nq < NQ; ++nq) s[t][nq] = mfma_16x16x32_bf16(kf, qf[nq][ds], s[t][nq]);
         }
       }
-      // register r of tile t in lane (ln, lg) is key j0 + 8 lg + 4 t + r, query wq0 + 16 nq + ln
+      // register r of tile t in lane (ln, lg) is key j0 + 8 lg + 4 t + r, query wq0 + 16 nq + ln.
+      // Blocks strictly below the diagonal and inside the window need no mask.
+      const bool full = j0 + KB - 1 <= wq0 && (W <= 0 || wq1 - j0 < W);
       bf16x8_t pf[NQ];
+      float mx[NQ];
 #pragma unroll
       for (int nq = 0; nq < NQ; ++nq) {
-        const int qi = wq0 + nq * 16 + ln;
-        float x[8];
-        float mx = -INFINITY;
+        if (!full) {
+          const int qi = wq0 + nq * 16 + ln;
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int kj = j0 + 8 * lg + 4 * t + r;
+              const bool vis = kj <= qi && kj < S && (W <= 0 || qi - kj < W);
+              if (!vis) s[t][nq][r] = -INFINITY;
+            }
+        }
+        float v = fmaxf(fmaxf(fmaxf(s[0][nq][0], s[0][nq][1]), fmaxf(s[0][nq][2], s[0][nq][3])),
+                        fmaxf(fmaxf(s[1][nq][0], s[1][nq][1]), fmaxf(s[1][nq][2], s[1][nq][3])));
+        v = fmaxf(v, __shfl_xor(v, 16, 64));
+        v = fmaxf(v, __shfl_xor(v, 32, 64));
+        mx[nq] = v * scale_log2;  // block max of the query's scaled scores (log2 units)
+      }
+      // Lazy rescaling: a query's reference max m moves only when the block max
+      // exceeds it by more than 2^8, so probabilities stay <= 256 and the O / l
+      // rescale (exact, by powers computed with exp2) is skipped on most blocks.
+      bool need = false;
+#pragma unroll
+      for (int nq = 0; nq < NQ; ++nq) need |= mx[nq] > m[nq] + 8.f;
+      if (__any(need)) {
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq) {
+          const float mnew = mx[nq] > m[nq] + 8.f ? mx[nq] : m[nq];
+          const float corr = mnew == -INFINITY ? 1.f : fast_exp2(m[nq] - mnew);
+          m[nq] = mnew;
+          l[nq] *= corr;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[dt][nq] *= corr;
+        }
+      }
+#pragma unroll
+      for (int nq = 0; nq < NQ; ++nq) {
+        const float mo = m[nq] == -INFINITY ? 0.f : m[nq];
+        float p[8];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kj = j0 + 8 * lg + 4 * t + r;
-            const bool vis = kj <= qi && kj < S && (W <= 0 || qi - kj < W);
-            const float v = vis ? s[t][nq][r] * scale_log2 : -INFINITY;
-            x[4 * t + r] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m[nq], mx);
-        const float muse = mnew == -INFINITY ? 0.f : mnew;
-        const float corr = fast_exp2(m[nq] - muse);
-        m[nq] = mnew;
-        float ps = 0.f;
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(x[2 * e] - muse), p1 = fast_exp2(x[2 * e + 1] - muse);
-          ps += p0 + p1;
-          pk[e] = pack_bf16x2(p0, p1);
-        }
-        l[nq] = l[nq] * corr + ps;
-        pf[nq] = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt][nq] *= corr;
+          for (int r = 0; r < 4; ++r) p[4 * t + r] = fast_exp2(fmaf(s[t][nq][r], scale_log2, -mo));
+        l[nq] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        pf[nq] = as_bf16x8(u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                   pack_bf16x2(p[6], p[7])});
       }
       // Oᵀ[d, query] += Vᵀ[d, keys] · Pᵀ[keys, query]
 #pragma unroll

@@ -18,17 +18,14 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// Round to nearest, ties to even (inputs here are finite or +-inf; a NaN input
-// stays a NaN because its payload bits keep the exponent all ones).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
 
+// Two fp32 -> bf16 conversions in one v_cvt_pk_bf16_f32 (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return bf16_t(pack_bf16x2(f, 0.f) & 0xFFFFu); }
 
 // Element type traits: load/store one value through fp32.
 template <typename T> struct Elem;

@@ -149,3 +149,18 @@ def test_attention_f32_matches_oracle(fwd, B, S, Hq, Hkv, D, W):
     o = fwd.attention(to_device(q), to_device(k), to_device(_vt(v)), window=W)
     ref = oracle.attention(q, k, v, W)
     assert err_over_scale(o.cpu().numpy(), ref) < 1e-5
+
+
+def test_bf16_output_rounding_is_nearest_even(fwd):
+    """rows of +-0.5 with eps = 0.75 give mean(x^2) + eps = 1 exactly, so y = x * w is
+    exact in fp32 and the stored bf16 must be its round-to-nearest-even value."""
+    rows, H = 64, 256
+    rng = np.random.default_rng(9)
+    x = np.where(rng.random((rows, H)) < 0.5, -0.5, 0.5).astype(np.float32)
+    w = rng.standard_normal(H).astype(np.float32)
+    w[:4] = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -9, -(1 + 2 ** -8)], np.float32)  # ties / halfway
+    y = bf16_to_f32(fwd.rmsnorm(to_device(x), to_device(w), 0.75, "bf16"))
+    exact = x * w                                   # exact products of 0.5 and w
+    u = exact.view(np.uint32).astype(np.uint64)
+    rne = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
+    assert np.array_equal(y, rne)
