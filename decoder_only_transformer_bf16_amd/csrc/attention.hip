@@ -6,12 +6,14 @@
 //   g = h / (Hq / Hkv), over keys j <= i (and i - j < W when W > 0).
 //
 // bf16 path (D in {64, 128, 256}): flash-style single pass with an online softmax.
-// The score tile is computed transposed, Sᵀ = K·Qᵀ with v_mfma_f32_16x16x32_bf16,
-// so that every lane owns one query column: the softmax statistics are per lane
-// except for one cross-lane max over the four 16-lane groups. The probabilities
-// then feed Oᵀ += Vᵀ·Pᵀ straight from registers as the MFMA B operand; values are
-// kept transposed (keys contiguous) so the A operand is a 16-byte LDS read.
-// K and Vᵀ slices of 32 keys are double-buffered in LDS.
+// The score tile is computed transposed, Sᵀ = K·Qᵀ with v_mfma_f32_32x32x16_bf16,
+// so that every lane owns one query column and 16 contiguous keys of a 32-key block:
+// the softmax statistics are per lane except for one cross-lane max. The
+// probabilities then feed Oᵀ += Vᵀ·Pᵀ straight from registers as the MFMA B operand;
+// values are kept transposed (keys contiguous) so the A operand is a 16-byte LDS
+// read. K and Vᵀ blocks stream global -> LDS by buffer loads through a 4-deep ring
+// (three blocks in flight), and the score MFMAs of block j + 1 are issued before the
+// softmax of block j so the two overlap.
 //
 // f32 path (D <= 64): one wavefront per query row on the vector ALUs.
 #include "common.h"
@@ -20,226 +22,259 @@
 namespace fwdk {
 namespace {
 
-constexpr int KB = 32;  // keys per slice
+constexpr int KB = 32;  // keys per block
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Key j of a slice (j = 8 g + 4 t + r) is stored in LDS row 16 t + 4 g + r, so that
-// row m of the t-th 16-row MFMA tile holds key 8 (m / 4) + 4 t + m % 4 and lane group
-// g of the transposed score tile ends up owning keys 8 g .. 8 g + 7.
-__device__ __forceinline__ int key_row(int j) { return ((j >> 2) & 1) * 16 + (j >> 3) * 4 + (j & 3); }
+// K block in LDS: row R = 8 a + 4 g + b holds key 16 g + 4 a + b, so that in the
+// transposed score tile Sᵀ = K·Qᵀ (v_mfma_f32_32x32x16_bf16, whose register r of lane
+// (n, g) is row 8 (r / 4) + 4 g + r % 4) lane group g = l / 32 owns the 16 contiguous
+// keys 16 g + r. Those 16 probabilities then feed Oᵀ += Vᵀ·Pᵀ directly as two MFMA B
+// operands (keys 16 g + 8 m + 0..7 in MFMA m), matched by 16-byte reads of Vᵀ rows.
+__device__ __forceinline__ int key_of_row(int R) { return ((R >> 2) & 1) * 16 + (R >> 3) * 4 + (R & 3); }
 
-// LDS layouts (16-byte chunks XOR-swizzled so that the 16 lanes an LDS read serves
-// together, which read one chunk column of 16 consecutive rows, hit distinct banks).
+// 16-byte chunk swizzles: the 16 lanes an LDS read serves together read one chunk
+// column of 16 consecutive rows, so (row's bank half, chunk) must differ across them.
 template <int D>
-__device__ __forceinline__ int k_off(int row, int chunk) {  // K tile: [32 rows][D]
-  return row * D + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 3);
+__device__ __forceinline__ int kswz(int R, int c) {
+  if constexpr (D == 64) return c ^ ((R >> 1) & 7);  // 128-byte rows: two rows per bank sweep
+  else return c ^ (R & 15);                          // >= 256-byte rows
 }
-__device__ __forceinline__ int v_off(int d, int chunk) {  // Vᵀ tile: [D rows][32 keys], 4 chunks per row
-  return d * KB + ((chunk ^ ((d >> 2) & 3)) << 3);
+__device__ __forceinline__ int vswz(int d, int c) { return c ^ ((d >> 2) & 3); }  // 64-byte rows
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int)(bytes < 0 ? 0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One 1 KiB piece (64 lanes x 16 bytes) of a K or Vᵀ block, global -> LDS directly.
+// Pieces 0 .. D/16-1 are K, D/16 .. D/8-1 are Vᵀ. Keys past the sequence read as zero
+// (out of the buffer's range); the partial 8-key chunk at the end of Vᵀ rows reads the
+// row padding, whose weight is exactly zero.
 template <int D>
-struct KVLoader {
-  static constexpr int kPer = D / 64;  // (32 * D / 8) chunks / 256 threads, same for K and Vᵀ
-  u32x4_t kv[kPer], vv[kPer];
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ kbase, int64_t ldk,
-                                       const bf16_t* __restrict__ vbase, int ldvt, int j0, int S, int tid) {
-#pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int q = tid + p * 256;
-      const int j = q / (D / 8), c = q % (D / 8);
-      kv[p] = (j0 + j < S) ? *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)(j0 + j) * ldk + c * 8)
-                           : u32x4_t{0u, 0u, 0u, 0u};
-      const int d = q >> 2, cv = q & 3;
-      const int key = j0 + cv * 8;
-      u32x4_t x = u32x4_t{0u, 0u, 0u, 0u};
-      if (key < S) {
-        x = *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)d * ldvt + key);
-        if (key + 8 > S) {  // keys past the sequence end hold padding: zero them
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k0 = key + 2 * e;
-            uint32_t w = x[e];
-            if (k0 >= S) w &= 0xFFFF0000u;
-            if (k0 + 1 >= S) w &= 0x0000FFFFu;
-            x[e] = w;
-          }
-        }
-      }
-      vv[p] = x;
-    }
+__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int64_t ldk, int ldvt,
+                                           bf16_t* klds, bf16_t* vlds, int j0, int S, int piece, int lane) {
+  constexpr int CH = D / 8, RPB = 64 / CH;  // K: chunks per row, rows per piece
+  if (piece < D / 16) {
+    const int R = piece * RPB + lane / CH;
+    const int c = kswz<D>(R, lane % CH);
+    const int key = j0 + key_of_row(R);
+    const uint32_t off = key < S ? (uint32_t)(key * ldk + c * 8) * 2u : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(klds + piece * 512), 16, off, 0, 0, 0);
+  } else {
+    const int vp = piece - D / 16;
+    const int d = vp * 16 + lane / 4;
+    const int c = vswz(d, lane & 3);
+    const int key = j0 + c * 8;
+    const uint32_t off = key < S ? (uint32_t)(d * ldvt + key) * 2u : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vlds + vp * 512), 16, off, 0, 0, 0);
   }
-  __device__ __forceinline__ void store(bf16_t* klds, bf16_t* vlds, int tid) const {
-#pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int q = tid + p * 256;
-      const int j = q / (D / 8), c = q % (D / 8);
-      *reinterpret_cast<u32x4_t*>(klds + k_off<D>(key_row(j), c)) = kv[p];
-      *reinterpret_cast<u32x4_t*>(vlds + v_off(q >> 2, q & 3)) = vv[p];
-    }
-  }
-};
+}
 
-template <int D, int NQ>
+template <int D, int QT, int ST>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
-  constexpr int BQ = 4 * 16 * NQ;  // queries per workgroup (4 wavefronts)
-  constexpr int DS = D / 32;       // 32-wide d slices of the score contraction
-  constexpr int DT = D / 16;       // 16-row d tiles of the output
-  __shared__ __attribute__((aligned(16))) bf16_t klds[2][KB * D];
-  __shared__ __attribute__((aligned(16))) bf16_t vlds[2][D * KB];
+  constexpr int QW = 32 * QT;      // queries per wavefront
+  constexpr int BQ = 4 * QW;       // queries per workgroup
+  constexpr int DS = D / 16;       // k-steps of the score contraction
+  constexpr int DT = D / 32;       // 32-row d tiles of the output
+  constexpr int PIECES = D / 8;    // 1 KiB loads per K+Vᵀ block
+  constexpr int LPW = PIECES / 4;  // ... per wavefront
+  constexpr int KSZ = KB * D, VSZ = D * KB;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[ST * (KSZ + VSZ)];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ln = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int ln = lane & 31, lg = lane >> 5;
   const int qb = gridDim.x - 1 - blockIdx.x;  // longest query blocks first
   const int h = blockIdx.y, b = blockIdx.z;
   const int g = h / (a.Hq / a.Hkv);
   const int S = a.S, W = a.window;
   const int q0 = qb * BQ;
-  const int wq0 = q0 + wave * 16 * NQ;
-  const int wq1 = min(wq0 + 16 * NQ, S) - 1;  // last valid query of this wavefront
+  const int wq0 = q0 + wave * QW;
+  const int wq1 = min(wq0 + QW, S) - 1;  // last valid query of this wavefront
 
   const bf16_t* qbase = (const bf16_t*)a.q + (int64_t)b * S * a.ldq + h * D;
   const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * S * a.ldk + g * D;
   const bf16_t* vbase = (const bf16_t*)a.vt + (int64_t)(b * a.Hkv + g) * D * a.ldvt;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (int64_t)S * a.ldk * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (int64_t)D * a.ldvt * 2);
 
-  // Qᵀ fragments (MFMA B operand): lane owns query wq0 + 16 nq + ln, d chunk 32 ds + 8 lg.
-  bf16x8_t qf[NQ][DS];
+  // Qᵀ fragments (MFMA B operand): lane owns query wq0 + 32 qt + ln, dims 16 ds + 8 lg .. + 7
+  bf16x8_t qf[QT][DS];
 #pragma unroll
-  for (int nq = 0; nq < NQ; ++nq) {
-    const int qi = wq0 + nq * 16 + ln;
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qi = wq0 + qt * 32 + ln;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (qi < S) v = *reinterpret_cast<const u32x4_t*>(qbase + (int64_t)qi * a.ldq + ds * 32 + lg * 8);
-      qf[nq][ds] = as_bf16x8(v);
+      if (qi < S) v = *reinterpret_cast<const u32x4_t*>(qbase + (int64_t)qi * a.ldq + ds * 16 + lg * 8);
+      qf[qt][ds] = as_bf16x8(v);
     }
   }
+  wait_vmcnt<0>();
 
-  floatx4_t o[DT][NQ];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) o[dt][nq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m[NQ], l[NQ];
-#pragma unroll
-  for (int nq = 0; nq < NQ; ++nq) {
-    m[nq] = -INFINITY;
-    l[nq] = 0.f;
-  }
-
+  // key blocks of the workgroup, and the active sub-range of this wavefront
   const int kv_end = min(S, q0 + BQ);
   const int kv_begin = W > 0 ? max(0, q0 - W + 1) : 0;
   const int kb0 = kv_begin / KB, kb1 = (kv_end + KB - 1) / KB;
+  const int wb0 = W > 0 ? max(kb0, (wq0 - W + 1) / KB) : kb0;
+  const int wb1 = wq0 < S ? min(kb1, wq1 / KB + 1) : kb0;  // empty when the wave has no queries
+  auto active = [&](int kb) { return kb >= wb0 && kb < wb1; };
 
-  KVLoader<D> ld;
+  auto issue_block = [&](int kb) {
+    bf16_t* kl = lds + (kb % ST) * (KSZ + VSZ);
+#pragma unroll
+    for (int p = 0; p < LPW; ++p)
+      load_piece<D>(rk, rv, a.ldk, a.ldvt, kl, kl + KSZ, kb * KB, S, wave + 4 * p, lane);
+  };
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (kb0 + s < kb1) issue_block(kb0 + s);
+
+  floatx16_t o[DT][QT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) o[dt][qt] = floatx16_t{};
+  float m[QT], l[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m[qt] = -INFINITY;
+    l[qt] = 0.f;
+  }
+
+  // Sᵀ of block kb (K from its LDS buffer)
+  auto scores = [&](int kb, floatx16_t (&sc)[QT]) {
+    const bf16_t* K = lds + (kb % ST) * (KSZ + VSZ);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) sc[qt] = floatx16_t{};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(K + ln * D + (kswz<D>(ln, 2 * ds + lg) << 3)));
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) sc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qt][ds], sc[qt], 0, 0, 0);
+    }
+  };
+
+  floatx16_t sc[QT], sn[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) sc[qt] = sn[qt] = floatx16_t{};
   if (kb0 < kb1) {
-    ld.load(kbase, a.ldk, vbase, a.ldvt, kb0 * KB, S, tid);
-    ld.store(klds[0], vlds[0], tid);
+    if (kb0 + ST - 2 < kb1) wait_vmcnt<(ST - 2) * LPW>();
+    else wait_vmcnt<0>();
   }
   __syncthreads();
+  if (active(kb0)) scores(kb0, sc);
 
   for (int kb = kb0; kb < kb1; ++kb) {
-    const int cur = (kb - kb0) & 1;
-    if (kb + 1 < kb1) ld.load(kbase, a.ldk, vbase, a.ldvt, (kb + 1) * KB, S, tid);
-
-    const int j0 = kb * KB;
-    const bool active = wq0 < S && j0 <= wq1 && !(W > 0 && j0 + KB - 1 < wq0 - W + 1);
-    if (active) {
-      const bf16_t* K = klds[cur];
-      const bf16_t* V = vlds[cur];
-      // Sᵀ[key, query]: tile t covers LDS rows 16 t .. 16 t + 15
-      floatx4_t s[2][NQ];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) s[t][nq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-          const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(K + k_off<D>(16 * t + ln, ds * 4 + lg)));
-#pragma unroll
-          for (int nq = 0; nq < NQ; ++nq) s[t][nq] = mfma_16x16x32_bf16(kf, qf[nq][ds], s[t][nq]);
-        }
-      }
-      // register r of tile t in lane (ln, lg) is key j0 + 8 lg + 4 t + r, query wq0 + 16 nq + ln.
+    if (kb + 1 < kb1) {
+      if (kb + ST - 2 < kb1) wait_vmcnt<(ST - 3) * LPW>();  // block kb + 1 has landed
+      else wait_vmcnt<0>();
+      __syncthreads();  // ... for everyone; and everyone is done with block kb - 1
+      if (kb + ST - 1 < kb1) issue_block(kb + ST - 1);  // refill block kb - 1's buffer
+      if (active(kb + 1)) scores(kb + 1, sn);  // MFMAs that overlap the softmax below
+    }
+    if (active(kb)) {
+      const int j0 = kb * KB;
+      // lane (ln, lg), register r of q tile qt: key j0 + 16 lg + r, query wq0 + 32 qt + ln.
       // Blocks strictly below the diagonal and inside the window need no mask.
       const bool full = j0 + KB - 1 <= wq0 && (W <= 0 || wq1 - j0 < W);
-      bf16x8_t pf[NQ];
-      float mx[NQ];
+      float mx[QT];
 #pragma unroll
-      for (int nq = 0; nq < NQ; ++nq) {
+      for (int qt = 0; qt < QT; ++qt) {
         if (!full) {
-          const int qi = wq0 + nq * 16 + ln;
+          // key j0 + 16 lg + r is visible from query qi iff 0 <= qi - key < window
+          // (window = W if W > 0, else unbounded) and key < S
+          const int qi = wq0 + qt * 32 + ln;
+          const int d0 = qi - (j0 + 16 * lg);            // qi - key for r = 0
+          const int wlim = W > 0 ? W : 0x7FFFFFFF;
+          const int klim = S - (j0 + 16 * lg);           // r < klim <=> key < S
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int kj = j0 + 8 * lg + 4 * t + r;
-              const bool vis = kj <= qi && kj < S && (W <= 0 || qi - kj < W);
-              if (!vis) s[t][nq][r] = -INFINITY;
-            }
+          for (int r = 0; r < 16; ++r) {
+            const int dd = d0 - r;
+            const bool vis = (unsigned)dd < (unsigned)wlim && r < klim;
+            sc[qt][r] = vis ? sc[qt][r] : -INFINITY;
+          }
         }
-        float v = fmaxf(fmaxf(fmaxf(s[0][nq][0], s[0][nq][1]), fmaxf(s[0][nq][2], s[0][nq][3])),
-                        fmaxf(fmaxf(s[1][nq][0], s[1][nq][1]), fmaxf(s[1][nq][2], s[1][nq][3])));
-        v = fmaxf(v, __shfl_xor(v, 16, 64));
-        v = fmaxf(v, __shfl_xor(v, 32, 64));
-        mx[nq] = v * scale_log2;  // block max of the query's scaled scores (log2 units)
+        float v = sc[qt][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) v = fmaxf(v, sc[qt][r]);
+        mx[qt] = v;
       }
-      // Lazy rescaling: a query's reference max m moves only when the block max
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 32, 64)) * scale_log2;
+      // Lazy rescaling: the reference max m of a query moves only when a block max
       // exceeds it by more than 2^8, so probabilities stay <= 256 and the O / l
-      // rescale (exact, by powers computed with exp2) is skipped on most blocks.
+      // rescale (exact powers of exp2) is skipped on most blocks.
       bool need = false;
 #pragma unroll
-      for (int nq = 0; nq < NQ; ++nq) need |= mx[nq] > m[nq] + 8.f;
+      for (int qt = 0; qt < QT; ++qt) need |= mx[qt] > m[qt] + 8.f;
       if (__any(need)) {
 #pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) {
-          const float mnew = mx[nq] > m[nq] + 8.f ? mx[nq] : m[nq];
-          const float corr = mnew == -INFINITY ? 1.f : fast_exp2(m[nq] - mnew);
-          m[nq] = mnew;
-          l[nq] *= corr;
+        for (int qt = 0; qt < QT; ++qt) {
+          const float mnew = mx[qt] > m[qt] + 8.f ? mx[qt] : m[qt];
+          const float corr = mnew == -INFINITY ? 1.f : fast_exp2(m[qt] - mnew);
+          m[qt] = mnew;
+          l[qt] *= corr;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[dt][nq] *= corr;
+          for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= corr;
         }
       }
+      bf16x8_t pf[QT][2];
 #pragma unroll
-      for (int nq = 0; nq < NQ; ++nq) {
-        const float mo = m[nq] == -INFINITY ? 0.f : m[nq];
-        float p[8];
+      for (int qt = 0; qt < QT; ++qt) {
+        const float mo = m[qt] == -INFINITY ? 0.f : m[qt];
+        float p[16];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(sc[qt][r], scale_log2, -mo));
+        float ps = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p[4 * t + r] = fast_exp2(fmaf(s[t][nq][r], scale_log2, -mo));
-        l[nq] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        pf[nq] = as_bf16x8(u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                                   pack_bf16x2(p[6], p[7])});
+        for (int r = 0; r < 16; ++r) ps += p[r];
+        l[qt] += ps;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+          pf[qt][mm] = as_bf16x8(u32x4_t{pack_bf16x2(p[8 * mm + 0], p[8 * mm + 1]), pack_bf16x2(p[8 * mm + 2], p[8 * mm + 3]),
+                                         pack_bf16x2(p[8 * mm + 4], p[8 * mm + 5]), pack_bf16x2(p[8 * mm + 6], p[8 * mm + 7])});
       }
       // Oᵀ[d, query] += Vᵀ[d, keys] · Pᵀ[keys, query]
+      const bf16_t* V = lds + (kb % ST) * (KSZ + VSZ) + KSZ;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(V + v_off(dt * 16 + ln, lg)));
+        const int d = dt * 32 + ln;
 #pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) o[dt][nq] = mfma_16x16x32_bf16(vf, pf[nq], o[dt][nq]);
+        for (int mm = 0; mm < 2; ++mm) {
+          const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(V + d * KB + (vswz(d, 2 * lg + mm) << 3)));
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+            o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qt][mm], o[dt][qt], 0, 0, 0);
+        }
       }
     }
-    if (kb + 1 < kb1) ld.store(klds[cur ^ 1], vlds[cur ^ 1], tid);
-    __syncthreads();
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) sc[qt] = sn[qt];
   }
 
-  // normalise and store: register r of d tile dt is dim 16 dt + 4 lg + r of query wq0 + 16 nq + ln
+  // normalise and store: register r of d tile dt is dim 32 dt + 8 (r / 4) + 4 lg + r % 4
   bf16_t* obase = (bf16_t*)a.o + (int64_t)b * S * a.ldo + h * D;
 #pragma unroll
-  for (int nq = 0; nq < NQ; ++nq) {
-    float lt = l[nq];
-    lt += __shfl_xor(lt, 16, 64);
+  for (int qt = 0; qt < QT; ++qt) {
+    float lt = l[qt];
     lt += __shfl_xor(lt, 32, 64);
     const float inv = 1.f / lt;
-    const int qi = wq0 + nq * 16 + ln;
+    const int qi = wq0 + qt * 32 + ln;
     if (qi < S) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const floatx4_t v = o[dt][nq] * inv;
-        *reinterpret_cast<u32x2_t*>(obase + (int64_t)qi * a.ldo + dt * 16 + lg * 4) =
-            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      }
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const floatx16_t& v = o[dt][qt];
+          *reinterpret_cast<u32x2_t*>(obase + (int64_t)qi * a.ldo + dt * 32 + a4 * 8 + lg * 4) =
+              u32x2_t{pack_bf16x2(v[4 * a4] * inv, v[4 * a4 + 1] * inv), pack_bf16x2(v[4 * a4 + 2] * inv, v[4 * a4 + 3] * inv)};
+        }
     }
   }
 }
@@ -326,24 +361,15 @@ template <int D>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
   const float sl = kLog2e / sqrtf((float)D);
   const int64_t heads = (int64_t)a.B * a.Hq;
-  constexpr int kMaxNQ = D >= 256 ? 2 : 4;
-  // largest per-wave query count that still gives >= 512 workgroups
-  int nq = kMaxNQ;
-  while (nq > 1 && heads * ((a.S + 64 * nq - 1) / (64 * nq)) < 512) nq >>= 1;
   const dim3 blk(256);
-  switch (nq) {
-    case 4:
-      if constexpr (kMaxNQ >= 4) {
-        hipLaunchKernelGGL((attn_bf16_kernel<D, 4>), dim3((a.S + 255) / 256, a.Hq, a.B), blk, 0, s, a, sl);
-        break;
-      }
-      [[fallthrough]];
-    case 2:
-      hipLaunchKernelGGL((attn_bf16_kernel<D, 2>), dim3((a.S + 127) / 128, a.Hq, a.B), blk, 0, s, a, sl);
-      break;
-    default:
-      hipLaunchKernelGGL((attn_bf16_kernel<D, 1>), dim3((a.S + 63) / 64, a.Hq, a.B), blk, 0, s, a, sl);
+  // two 32-query tiles per wavefront when registers allow it and the grid stays full
+  if constexpr (D <= 128) {
+    if (heads * ((a.S + 255) / 256) >= 512) {
+      hipLaunchKernelGGL((attn_bf16_kernel<D, 2, 4>), dim3((a.S + 255) / 256, a.Hq, a.B), blk, 0, s, a, sl);
+      return hipGetLastError();
+    }
   }
+  hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 4>), dim3((a.S + 127) / 128, a.Hq, a.B), blk, 0, s, a, sl);
   return hipGetLastError();
 }
 

@@ -182,7 +182,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const bf16_t* __restri
   __shared__ __attribute__((aligned(1024))) bf16_t lds[ST * SLICE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int nTM = (M + BM - 1) / BM, nTN = (N + BN - 1) / BN;
   int tm, tn;

@@ -194,7 +194,8 @@ int fwd_gemm(const void* X, const void* W, float* Y, int32_t P, int32_t in, int3
  * over keys j <= i (and i - j < window when window > 0), g = h / (Hq / Hkv).
  * Device buffers of `dtype`: q [B, S, Hq, D], k [B, S, Hkv, D],
  * v_t [B, Hkv, D, Sp] with Sp = S rounded up to a multiple of 8 (values
- * transposed, keys contiguous; entries past S are ignored), o [B, S, Hq, D].
+ * transposed, keys contiguous; the entries past S are read with weight exactly
+ * zero, so they must be finite), o [B, S, Hq, D].
  * No RoPE is applied here. Errors: FWD_E_ARG, FWD_E_CONFIG, FWD_E_UNAVAILABLE, FWD_E_HIP.
  */
 int fwd_attention(const void* q, const void* k, const void* v_t, void* o, int32_t B, int32_t S,

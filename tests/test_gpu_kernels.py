@@ -111,10 +111,11 @@ def _attn_inputs(B, S, Hq, Hkv, D, dt, seed=3):
 
 
 def _vt(v):
-    """values transposed to [B, Hkv, D, Sp] with Sp = S rounded up to 8 (padding = NaN bits)."""
+    """values transposed to [B, Hkv, D, Sp] with Sp = S rounded up to 8; the padding holds
+    a large finite value (bf16 / f32 1000.0) that must not leak into the output."""
     B, S, Hkv, D = v.shape
     Sp = (S + 7) // 8 * 8
-    out = np.full((B, Hkv, D, Sp), 0xFFC0 if v.dtype == np.uint16 else np.nan, dtype=v.dtype)
+    out = np.full((B, Hkv, D, Sp), 0x447A if v.dtype == np.uint16 else 1000.0, dtype=v.dtype)
     out[..., :S] = np.transpose(v, (0, 2, 3, 1))
     return out
 
