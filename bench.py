@@ -66,7 +66,7 @@ def cpu_baseline(cfg, S):
         for name in wl.weight_shapes(c):
             w[name]                                   # draw outside the timed region
         t = time.perf_counter()
-        oracle.forward(c, w, ids, want_logits=True, want_hidden=False)
+        oracle.forward(c, w, ids, want_logits=True, want_hidden=False)  # head included
         times[n] = time.perf_counter() - t
         del w
     t_layer = max(times[1] - times[0], 1e-9)

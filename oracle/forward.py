@@ -12,7 +12,10 @@ Sources (page title, then the passage):
         float64-accumulated f32 triple loop; err/scale error model).
 
 Every function takes float32 arrays, computes in float64 and returns float32.
-Readings of points the pages leave open are listed in DESIGN.md ("Readings").
+Where the pages leave a point open this file takes the plainest reading: rotate-half
+RoPE pairs, attention scale 1/sqrt(D), a window W keeps keys with 0 <= i - j < W,
+the softcap is applied before the argmax, ties go to the lowest index, and every
+row of a batch is its own sequence at positions 0..S-1.
 """
 from __future__ import annotations
 
@@ -29,6 +32,15 @@ def _f64(a) -> np.ndarray:
 
 def _f32(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64).astype(np.float32)
+
+
+def round_bf16(a) -> np.ndarray:
+    """float32 -> nearest bf16 (ties to even) -> float32. Used only by the diagnostic
+    mode of forward(), which rounds where a bf16 implementation must round, to tell a
+    precision deficit from a bug; the reference itself never rounds activations."""
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
 
 
 # ---------------------------------------------------------------- projections
@@ -166,6 +178,20 @@ def attention(q, k, v, window: int = 0) -> np.ndarray:
     return out
 
 
+def _attention_rounded(q, k, v, window: int) -> np.ndarray:
+    """Diagnostic only: attention with the probabilities rounded to bf16 before the
+    value product (the normaliser stays exact)."""
+    v64 = _f64(v)
+    B, S, Hkv, D = v64.shape
+    Hq = np.asarray(q).shape[2]
+    out = np.empty((B, S, Hq, D), dtype=np.float32)
+    for b in range(B):
+        p = attention_probs(np.asarray(q)[b:b + 1], np.asarray(k)[b:b + 1], window)[0]
+        for h in range(Hq):
+            out[b, :, h, :] = _f32(_f64(round_bf16(p[h].astype(np.float32))) @ v64[b, :, h // (Hq // Hkv), :])
+    return out
+
+
 # ---------------------------------------------------------------- feed-forward
 def silu(z) -> np.ndarray:
     """silu(z) = z / (1 + e^-z), float64 in and out."""
@@ -201,7 +227,7 @@ def argmax(z) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- whole forward
-def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = True):
+def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = True, bf16_points: bool = False):
     """The prefill forward pass over a batch of prompts.
 
     cfg: an object with the geometry fields n_layers, hidden, n_heads, n_kv_heads,
@@ -211,7 +237,11 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
     weights: mapping name -> float32 array (names as documented on the workloads).
     ids: int [B, S]; every row is an independent sequence at positions 0..S-1.
 
-    Returns dict(logits [B,S,V] f32, hidden [L+2,B,S,H] f32, argmax [B,S] i32).
+    Returns dict(logits [B,S,V] f32, hidden [L+2,B,S,H] f32, argmax [B,S] i32); with
+    want_logits=False the head is skipped and logits / argmax are None.
+    bf16_points=True is a diagnostic, not the reference: it rounds every matrix-product
+    input (normalised activations, rotated q / k, v, attention probabilities and
+    output, SwiGLU output) to bf16, as a bf16 implementation does.
     Slots ([fp] Theorem 1): 0 = embedding, l+1 = after layer l, L+1 = final norm.
     """
     ids = np.asarray(ids)
@@ -231,24 +261,26 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
     if want_hidden:
         hidden[0] = x
 
+    rb = round_bf16 if bf16_points else (lambda a: a)
     for l in range(L):
         p = f"layers.{l}."
         window = cfg.sliding_window if kinds[l] == "local" else 0
         # attention sublayer
-        n = rmsnorm(x, weights[p + "attn_norm"], eps)
+        n = rb(rmsnorm(x, weights[p + "attn_norm"], eps))
         q = gemm(n, weights[p + "wq"]).reshape(B, S, Hq, D)
         k = gemm(n, weights[p + "wk"]).reshape(B, S, Hkv, D)
-        v = gemm(n, weights[p + "wv"]).reshape(B, S, Hkv, D)
-        q = np.stack([rope(q[b], positions, cfg.rope_theta) for b in range(B)])
-        k = np.stack([rope(k[b], positions, cfg.rope_theta) for b in range(B)])
-        o = attention(q, k, v, window).reshape(B, S, Hq * D)
+        v = rb(gemm(n, weights[p + "wv"]).reshape(B, S, Hkv, D))
+        q = rb(np.stack([rope(q[b], positions, cfg.rope_theta) for b in range(B)]))
+        k = rb(np.stack([rope(k[b], positions, cfg.rope_theta) for b in range(B)]))
+        o = rb(_attention_rounded(q, k, v, window) if bf16_points else attention(q, k, v, window))
+        o = o.reshape(B, S, Hq * D)
         u = gemm(o, weights[p + "wo"])
         if sandwich:
             u = rmsnorm(u, weights[p + "post_attn_norm"], eps)
         x = _f32(_f64(x) + _f64(u))
         # feed-forward sublayer
-        n = rmsnorm(x, weights[p + "ffn_norm"], eps)
-        a = swiglu(gemm(n, weights[p + "w_gate"]), gemm(n, weights[p + "w_up"]))
+        n = rb(rmsnorm(x, weights[p + "ffn_norm"], eps))
+        a = rb(swiglu(gemm(n, weights[p + "w_gate"]), gemm(n, weights[p + "w_up"])))
         d = gemm(a, weights[p + "w_down"])
         if sandwich:
             d = rmsnorm(d, weights[p + "post_ffn_norm"], eps)
@@ -259,7 +291,7 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
     h = rmsnorm(x, weights["final_norm"], eps)
     if want_hidden:
         hidden[L + 1] = h
-    z = softcap(gemm(h, E), cfg.final_logit_softcap)                    # tied head
-    out = {"argmax": argmax(z), "hidden": hidden}
-    out["logits"] = z if want_logits else None
-    return out
+    if not want_logits:                          # hidden slots only: the head is not needed
+        return {"argmax": None, "hidden": hidden, "logits": None}
+    z = softcap(gemm(rb(h), E), cfg.final_logit_softcap)                # tied head
+    return {"argmax": argmax(z), "hidden": hidden, "logits": z}

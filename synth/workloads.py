@@ -10,7 +10,9 @@ oracle and the library binding both read:
   layers.{l}.w_gate / w_up [F, H], w_down [H, F]
   final_norm [H]
 
-Matrices are N(0, 0.02^2); norm gains are 1.0 (readings).
+Matrices are N(0, 0.02^2); norm gains are 1.0 (gains drawn from N(0, 0.02^2) would
+shrink every normalised activation ~50x and make attention scores and RoPE
+numerically invisible, so the plainest non-degenerate reading sets them to one).
 """
 from __future__ import annotations
 

@@ -59,3 +59,22 @@ def argmax_check(got_ids, ref_logits, got_logits):
             if ref[t, ids[t]] < ref[t, best] - 2 * eps:
                 fails.append((t, int(ids[t]), best, margin, eps))
     return pinned, near, fails
+
+
+COS_PRIMARY = 0.9999        # "N7 · model/forward-parity", Theorem 1 proof (f32 forward vs f32 reference)
+COS_HALF_PRECISION = 0.999  # "N9 · metalgemm", Theorem 1 proof (half-precision device forward vs CPU reference)
+FLOOR_SLACK = 1.25
+
+
+def slot_parity(got, ref, ref_bf16_fn):
+    """Hidden-slot gate. Primary: cosine >= 0.9999 against the float64 oracle. Where
+    bf16 operands cannot reach that (deep configurations), the slot must instead be
+    no farther from the oracle than FLOOR_SLACK times the distance of the oracle
+    itself rounded to bf16 at the GPU's rounding points (ref_bf16_fn() -> that slot),
+    and never below the pages' half-precision gate of 0.999. Returns (ok, cos, floor)."""
+    c = cosine(got, ref)
+    if c >= COS_PRIMARY:
+        return True, c, None
+    floor = cosine(ref_bf16_fn(), ref)
+    ok = c >= COS_HALF_PRECISION and (1.0 - c) <= FLOOR_SLACK * (1.0 - floor) + 2e-6
+    return ok, c, floor
