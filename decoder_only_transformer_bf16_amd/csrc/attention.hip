@@ -11,9 +11,10 @@
 // the softmax statistics are per lane except for one cross-lane max. The
 // probabilities then feed Oᵀ += Vᵀ·Pᵀ straight from registers as the MFMA B operand;
 // values are kept transposed (keys contiguous) so the A operand is a 16-byte LDS
-// read. K and Vᵀ blocks stream global -> LDS by buffer loads through a 4-deep ring
-// (three blocks in flight), and the score MFMAs of block j + 1 are issued before the
-// softmax of block j so the two overlap.
+// read. K and Vᵀ blocks stream global -> LDS by buffer loads through a 3-deep ring
+// (two blocks in flight), and the score MFMAs of block j + 1 are issued before the
+// softmax of block j so the two overlap. Registers are held to two wavefronts per
+// SIMD, so one wavefront's softmax also overlaps the other's MFMAs.
 //
 // f32 path (D <= 64): one wavefront per query row on the vector ALUs.
 #include "common.h"
@@ -77,7 +78,7 @@ __device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t rk, __amdgpu_b
 }
 
 template <int D, int QT, int ST>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
   constexpr int QW = 32 * QT;      // queries per wavefront
   constexpr int BQ = 4 * QW;       // queries per workgroup
   constexpr int DS = D / 16;       // k-steps of the score contraction
@@ -362,14 +363,15 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
   const float sl = kLog2e / sqrtf((float)D);
   const int64_t heads = (int64_t)a.B * a.Hq;
   const dim3 blk(256);
-  // two 32-query tiles per wavefront when registers allow it and the grid stays full
-  if constexpr (D <= 128) {
+  // two 32-query tiles per wavefront only where they fit beside two wavefronts per
+  // SIMD without spilling (D = 64), and only when the grid stays full
+  if constexpr (D == 64) {
     if (heads * ((a.S + 255) / 256) >= 512) {
-      hipLaunchKernelGGL((attn_bf16_kernel<D, 2, 4>), dim3((a.S + 255) / 256, a.Hq, a.B), blk, 0, s, a, sl);
+      hipLaunchKernelGGL((attn_bf16_kernel<D, 2, 3>), dim3((a.S + 255) / 256, a.Hq, a.B), blk, 0, s, a, sl);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 4>), dim3((a.S + 127) / 128, a.Hq, a.B), blk, 0, s, a, sl);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 3>), dim3((a.S + 127) / 128, a.Hq, a.B), blk, 0, s, a, sl);
   return hipGetLastError();
 }
 

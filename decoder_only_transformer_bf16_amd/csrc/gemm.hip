@@ -150,6 +150,17 @@ __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, bf16_t* ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + blk * 512), 16, off, 0, 0, 0);
 }
 
+// The VGPR route: the same 1 KiB piece fetched into registers, then written to the
+// LDS position the DMA route would have used (byte 16 l of the piece).
+template <int BK>
+__device__ __forceinline__ u32x4_t fetch_block(__amdgpu_buffer_rsrc_t rs, int K, int k0, int blk, int lane) {
+  constexpr int CH = BK / 8, RPB = 64 / CH;
+  const int row = blk * RPB + lane / CH;
+  const int kk = k0 + swz<BK>(row, lane % CH) * 8;
+  const uint32_t off = kk < K ? (uint32_t)(row * K + kk) * 2u : 0x80000000u;
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -158,9 +169,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Tile configuration: BM x BN output tile, BK-wide K slices, STAGES LDS buffers,
 // WM x WN wavefronts (each owning a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles).
-template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_>
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, bool DMA_ = true>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
+  static constexpr bool DMA = DMA_;  // global -> LDS by buffer DMA, else through VGPRs + ds_write
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32, KS = BK / 16;
   static constexpr int LOADS_A = BM * (BK / 8) / 64 / NW;      // 1 KiB buffer loads per wave per slice
@@ -210,11 +222,36 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const bf16_t* __restri
     if (p < LA) load_block<BK>(ra, buf, K, k0, wave + p * NW, lane);
     else load_block<BK>(rb, buf + BM * BK, K, k0, wave + (p - LA) * NW, lane);
   };
+  u32x4_t stage[C::DMA ? 1 : LT];  // VGPR route: one slice in flight in registers
+  auto fetch = [&](int p, int k0) {
+    if constexpr (!C::DMA) {
+      if (p < LA) stage[p] = fetch_block<BK>(ra, K, k0, wave + p * NW, lane);
+      else stage[p] = fetch_block<BK>(rb, K, k0, wave + (p - LA) * NW, lane);
+    }
+  };
+  auto put = [&](int p, bf16_t* buf) {
+    if constexpr (!C::DMA) {
+      bf16_t* dst = p < LA ? buf + (wave + p * NW) * 512 : buf + BM * BK + (wave + (p - LA) * NW) * 512;
+      *reinterpret_cast<u32x4_t*>(dst + lane * 8) = stage[p];
+    }
+  };
+  if constexpr (C::DMA) {
 #pragma unroll
-  for (int q = 0; q < ST; ++q)
-    if (q < nk)
+    for (int q = 0; q < ST; ++q)
+      if (q < nk)
 #pragma unroll
-      for (int p = 0; p < LT; ++p) issue_load(p, lds + q * SLICE, q * BK);
+        for (int p = 0; p < LT; ++p) issue_load(p, lds + q * SLICE, q * BK);
+  } else {
+    static_assert(ST == 2, "the VGPR route stages one slice in registers beside two LDS buffers");
+#pragma unroll
+    for (int p = 0; p < LT; ++p) fetch(p, 0);
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int p = 0; p < LT; ++p) put(p, lds);
+    if (nk > 1)
+#pragma unroll
+      for (int p = 0; p < LT; ++p) fetch(p, BK);
+  }
   const int lr = lane & 31, lk = lane >> 5;
   const int arow = wm * WTM + lr, brow = BM + wn * WTN + lr;  // tile rows this lane reads (+32 i / +32 j)
   bf16x8_t fa[2][TM], fb[2][TN];
@@ -222,8 +259,10 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const bf16_t* __restri
     if (f < TM) fa[buf][f] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(base + lds_off<BK>(arow + f * 32, kk * 2 + lk)));
     else fb[buf][f - TM] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(base + lds_off<BK>(brow + (f - TM) * 32, kk * 2 + lk)));
   };
-  if (nk > 1) wait_vmcnt<(ST - 1) * LT>();
-  else wait_vmcnt<0>();
+  if constexpr (C::DMA) {
+    if (nk > 1) wait_vmcnt<(ST - 1) * LT>();
+    else wait_vmcnt<0>();
+  }
   __syncthreads();
 #pragma unroll
   for (int f = 0; f < FR; ++f) read_frag(lds, f, 0, 0);
@@ -232,6 +271,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const bf16_t* __restri
     bf16_t* cur = lds + (kt % ST) * SLICE;
     const bf16_t* nxt = lds + ((kt + 1) % ST) * SLICE;
     const bool refill = kt + ST < nk;
+    const bool refetch = kt + 2 < nk;  // VGPR route: fetch slice kt + 2 after the barrier
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int rb_ = kk & 1, wb = rb_ ^ 1;  // register buffers: read from rb_, prefetch into wb
@@ -239,9 +279,17 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const bf16_t* __restri
       for (int x = 0; x < MF; ++x) {
         if (kk == KS - 1 && x == H) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // all of slice kt is in registers
-          if (kt + 1 < nk) {
-            if (kt + ST - 1 < nk) wait_vmcnt<(ST - 2) * LT>();  // slice kt + 1 has landed
-            else wait_vmcnt<0>();
+          if constexpr (C::DMA) {
+            if (kt + 1 < nk) {
+              if (kt + ST - 1 < nk) wait_vmcnt<(ST - 2) * LT>();  // slice kt + 1 has landed
+              else wait_vmcnt<0>();
+            }
+          } else if (kt + 1 < nk) {
+            // slice kt + 1 sits in the staging registers: write it to the buffer slice
+            // kt - 1 used (free since the previous barrier)
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int p = 0; p < LT; ++p) put(p, const_cast<bf16_t*>(nxt));
           }
           __syncthreads();
         }
@@ -255,9 +303,14 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const bf16_t* __restri
           // (on the last slice this reads a stale but in-bounds buffer; never used)
 #pragma unroll
           for (int f = (y * FR) / (MF - H); f < ((y + 1) * FR) / (MF - H); ++f) read_frag(nxt, f, 0, wb);
-          if (refill) {
+          if constexpr (C::DMA) {
+            if (refill) {
 #pragma unroll
-            for (int p = (y * LT) / (MF - H); p < ((y + 1) * LT) / (MF - H); ++p) issue_load(p, cur, (kt + ST) * BK);
+              for (int p = (y * LT) / (MF - H); p < ((y + 1) * LT) / (MF - H); ++p) issue_load(p, cur, (kt + ST) * BK);
+            }
+          } else if (refetch) {
+#pragma unroll
+            for (int p = (y * LT) / (MF - H); p < ((y + 1) * LT) / (MF - H); ++p) fetch(p, (kt + 2) * BK);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
