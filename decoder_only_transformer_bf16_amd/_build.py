@@ -17,6 +17,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", INCLUDE, "-I", CSRC,
          # keep the compiler from emitting packed-fp32 VALU forms
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # fuse a*b+c into one fma only where it is written as one expression, so a
+         # value's rounding does not depend on the code around it (e.g. on whether
+         # its GEMM tile is cut by the last row)
+         "-ffp-contract=on",
          "-Wno-unused-command-line-argument"]
 
 
@@ -53,9 +57,10 @@ if __name__ == "__main__":
 
 
 def source_digest(files=("gemm.hip", "common.h", "kernels.h")) -> str:
-    """sha256 over the GEMM kernel sources (ties stored counter data to the kernel it measured)."""
+    """sha256 over the GEMM kernel sources and the compile flags (ties stored counter
+    data to the kernel it measured)."""
     import hashlib
-    h = hashlib.sha256()
+    h = hashlib.sha256(" ".join(FLAGS).encode())
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())

@@ -18,6 +18,17 @@ namespace {
 // ------------------------------------------------------------------ epilogues
 // Every epilogue receives pairs of accumulator values (v0 at packed column c,
 // v1 at packed column c + C) of one output row. ok0 / ok1 flag columns < N.
+// batch() takes R rows of one column pair at once (row[q] < 0: skip); the default
+// loops over pair(). Epilogues that read memory override it to issue every load
+// before the first store (the output may alias the input, so the compiler could
+// not reorder them itself).
+template <class E, int R>
+__device__ __forceinline__ void batch_pairs(const E& e, const int (&row)[R], int c, const float (&v0)[R],
+                                            const float (&v1)[R], bool ok0, bool ok1) {
+#pragma unroll
+  for (int q = 0; q < R; ++q)
+    if (row[q] >= 0) e.pair(row[q], c, v0[q], v1[q], ok0, ok1);
+}
 
 template <int C>
 struct EpiStore {
@@ -39,6 +50,11 @@ struct EpiStore {
     if (ok0) y[0] = apply(v0);
     if (ok1) y[C] = apply(v1);
   }
+  template <int R>
+  __device__ __forceinline__ void batch(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
+                                        bool ok0, bool ok1) const {
+    batch_pairs(*this, row, c, v0, v1, ok0, ok1);
+  }
 };
 
 template <int C>
@@ -50,6 +66,24 @@ struct EpiResidual {
     const int64_t i = (int64_t)row * ld + c;
     if (ok0) xout[i] = xin[i] + v0;
     if (ok1) xout[i + C] = xin[i + C] + v1;
+  }
+  template <int R>
+  __device__ __forceinline__ void batch(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
+                                        bool ok0, bool ok1) const {
+    float a[R], b[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {  // all loads first
+      const int64_t i = (int64_t)(row[q] < 0 ? 0 : row[q]) * ld + c;
+      a[q] = (row[q] >= 0 && ok0) ? xin[i] : 0.f;
+      b[q] = (row[q] >= 0 && ok1) ? xin[i + C] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      if (row[q] < 0) continue;
+      const int64_t i = (int64_t)row[q] * ld + c;
+      if (ok0) xout[i] = a[q] + v0[q];
+      if (ok1) xout[i + C] = b[q] + v1[q];
+    }
   }
 };
 
@@ -64,6 +98,11 @@ struct EpiSwiGLU {
     const float s = g * fast_rcp(1.f + fast_exp2(-kLog2e * g));
     Elem<T>::store(a + (int64_t)row * F + f, s * u);
   }
+  template <int R>
+  __device__ __forceinline__ void batch(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
+                                        bool ok0, bool ok1) const {
+    batch_pairs(*this, row, c, v0, v1, ok0, ok1);
+  }
 };
 
 template <int C, typename T>
@@ -71,6 +110,31 @@ struct EpiRope {
   T* qkv;  // [M, (Hq + 2 Hkv) D]: rotated q, rotated k, plain v, natural dim order
   const float2* cs;
   int Hq, Hkv, D, S;
+  template <int R>
+  __device__ __forceinline__ void batch(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
+                                        bool ok0, bool ok1) const {
+    const int qsz = Hq * D, ksz = Hkv * D;
+    if (!ok0) return;
+    if (c >= qsz + ksz) {  // value columns: plain stores
+      batch_pairs(*this, row, c, v0, v1, ok0, ok1);
+      return;
+    }
+    const int sec = c < qsz ? 0 : qsz;
+    const int cc = c - sec;
+    const int head = cc / D, pd = cc - head * D;
+    const int k = (pd / (2 * C)) * C + (pd % C);  // rotation index in [0, D/2)
+    float2 r[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q)  // all table loads first
+      r[q] = cs[(int64_t)((row[q] < 0 ? 0 : row[q]) % S) * (D / 2) + k];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      if (row[q] < 0) continue;
+      T* dst = qkv + (int64_t)row[q] * (qsz + 2 * ksz) + sec + head * D + k;
+      Elem<T>::store(dst, v0[q] * r[q].x - v1[q] * r[q].y);
+      Elem<T>::store(dst + D / 2, v0[q] * r[q].y + v1[q] * r[q].x);
+    }
+  }
   __device__ __forceinline__ void pair(int row, int c, float v0, float v1, bool ok0, bool) const {
     if (!ok0) return;
     const int qsz = Hq * D, ksz = Hkv * D;
@@ -169,9 +233,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Tile configuration: BM x BN output tile, BK-wide K slices, STAGES LDS buffers,
 // WM x WN wavefronts (each owning a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles).
-template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, bool DMA_ = true>
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, bool DMA_ = true, int OCC_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
+  static constexpr int OCC = OCC_;  // workgroups per CU the register budget is sized for
   static constexpr bool DMA = DMA_;  // global -> LDS by buffer DMA, else through VGPRs + ds_write
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32, KS = BK / 16;
@@ -179,13 +244,13 @@ struct Cfg {
   static constexpr int LOADS = (BM + BN) * (BK / 8) / 64 / NW;
   static_assert(LOADS_A * NW * 64 == BM * (BK / 8) && LOADS * NW * 64 == (BM + BN) * (BK / 8), "load split");
   static constexpr int LDS_BYTES = STAGES * (BM + BN) * BK * 2;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(LDS_BYTES * OCC <= 160 * 1024, "LDS budget");
   static_assert(TN % 2 == 0, "pair epilogues need an even number of 32-column sub-tiles");
   static_assert(KS % 2 == 0, "fragment register buffers alternate per sub-step");
 };
 
 template <class C, class Epi>
-__global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const bf16_t* __restrict__ X,
+__global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* __restrict__ X,
                                                          const bf16_t* __restrict__ W, int M, int N, int K,
                                                          Epi epi) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::STAGES, NW = C::NW;
@@ -326,11 +391,16 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const bf16_t* __restri
     for (int jp = 0; jp < TN / 2; ++jp) {
       const int c = n0 + wn * WTN + jp * 64 + lr;
       const bool ok0 = c < N, ok1 = c + 32 < N;
+      int rows[16];
+      float v0[16], v1[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
-        if (row < M) epi.pair(row, c, acc[i][2 * jp][r], acc[i][2 * jp + 1][r], ok0, ok1);
+        rows[r] = row < M ? row : -1;
+        v0[r] = acc[i][2 * jp][r];
+        v1[r] = acc[i][2 * jp + 1][r];
       }
+      epi.batch(rows, c, v0, v1, ok0, ok1);
     }
 }
 

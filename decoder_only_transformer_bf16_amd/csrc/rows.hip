@@ -31,6 +31,10 @@ __device__ __forceinline__ float4 mul4(float4 a, float4 b, float s) {
   return float4{a.x * b.x * s, a.y * b.y * s, a.z * b.z * s, a.w * b.w * s};
 }
 
+// Rows of up to kMaxV * 256 elements are held in registers (kMaxV float4 per lane),
+// so every load of a row is in flight before the reduction; longer rows loop.
+constexpr int kMaxV = 16;
+
 // y = x * w / sqrt(mean(x^2) + eps)  ("N7 · model/forward-parity", intro: RMSNorm)
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ w,
@@ -39,6 +43,28 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float* xr = x + (int64_t)row * H;
+  if (H <= kMaxV * 256) {
+    float4 v[kMaxV];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxV; ++j) {
+      const int i = lane * 4 + j * 256;
+      v[j] = i < H ? Vec4<float>::load(xr + i) : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxV; ++j) ss += sumsq4(v[j]);
+    ss = wave_sum(ss);
+    const float r = fast_rsqrt(ss / (float)H + eps);
+#pragma unroll
+    for (int j = 0; j < kMaxV; ++j) {
+      const int i = lane * 4 + j * 256;
+      if (i >= H) continue;
+      const float4 o = mul4(v[j], Vec4<float>::load(w + i), r);
+      Vec4<T>::store(y + (int64_t)row * H + i, o);
+      if (y32) Vec4<float>::store(y32 + (int64_t)row * H + i, o);
+    }
+    return;
+  }
   float ss = 0.f;
   for (int i = lane * 4; i < H; i += 256) ss += sumsq4(Vec4<float>::load(xr + i));
   ss = wave_sum(ss);
@@ -61,6 +87,41 @@ __global__ __launch_bounds__(256) void add_norm_kernel(const float* __restrict__
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const int64_t off = (int64_t)row * H;
+  if (H <= kMaxV * 256) {
+    float4 uv[kMaxV], xv[kMaxV];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxV; ++j) {
+      const int i = lane * 4 + j * 256;
+      uv[j] = i < H ? Vec4<float>::load(u + off + i) : float4{0.f, 0.f, 0.f, 0.f};
+      xv[j] = i < H ? Vec4<float>::load(xin + off + i) : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxV; ++j) ss += sumsq4(uv[j]);
+    ss = wave_sum(ss);
+    const float ru = fast_rsqrt(ss / (float)H + eps);
+    float sx = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxV; ++j) {
+      const int i = lane * 4 + j * 256;
+      if (i >= H) continue;
+      const float4 n = mul4(uv[j], Vec4<float>::load(wpost + i), ru);
+      xv[j] = float4{xv[j].x + n.x, xv[j].y + n.y, xv[j].z + n.z, xv[j].w + n.w};
+      Vec4<float>::store(xout + off + i, xv[j]);
+      sx += sumsq4(xv[j]);
+    }
+    sx = wave_sum(sx);
+    const float rx = fast_rsqrt(sx / (float)H + eps);
+#pragma unroll
+    for (int j = 0; j < kMaxV; ++j) {
+      const int i = lane * 4 + j * 256;
+      if (i >= H) continue;
+      const float4 v = mul4(xv[j], Vec4<float>::load(wnext + i), rx);
+      Vec4<T>::store(y + off + i, v);
+      if (y32) Vec4<float>::store(y32 + off + i, v);
+    }
+    return;
+  }
   float ss = 0.f;
   for (int i = lane * 4; i < H; i += 256) ss += sumsq4(Vec4<float>::load(u + off + i));
   ss = wave_sum(ss);
