@@ -168,14 +168,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, float sca
     if (kb0 + ST - 2 < kb1) wait_vmcnt<(ST - 2) * LPW>();
     else wait_vmcnt<0>();
   }
-  __syncthreads();
+  lds_barrier();
   if (active(kb0)) scores(kb0, sc);
 
   for (int kb = kb0; kb < kb1; ++kb) {
     if (kb + 1 < kb1) {
       if (kb + ST - 2 < kb1) wait_vmcnt<(ST - 3) * LPW>();  // block kb + 1 has landed
       else wait_vmcnt<0>();
-      __syncthreads();  // ... for everyone; and everyone is done with block kb - 1
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_barrier();  // ... for everyone; and everyone is done with block kb - 1
       if (kb + ST - 1 < kb1) issue_block(kb + ST - 1);  // refill block kb - 1's buffer
       if (active(kb + 1)) scores(kb + 1, sn);  // MFMAs that overlap the softmax below
     }

@@ -56,6 +56,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// Workgroup barrier without the memory fence of __syncthreads(): that fence makes
+// the compiler drain every outstanding buffer->LDS load (vmcnt(0)) first, which
+// would empty a multi-stage load pipeline at each step. Callers wait for exactly
+// what they need (s_waitcnt vmcnt / lgkmcnt) before calling it; the "memory"
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 // MFMA wrappers (CDNA4): D = A * B + C with fp32 accumulation.

@@ -214,8 +214,8 @@ __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, bf16_t* ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + blk * 512), 16, off, 0, 0, 0);
 }
 
-// The VGPR route: the same 1 KiB piece fetched into registers, then written to the
-// LDS position the DMA route would have used (byte 16 l of the piece).
+// The VGPR route: the same 1 KiB piece fetched into registers; put_block writes it
+// to the LDS position the DMA route would have used (byte 16 l of the piece).
 template <int BK>
 __device__ __forceinline__ u32x4_t fetch_block(__amdgpu_buffer_rsrc_t rs, int K, int k0, int blk, int lane) {
   constexpr int CH = BK / 8, RPB = 64 / CH;
@@ -224,6 +224,9 @@ __device__ __forceinline__ u32x4_t fetch_block(__amdgpu_buffer_rsrc_t rs, int K,
   const uint32_t off = kk < K ? (uint32_t)(row * K + kk) * 2u : 0x80000000u;
   return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
 }
+__device__ __forceinline__ void put_block(bf16_t* lds, int blk, int lane, const u32x4_t& v) {
+  *reinterpret_cast<u32x4_t*>(lds + blk * 512 + lane * 8) = v;
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -231,13 +234,45 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Accumulator layout of v_mfma_f32_32x32x16: register r of lane l holds row
+// 8 (r / 4) + 4 (l / 32) + r % 4 and column l % 32 of the 32x32 sub-tile. Hands a
+// wavefront's TM x TN sub-tiles (origin r0, c0) to the epilogue, 16 rows of one
+// column pair at a time.
+template <int TM, int TN, class Epi>
+__device__ __forceinline__ void write_tile(const Epi& epi, const floatx16_t (&acc)[TM][TN], int r0, int c0, int M,
+                                           int N, int lane) {
+  const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int jp = 0; jp < TN / 2; ++jp) {
+      const int c = c0 + jp * 64 + lr;
+      const bool ok0 = c < N, ok1 = c + 32 < N;
+      int rows[16];
+      float v0[16], v1[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+        rows[r] = row < M ? row : -1;
+        v0[r] = acc[i][2 * jp][r];
+        v1[r] = acc[i][2 * jp + 1][r];
+      }
+      epi.batch(rows, c, v0, v1, ok0, ok1);
+    }
+}
+
 // Tile configuration: BM x BN output tile, BK-wide K slices, STAGES LDS buffers,
 // WM x WN wavefronts (each owning a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles).
-template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, bool DMA_ = true, int OCC_ = 1>
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int OCC_ = 1, int BPOS_ = 1, int RPM_ = 2,
+          int LSPAN_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
-  static constexpr int OCC = OCC_;  // workgroups per CU the register budget is sized for
-  static constexpr bool DMA = DMA_;  // global -> LDS by buffer DMA, else through VGPRs + ds_write
+  static constexpr int OCC = OCC_;    // workgroups per CU the register budget is sized for
+  static constexpr int BPOS = BPOS_;  // the slice barrier precedes MFMA BPOS of the last sub-step
+  static constexpr int RPM = RPM_;    // fragment reads issued after each MFMA
+  // With two stages the refill of slice t + 1 must land before barrier t: its loads
+  // go out over the first LSPAN MFMAs of slice t (default: half the slice).
+  static constexpr int LSPAN = LSPAN_ > 0 ? LSPAN_ : (BK / 16) * (BM / WM / 32) * (BN / WN / 32) / 2;
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32, KS = BK / 16;
   static constexpr int LOADS_A = BM * (BK / 8) / 64 / NW;      // 1 KiB buffer loads per wave per slice
@@ -245,14 +280,24 @@ struct Cfg {
   static_assert(LOADS_A * NW * 64 == BM * (BK / 8) && LOADS * NW * 64 == (BM + BN) * (BK / 8), "load split");
   static constexpr int LDS_BYTES = STAGES * (BM + BN) * BK * 2;
   static_assert(LDS_BYTES * OCC <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 2, "one buffer being read, one being filled");
   static_assert(TN % 2 == 0, "pair epilogues need an even number of 32-column sub-tiles");
   static_assert(KS % 2 == 0, "fragment register buffers alternate per sub-step");
+  static_assert(BPOS >= 0 && BPOS + (TM + TN - 1) / RPM < TM * TN, "next-slice reads fit after the barrier");
 };
+
+// Fragment reads in the order the MFMAs of a sub-step consume them (MFMA x uses A
+// tile x % TM and B tile x / TM): A0, B0, A1 .. A(TM-1), B1 .. B(TN-1). Index f < TM
+// names A tile f, f >= TM names B tile f - TM.
+template <int TM>
+__device__ constexpr int need_frag(int n) {
+  return n == 0 ? 0 : n == 1 ? TM : n <= TM ? n - 1 : n;
+}
 
 template <class C, class Epi>
 __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* __restrict__ X,
-                                                         const bf16_t* __restrict__ W, int M, int N, int K,
-                                                         Epi epi) {
+                                                                  const bf16_t* __restrict__ W, int M, int N, int K,
+                                                                  Epi epi) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::STAGES, NW = C::NW;
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN, KS = C::KS;
   constexpr int SLICE = (BM + BN) * BK;  // elements per stage
@@ -274,49 +319,37 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx16_t{};
 
-  // Software pipeline. STAGES LDS buffers; slice t lives in buffer t % STAGES.
-  // Inside slice t, sub-step kk issues its TM x TN independent MFMAs, each followed
-  // by its share of the fragment reads for sub-step kk + 1. Halfway through the last
-  // sub-step (its fragments are in registers by then) one barrier both frees buffer
-  // t % STAGES and publishes slice t + 1; the second half of the MFMAs then carries
-  // the loads that refill the freed buffer with slice t + STAGES and the reads of
-  // slice t + 1's first fragments.
-  constexpr int MF = TM * TN, FR = TM + TN, H = MF / 2, LA = C::LOADS_A, LT = C::LOADS;
+  // Software pipeline over K slices; slice t lives in LDS buffer t % ST.
+  // One barrier per slice, early in its last sub-step (whose fragments were read
+  // during the previous sub-step): past barrier t every wavefront is done with
+  // buffer (t - 1) % ST and slice t + 1 has landed. While computing slice t, the
+  // wavefront refills buffer (t - 1) % ST with slice t + ST - 1, its LT
+  // buffer->LDS loads spread evenly over the slice's MFMAs so the address and data
+  // paths see a steady stream rather than a burst. Fragment reads for sub-step
+  // kk + 1 (for the last sub-step: the next slice's first, after the barrier) go
+  // out RPM per MFMA, front-loaded and in the order the MFMAs consume them, into
+  // the register set the current MFMAs are not using.
+  constexpr int MF = TM * TN, FR = TM + TN, LA = C::LOADS_A, LT = C::LOADS, RPM = C::RPM;
+  constexpr int G = KS * MF;                   // MFMAs per slice
+  constexpr int GB = (KS - 1) * MF + C::BPOS;  // the barrier sits before MFMA GB
+  // load p of a refill follows MFMA (p * LS) / LT; LPRE of them precede the barrier.
+  // With ST >= 3 the refill (slice t + ST - 1) may straddle the barrier; with two
+  // stages it is slice t + 1 itself and must be issued before it.
+  constexpr int LS = ST == 2 ? (C::LSPAN < GB ? C::LSPAN : GB) : G;
+  constexpr int LPRE = (GB * LT + LS - 1) / LS < LT ? (GB * LT + LS - 1) / LS : LT;
+  static_assert(ST > 2 || LPRE == LT, "two stages: every refill load precedes the barrier");
+  constexpr int WAIT_STEADY = ST == 2 ? 0 : (ST - 3) * LT + LPRE;  // loads allowed in flight at a barrier
+  static_assert(WAIT_STEADY < 64, "vmcnt range");
   const int nk = (K + BK - 1) / BK;
   auto issue_load = [&](int p, bf16_t* buf, int k0) {  // load p of this wave's share of one slice
     if (p < LA) load_block<BK>(ra, buf, K, k0, wave + p * NW, lane);
     else load_block<BK>(rb, buf + BM * BK, K, k0, wave + (p - LA) * NW, lane);
   };
-  u32x4_t stage[C::DMA ? 1 : LT];  // VGPR route: one slice in flight in registers
-  auto fetch = [&](int p, int k0) {
-    if constexpr (!C::DMA) {
-      if (p < LA) stage[p] = fetch_block<BK>(ra, K, k0, wave + p * NW, lane);
-      else stage[p] = fetch_block<BK>(rb, K, k0, wave + (p - LA) * NW, lane);
-    }
-  };
-  auto put = [&](int p, bf16_t* buf) {
-    if constexpr (!C::DMA) {
-      bf16_t* dst = p < LA ? buf + (wave + p * NW) * 512 : buf + BM * BK + (wave + (p - LA) * NW) * 512;
-      *reinterpret_cast<u32x4_t*>(dst + lane * 8) = stage[p];
-    }
-  };
-  if constexpr (C::DMA) {
 #pragma unroll
-    for (int q = 0; q < ST; ++q)
-      if (q < nk)
+  for (int q = 0; q < ST - 1; ++q)
+    if (q < nk)
 #pragma unroll
-        for (int p = 0; p < LT; ++p) issue_load(p, lds + q * SLICE, q * BK);
-  } else {
-    static_assert(ST == 2, "the VGPR route stages one slice in registers beside two LDS buffers");
-#pragma unroll
-    for (int p = 0; p < LT; ++p) fetch(p, 0);
-    wait_vmcnt<0>();
-#pragma unroll
-    for (int p = 0; p < LT; ++p) put(p, lds);
-    if (nk > 1)
-#pragma unroll
-      for (int p = 0; p < LT; ++p) fetch(p, BK);
-  }
+      for (int p = 0; p < LT; ++p) issue_load(p, lds + q * SLICE, q * BK);
   const int lr = lane & 31, lk = lane >> 5;
   const int arow = wm * WTM + lr, brow = BM + wn * WTN + lr;  // tile rows this lane reads (+32 i / +32 j)
   bf16x8_t fa[2][TM], fb[2][TN];
@@ -324,84 +357,51 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
     if (f < TM) fa[buf][f] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(base + lds_off<BK>(arow + f * 32, kk * 2 + lk)));
     else fb[buf][f - TM] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(base + lds_off<BK>(brow + (f - TM) * 32, kk * 2 + lk)));
   };
-  if constexpr (C::DMA) {
-    if (nk > 1) wait_vmcnt<(ST - 1) * LT>();
-    else wait_vmcnt<0>();
-  }
-  __syncthreads();
+  if (nk >= ST - 1) wait_vmcnt<(ST - 2) * LT>();  // slice 0 has landed
+  else wait_vmcnt<0>();
+  lds_barrier();
 #pragma unroll
   for (int f = 0; f < FR; ++f) read_frag(lds, f, 0, 0);
 
   for (int kt = 0; kt < nk; ++kt) {
-    bf16_t* cur = lds + (kt % ST) * SLICE;
+    const bf16_t* cur = lds + (kt % ST) * SLICE;
     const bf16_t* nxt = lds + ((kt + 1) % ST) * SLICE;
-    const bool refill = kt + ST < nk;
-    const bool refetch = kt + 2 < nk;  // VGPR route: fetch slice kt + 2 after the barrier
+    bf16_t* fill = lds + ((kt + ST - 1) % ST) * SLICE;
+    const bool refill = kt + ST - 1 < nk;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int rb_ = kk & 1, wb = rb_ ^ 1;  // register buffers: read from rb_, prefetch into wb
 #pragma unroll
       for (int x = 0; x < MF; ++x) {
-        if (kk == KS - 1 && x == H) {
+        const int g = kk * MF + x;
+        if (g == GB) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // all of slice kt is in registers
-          if constexpr (C::DMA) {
-            if (kt + 1 < nk) {
-              if (kt + ST - 1 < nk) wait_vmcnt<(ST - 2) * LT>();  // slice kt + 1 has landed
-              else wait_vmcnt<0>();
-            }
-          } else if (kt + 1 < nk) {
-            // slice kt + 1 sits in the staging registers: write it to the buffer slice
-            // kt - 1 used (free since the previous barrier)
-            wait_vmcnt<0>();
-#pragma unroll
-            for (int p = 0; p < LT; ++p) put(p, const_cast<bf16_t*>(nxt));
-          }
-          __syncthreads();
+          if (refill) wait_vmcnt<WAIT_STEADY>();  // slice kt + 1 has landed
+          else wait_vmcnt<0>();
+          lds_barrier();
         }
         const int i = x % TM, j = x / TM;
         acc[i][j] = mfma_32x32x16_bf16(fa[rb_][i], fb[rb_][j], acc[i][j]);
         if (kk + 1 < KS) {
 #pragma unroll
-          for (int f = (x * FR) / MF; f < ((x + 1) * FR) / MF; ++f) read_frag(cur, f, kk + 1, wb);
-        } else if (x >= H) {
-          const int y = x - H;
+          for (int n = x * RPM; n < (x + 1) * RPM && n < FR; ++n) read_frag(cur, need_frag<TM>(n), kk + 1, wb);
+        } else if (x >= C::BPOS) {
+          const int y = x - C::BPOS;
           // (on the last slice this reads a stale but in-bounds buffer; never used)
 #pragma unroll
-          for (int f = (y * FR) / (MF - H); f < ((y + 1) * FR) / (MF - H); ++f) read_frag(nxt, f, 0, wb);
-          if constexpr (C::DMA) {
-            if (refill) {
+          for (int n = y * RPM; n < (y + 1) * RPM && n < FR; ++n) read_frag(nxt, need_frag<TM>(n), 0, wb);
+        }
+        if (refill) {
 #pragma unroll
-              for (int p = (y * LT) / (MF - H); p < ((y + 1) * LT) / (MF - H); ++p) issue_load(p, cur, (kt + ST) * BK);
-            }
-          } else if (refetch) {
-#pragma unroll
-            for (int p = (y * LT) / (MF - H); p < ((y + 1) * LT) / (MF - H); ++p) fetch(p, (kt + 2) * BK);
-          }
+          for (int p = 0; p < LT; ++p)
+            if ((p * LS) / LT == g) issue_load(p, fill, (kt + ST - 1) * BK);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
-  // Accumulator layout of v_mfma_f32_32x32x16: register r of lane l holds
-  // row 8 (r / 4) + 4 (l / 32) + r % 4 and column l % 32 of the 32x32 sub-tile.
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int jp = 0; jp < TN / 2; ++jp) {
-      const int c = n0 + wn * WTN + jp * 64 + lr;
-      const bool ok0 = c < N, ok1 = c + 32 < N;
-      int rows[16];
-      float v0[16], v1[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
-        rows[r] = row < M ? row : -1;
-        v0[r] = acc[i][2 * jp][r];
-        v1[r] = acc[i][2 * jp + 1][r];
-      }
-      epi.batch(rows, c, v0, v1, ok0, ok1);
-    }
+  write_tile<TM, TN>(epi, acc, m0 + wm * WTM, n0 + wn * WTN, M, N, lane);
 }
 
 template <class C, class Epi>
@@ -412,8 +412,197 @@ hipError_t launch_cfg(const void* X, const void* W, int M, int N, int K, const E
   return hipGetLastError();
 }
 
-using CfgBig = Cfg<256, 256, 64, 2, 2, 4>;  // 8 wavefronts: two per SIMD
-using CfgSmall = Cfg<128, 128, 64, 2, 2, 2>;
+using CfgSmall = Cfg<128, 128, 32, 4, 2, 2>;
+
+
+// ------------------------------------------------------------------ ping-pong kernel
+// 8 wavefronts, two per SIMD, in two groups of four (waves 0-3 and 4-7, one of
+// each group per SIMD). The groups alternate between a compute phase (all MFMAs
+// of one K slice on fragments already in registers) and a memory phase (the
+// fragment reads of the next slice from LDS, plus a share of the buffer->LDS
+// loads of a later slice), one workgroup barrier apart, so that each SIMD's
+// matrix pipe is fed by one wavefront while the other waits on memory.
+//   group 0: memory(s) in step 2s,     compute(s) in step 2s + 1
+//   group 1: memory(s) in step 2s + 1, compute(s) in step 2s + 2
+// Slice s lives in buffer s % ST; memory(s) also loads slice s + ST - 1 into
+// buffer (s - 1) % ST, free since the barrier ending step 2s - 1. Every barrier
+// ending an odd step has slice s + 1 landed (each wavefront waits for its own
+// loads of it first), which memory(s + 1) of group 0 needs at step 2s + 2.
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int RS_ = 0>
+struct PPCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
+  static constexpr int RS = RS_;  // 0: buffer->LDS DMA; else slices staged in registers (VGPR route)
+  static constexpr int NW = WM * WN, NT = NW * 64;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32, KS = BK / 16;
+  static constexpr int LOADS_A = BM * (BK / 8) / 64 / NW;
+  static constexpr int LOADS = (BM + BN) * (BK / 8) / 64 / NW;
+  static_assert(NW == 8, "two groups of four wavefronts");
+  static_assert(LOADS_A * NW * 64 == BM * (BK / 8) && LOADS * NW * 64 == (BM + BN) * (BK / 8), "load split");
+  static constexpr int LDS_BYTES = STAGES * (BM + BN) * BK * 2;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 3, "the lagging group still reads slice s - 1 while slice s + ST - 1 loads");
+  static_assert(TN % 2 == 0, "pair epilogues need an even number of 32-column sub-tiles");
+  static_assert((STAGES - 2) * LOADS < 64, "vmcnt range");
+};
+
+template <class C, class Epi>
+__global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
+                                                        int M, int N, int K, Epi epi) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::STAGES, NW = C::NW;
+  constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN, KS = C::KS;
+  constexpr int SLICE = (BM + BN) * BK, LA = C::LOADS_A, LT = C::LOADS, FR = TM + TN;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[ST * SLICE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int nTM = (M + BM - 1) / BM, nTN = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, nTM, nTN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(X + (int64_t)m0 * K, (int64_t)min(BM, M - m0) * K * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + (int64_t)n0 * K, (int64_t)min(BN, N - n0) * K * 2);
+  const int nk = (K + BK - 1) / BK;
+  auto issue_load = [&](int p, bf16_t* buf, int k0) {
+    if (p < LA) load_block<BK>(ra, buf, K, k0, wave + p * NW, lane);
+    else load_block<BK>(rb, buf + BM * BK, K, k0, wave + (p - LA) * NW, lane);
+  };
+  const int lr = lane & 31, lk = lane >> 5;
+  const int arow = wm * WTM + lr, brow = BM + wn * WTN + lr;
+  bf16x8_t fa[KS][TM], fb[KS][TN];
+  auto read_slice = [&](const bf16_t* base) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int n = 0; n < FR; ++n) {
+        const int f = need_frag<TM>(n);
+        if (f < TM) fa[kk][f] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(base + lds_off<BK>(arow + f * 32, kk * 2 + lk)));
+        else fb[kk][f - TM] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(base + lds_off<BK>(brow + (f - TM) * 32, kk * 2 + lk)));
+      }
+    }
+  };
+
+  floatx16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx16_t{};
+
+  constexpr int RS = C::RS;
+  u32x4_t stage[RS > 0 ? RS : 1][LT];  // VGPR route: slices in flight in registers
+  auto fetch = [&](int slot, int k0) {
+#pragma unroll
+    for (int p = 0; p < LT; ++p)
+      stage[slot][p] = p < LA ? fetch_block<BK>(ra, K, k0, wave + p * NW, lane)
+                              : fetch_block<BK>(rb, K, k0, wave + (p - LA) * NW, lane);
+  };
+  auto put = [&](int slot, bf16_t* buf) {
+#pragma unroll
+    for (int p = 0; p < LT; ++p) {
+      if (p < LA) put_block(buf, wave + p * NW, lane, stage[slot][p]);
+      else put_block(buf + BM * BK, wave + (p - LA) * NW, lane, stage[slot][p]);
+    }
+  };
+  auto compute = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int x = 0; x < TM * TN; ++x) {
+        const int i = x % TM, j = x / TM;
+        acc[i][j] = mfma_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j]);
+      }
+  };
+
+  if constexpr (RS == 0) {
+#pragma unroll
+    for (int q = 0; q < ST - 1; ++q)
+      if (q < nk)
+#pragma unroll
+        for (int p = 0; p < LT; ++p) issue_load(p, lds + q * SLICE, q * BK);
+    if (nk >= ST - 1) wait_vmcnt<(ST - 2) * LT>();  // slice 0 has landed
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (group == 1) lds_barrier();  // group 1 runs one step behind
+
+    for (int s = 0; s < nk; ++s) {
+      // memory(s)
+      read_slice(lds + (s % ST) * SLICE);
+      const bool refill = s + ST - 1 < nk;
+      if (refill) {
+        bf16_t* fill = lds + ((s + ST - 1) % ST) * SLICE;
+#pragma unroll
+        for (int p = 0; p < LT; ++p) issue_load(p, fill, (s + ST - 1) * BK);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // fragments in registers, buffer s % ST read
+      if (group == 1) {  // this barrier ends an odd step: slice s + 1 must have landed
+        if (refill) wait_vmcnt<(ST - 2) * LT>();
+        else wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      compute();  // compute(s)
+      __builtin_amdgcn_sched_barrier(0);
+      if (group == 0) {  // this barrier ends an odd step
+        if (refill) wait_vmcnt<(ST - 2) * LT>();
+        else wait_vmcnt<0>();
+      }
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // VGPR route: memory(s) writes slice s + 1 from registers into buffer (s + 1) % ST,
+    // refills those registers with slice s + 1 + RS, then reads slice s's fragments.
+    // Slice s + 1 is visible after the barrier ending step 2s + 1 (both groups have
+    // written their parts and drained lgkmcnt); buffer (s + 1) % ST last held slice
+    // s + 1 - ST, read by group 1 in step 2s + 3 - 2 ST < 2s.
+    static_assert(ST >= 3, "buffer reuse distance");
+    static_assert(RS == 1, "register slots are indexed by slice parity only when RS == 1");
+    fetch(0, 0);
+    wait_vmcnt<0>();
+    put(0, lds);
+#pragma unroll
+    for (int q = 1; q <= RS; ++q)
+      if (q < nk) fetch(q % RS, q * BK);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (group == 1) lds_barrier();
+
+    for (int s = 0; s < nk; ++s) {
+      if (s + 1 < nk) {
+        if (s + RS < nk) wait_vmcnt<(RS - 1) * LT>();  // slice s + 1 is in registers
+        else wait_vmcnt<0>();
+        put((s + 1) % RS, lds + ((s + 1) % ST) * SLICE);
+        if (s + 1 + RS < nk) fetch((s + 1) % RS, (s + 1 + RS) * BK);
+      }
+      read_slice(lds + (s % ST) * SLICE);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      compute();
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (group == 0) lds_barrier();  // matches group 1's extra barrier
+
+  write_tile<TM, TN>(epi, acc, m0 + wm * WTM, n0 + wn * WTN, M, N, lane);
+}
+
+// 8 wavefronts (two per SIMD) in ping-pong, 64 x 128 outputs each, four K slices of
+// 32 in flight
+using CfgBig = PPCfg<256, 256, 32, 4, 4, 2>;
+
+template <class C, class Epi>
+hipError_t launch_pp(const void* X, const void* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
+  const int grid = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL((gemm_pp_kernel<C, Epi>), dim3(grid), dim3(C::NT), 0, s, (const bf16_t*)X, (const bf16_t*)W,
+                     M, N, K, epi);
+  return hipGetLastError();
+}
 
 // ------------------------------------------------------------------ f32 VALU kernel
 // 64x64 output tile, 256 threads, 4x4 outputs per thread, K slices of 16.
@@ -465,7 +654,7 @@ template <class Epi>
 hipError_t launch_bf16(const void* X, const void* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 256) return launch_cfg<CfgBig>(X, W, M, N, K, epi, s);
+  if (big >= 256) return launch_pp<CfgBig>(X, W, M, N, K, epi, s);
   return launch_cfg<CfgSmall>(X, W, M, N, K, epi, s);
 }
 
