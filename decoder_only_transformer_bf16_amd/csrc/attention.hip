@@ -261,7 +261,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, float sca
   }
 
   // normalise and store: register r of d tile dt is dim 32 dt + 8 (r / 4) + 4 lg + r % 4
-  bf16_t* obase = (bf16_t*)a.o + (int64_t)b * S * a.ldo + h * D;
+  // o row b * S + qi, columns h * D + d: row-major with stride ldo, or K-tiled with
+  // row width ldo (four consecutive columns never cross a 32-wide tile)
+  bf16_t* obase = (bf16_t*)a.o + (a.o_tiled ? 0 : (int64_t)b * S * a.ldo + h * D);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     float lt = l[qt];
@@ -274,7 +276,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, float sca
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const floatx16_t& v = o[dt][qt];
-          *reinterpret_cast<u32x2_t*>(obase + (int64_t)qi * a.ldo + dt * 32 + a4 * 8 + lg * 4) =
+          const int d = dt * 32 + a4 * 8 + lg * 4;
+          const int64_t at = a.o_tiled ? tiled_index((int64_t)b * S + qi, h * D + d, (int)a.ldo) : (int64_t)qi * a.ldo + d;
+          *reinterpret_cast<u32x2_t*>(obase + at) =
               u32x2_t{pack_bf16x2(v[4 * a4] * inv, v[4 * a4 + 1] * inv), pack_bf16x2(v[4 * a4 + 2] * inv, v[4 * a4 + 3] * inv)};
         }
     }
@@ -404,6 +408,7 @@ bool attention_supported(DType dt, int D) {
 
 hipError_t attention(DType dt, const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
+  if (a.o_tiled && (dt != DType::BF16 || a.ldo != (int64_t)a.Hq * a.D || a.ldo % 32)) return hipErrorInvalidValue;
   if (dt == DType::BF16) {
     switch (a.D) {
       case 64: return launch_bf16<64>(a, s);

@@ -56,6 +56,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// K-tiled bf16 operand layout: a [rows, K] matrix (K a multiple of 32) stored as
+// 16 x 32 tiles of 1 KiB, tile (r / 16, c / 32) at element ((r / 16) * (K / 32) +
+// c / 32) * 512, row-major inside the tile. A GEMM reads one tile per 64-lane
+// 16-byte load, i.e. 1 KiB of contiguous memory, where a row-major layout would
+// touch sixteen half cache lines. Row count is padded to a multiple of 16.
+__device__ __forceinline__ int64_t tiled_index(int64_t r, int c, int K) {
+  return ((r >> 4) * (K >> 5) + (c >> 5)) * 512 + (r & 15) * 32 + (c & 31);
+}
+
 // Workgroup barrier without the memory fence of __syncthreads(): that fence makes
 // the compiler drain every outstanding buffer->LDS load (vmcnt(0)) first, which
 // would empty a multi-stage load pipeline at each step. Callers wait for exactly

@@ -62,8 +62,9 @@ int check_config(const fwd_config* c) {
   const int vec = dt == DType::BF16 ? 8 : 4;
   if (c->hidden % vec || c->ffn % vec || (c->n_heads * c->head_dim) % vec)
     return fail(FWD_E_CONFIG, "hidden, ffn and n_heads*head_dim must be multiples of 8 (bf16) / 4 (f32)");
-  if (dt == DType::BF16 && (c->ffn % 32 || (c->n_heads * c->head_dim) % 32 || (c->n_kv_heads * c->head_dim) % 32))
-    return fail(FWD_E_CONFIG, "bf16 needs ffn and head widths that are multiples of 32");
+  if (dt == DType::BF16 && (c->hidden % 32 || c->ffn % 32 || (c->n_heads * c->head_dim) % 32 ||
+                            (c->n_kv_heads * c->head_dim) % 32))
+    return fail(FWD_E_CONFIG, "bf16 needs hidden, ffn and head widths that are multiples of 32");
   if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return fail(FWD_E_CONFIG, "rms_eps must be positive");
   if (!(c->rope_theta > 1.0) || !std::isfinite(c->rope_theta)) return fail(FWD_E_CONFIG, "rope_theta must be > 1");
   if (std::isnan(c->final_logit_softcap) || c->final_logit_softcap < 0.f || std::isinf(c->final_logit_softcap))
@@ -81,21 +82,26 @@ int check_config(const fwd_config* c) {
   return FWD_OK;
 }
 
+// bf16 GEMM operands (weights, normalised activations, attention and SwiGLU
+// outputs) are kept K-tiled (16 x 32 tiles, rows padded to 16); f32 is row-major.
 struct Geometry {
   int64_t esize, H, Hq, Hkv, D, F, V, L, T, qkv_rows, logit_chunk;
+  bool tiled;
+  int64_t rows(int64_t r) const { return tiled ? round_up(r, 16) : r; }  // allocated rows of an operand
   int64_t weight_bytes() const {
-    const int64_t per_layer = (qkv_rows * H + H * Hq * D + 2 * F * H + H * F) * esize + 4 * H * 4;
-    return V * H * esize + H * 4 + L * per_layer;
+    const int64_t per_layer =
+        (rows(qkv_rows) * H + rows(H) * Hq * D + rows(2 * F) * H + rows(H) * F) * esize + 4 * H * 4;
+    return rows(V) * H * esize + H * 4 + L * per_layer;
   }
   // Workspace (bytes, each buffer rounded to 256) for up to T tokens.
   int64_t workspace_bytes(bool sandwich) const {
     auto r = [](int64_t b) { return round_up(b, 256); };
     int64_t w = 2 * r(T * H * 4);                       // residual stream, mid-layer copy
-    w += r(T * H * esize);                              // normalised activations
+    w += r(rows(T) * H * esize);                        // normalised activations
     w += r(T * (Hq + 2 * Hkv) * D * esize);             // rotated q | rotated k | v
     w += r(8 * T * Hkv * D * esize);                    // transposed v, padded keys
-    w += r(T * Hq * D * esize);                         // attention output
-    w += r(T * F * esize);                              // SwiGLU output
+    w += r(rows(T) * Hq * D * esize);                   // attention output
+    w += r(rows(T) * F * esize);                        // SwiGLU output
     if (sandwich) w += r(T * H * 4);                    // sublayer output before its norm
     w += r(T * 4) + r(T * 4) + 256;                     // ids, argmax, flag
     w += r(logit_chunk * V * 4);                        // logits when the caller wants none
@@ -116,7 +122,8 @@ Geometry geometry(const fwd_config* c) {
   g.L = c->n_layers;
   g.T = c->max_tokens;
   g.qkv_rows = (g.Hq + 2 * g.Hkv) * g.D;
-  g.logit_chunk = std::min<int64_t>(g.T, 1024);
+  g.logit_chunk = std::min<int64_t>(g.T, 1024);  // a multiple of 16 whenever it splits T
+  g.tiled = c->dtype == FWD_DTYPE_BF16;
   return g;
 }
 
@@ -301,11 +308,6 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
 
   auto run = [&]() -> int {
     // ---- weights ----
-    if (int rc = m->alloc(&m->embed, g.V * g.H * g.esize)) return rc;
-    HIP_TRY(hipMemcpyAsync(m->embed, w->embed, g.V * g.H * g.esize, hipMemcpyDeviceToDevice, s));
-    if (int rc = m->alloc((void**)&m->final_norm, g.H * 4)) return rc;
-    HIP_TRY(fwdk::gains_to_f32(m->dt, w->final_norm, m->final_norm, (int)g.H, s));
-
     // row maps, uploaded once
     std::vector<int32_t> maps;
     auto append = [&](const std::vector<int32_t>& v) {
@@ -318,6 +320,7 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     const size_t mv = append(identity_map((int)(g.Hkv * g.D), (int)((g.Hq + g.Hkv) * g.D)));
     const size_t mg = append(glu_row_map((int)g.F, C, 0));
     const size_t mu = append(glu_row_map((int)g.F, C, 1));
+    const size_t mid = append(identity_map((int)std::max(g.V, std::max(g.H, g.F)), 0));
     int32_t* dmaps = nullptr;
     HIP_TRY(hipMalloc((void**)&dmaps, maps.size() * 4));
     struct Free {
@@ -326,7 +329,24 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     } free_maps{dmaps};
     HIP_TRY(hipMemcpyAsync(dmaps, maps.data(), maps.size() * 4, hipMemcpyHostToDevice, s));
 
-    const int64_t rowH = g.H * g.esize;
+    // dst[map[r], :] = src[r, :] for an operand of `rows` (allocated g.rows(rows)) x K,
+    // K-tiled for bf16 (padding rows cleared), row-major for f32
+    auto place = [&](void* dst, int64_t dst_rows, const void* src, size_t map, int rows, int64_t K) -> int {
+      if (g.tiled) {
+        HIP_TRY(hipMemsetAsync(dst, 0, g.rows(dst_rows) * K * g.esize, s));
+        HIP_TRY(fwdk::pack_tiled(dst, src, dmaps + map, rows, (int)K, s));
+      } else {
+        HIP_TRY(fwdk::copy_rows(dst, src, dmaps + map, rows, K * g.esize, s));
+      }
+      return FWD_OK;
+    };
+    auto alloc_operand = [&](void** p, int64_t rows, int64_t K) { return m->alloc(p, g.rows(rows) * K * g.esize); };
+
+    if (int rc = alloc_operand(&m->embed, g.V, g.H)) return rc;
+    if (int rc = place(m->embed, g.V, w->embed, mid, (int)g.V, g.H)) return rc;
+    if (int rc = m->alloc((void**)&m->final_norm, g.H * 4)) return rc;
+    HIP_TRY(fwdk::gains_to_f32(m->dt, w->final_norm, m->final_norm, (int)g.H, s));
+
     m->layers.resize(g.L);
     for (int l = 0; l < g.L; ++l) {
       const fwd_layer_weights& W = w->layers[l];
@@ -342,18 +362,27 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
         HIP_TRY(fwdk::gains_to_f32(m->dt, W.post_attn_norm, L.post_attn, (int)g.H, s));
         HIP_TRY(fwdk::gains_to_f32(m->dt, W.post_ffn_norm, L.post_ffn, (int)g.H, s));
       }
-      if (int rc = m->alloc(&L.wqkv, g.qkv_rows * rowH)) return rc;
-      HIP_TRY(fwdk::copy_rows(L.wqkv, W.wq, dmaps + mq, (int)(g.Hq * g.D), rowH, s));
-      HIP_TRY(fwdk::copy_rows(L.wqkv, W.wk, dmaps + mk, (int)(g.Hkv * g.D), rowH, s));
-      HIP_TRY(fwdk::copy_rows(L.wqkv, W.wv, dmaps + mv, (int)(g.Hkv * g.D), rowH, s));
-      if (int rc = m->alloc(&L.wgu, 2 * g.F * rowH)) return rc;
-      HIP_TRY(fwdk::copy_rows(L.wgu, W.w_gate, dmaps + mg, (int)g.F, rowH, s));
-      HIP_TRY(fwdk::copy_rows(L.wgu, W.w_up, dmaps + mu, (int)g.F, rowH, s));
-      if (int rc = m->alloc(&L.wo, g.H * g.Hq * g.D * g.esize)) return rc;
-      HIP_TRY(hipMemcpyAsync(L.wo, W.wo, g.H * g.Hq * g.D * g.esize, hipMemcpyDeviceToDevice, s));
-      if (int rc = m->alloc(&L.wdown, g.H * g.F * g.esize)) return rc;
-      HIP_TRY(hipMemcpyAsync(L.wdown, W.w_down, g.H * g.F * g.esize, hipMemcpyDeviceToDevice, s));
+      if (int rc = alloc_operand(&L.wqkv, g.qkv_rows, g.H)) return rc;
+      if (g.tiled) HIP_TRY(hipMemsetAsync(L.wqkv, 0, g.rows(g.qkv_rows) * g.H * g.esize, s));
+      // (three sources into one operand: clear once, then pack each)
+      auto put = [&](void* dst, const void* src, size_t map, int rows, int64_t K) -> int {
+        if (g.tiled) HIP_TRY(fwdk::pack_tiled(dst, src, dmaps + map, rows, (int)K, s));
+        else HIP_TRY(fwdk::copy_rows(dst, src, dmaps + map, rows, K * g.esize, s));
+        return FWD_OK;
+      };
+      if (int rc = put(L.wqkv, W.wq, mq, (int)(g.Hq * g.D), g.H)) return rc;
+      if (int rc = put(L.wqkv, W.wk, mk, (int)(g.Hkv * g.D), g.H)) return rc;
+      if (int rc = put(L.wqkv, W.wv, mv, (int)(g.Hkv * g.D), g.H)) return rc;
+      if (int rc = alloc_operand(&L.wgu, 2 * g.F, g.H)) return rc;
+      if (g.tiled) HIP_TRY(hipMemsetAsync(L.wgu, 0, g.rows(2 * g.F) * g.H * g.esize, s));
+      if (int rc = put(L.wgu, W.w_gate, mg, (int)g.F, g.H)) return rc;
+      if (int rc = put(L.wgu, W.w_up, mu, (int)g.F, g.H)) return rc;
+      if (int rc = alloc_operand(&L.wo, g.H, g.Hq * g.D)) return rc;
+      if (int rc = place(L.wo, g.H, W.wo, mid, (int)g.H, g.Hq * g.D)) return rc;
+      if (int rc = alloc_operand(&L.wdown, g.H, g.F)) return rc;
+      if (int rc = place(L.wdown, g.H, W.w_down, mid, (int)g.H, g.F)) return rc;
     }
+    HIP_TRY(hipStreamSynchronize(s));  // the row maps are freed at scope end
 
     // ---- RoPE table: angle(t, k) = t * theta^(-2k/D), computed in double ----
     {
@@ -372,11 +401,11 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     const int64_t T = g.T;
     if (int rc = m->alloc((void**)&m->x, T * g.H * 4)) return rc;
     if (int rc = m->alloc((void**)&m->xb, T * g.H * 4)) return rc;
-    if (int rc = m->alloc(&m->n, T * g.H * g.esize)) return rc;
+    if (int rc = m->alloc(&m->n, g.rows(T) * g.H * g.esize)) return rc;
     if (int rc = m->alloc(&m->qk, T * (g.Hq + 2 * g.Hkv) * g.D * g.esize)) return rc;
     if (int rc = m->alloc(&m->vt, 8 * T * g.Hkv * g.D * g.esize)) return rc;
-    if (int rc = m->alloc(&m->o, T * g.Hq * g.D * g.esize)) return rc;
-    if (int rc = m->alloc(&m->a, T * g.F * g.esize)) return rc;
+    if (int rc = m->alloc(&m->o, g.rows(T) * g.Hq * g.D * g.esize)) return rc;
+    if (int rc = m->alloc(&m->a, g.rows(T) * g.F * g.esize)) return rc;
     if (sandwich)
       if (int rc = m->alloc((void**)&m->u, T * g.H * 4)) return rc;
     if (int rc = m->alloc((void**)&m->ids, T * 4)) return rc;
@@ -420,6 +449,7 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
   const bool sandwich = m->cfg.norm_placement == FWD_NORM_SANDWICH;
   const int64_t TH = T * H;
   float* hidden = o.hidden;
+  const bool tl = g.tiled;
 
   m->marks.clear();
   m->events_used = 0;
@@ -427,9 +457,9 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
   HIP_TRY(hipMemsetAsync(m->flag, 0, 4, s));
 
   float* cur = hidden ? hidden : m->x;
-  TIMED(m, FWD_KERNEL_EMBED, fwdk::embed(dt, m->ids, m->embed, cur, M, H, m->embed_scale, s));
+  TIMED(m, FWD_KERNEL_EMBED, fwdk::embed(dt, m->ids, m->embed, cur, M, H, m->embed_scale, tl, s));
   // first layer's input norm; every later sublayer input norm is fused below
-  if (L > 0) TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, cur, m->layers[0].attn_norm, m->n, nullptr, M, H, eps, s));
+  if (L > 0) TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, cur, m->layers[0].attn_norm, m->n, nullptr, M, H, eps, tl, s));
 
   const int ldvt = (int)round_up(S, 8);
   char* qk = (char*)m->qk;
@@ -443,7 +473,7 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
 
     // attention sublayer (its input norm is already in m->n)
     fwdk::RopeArgs ra{m->qk, m->rope_cs, Hq, Hkv, D, S};
-    TIMED(m, FWD_KERNEL_QKV_ROPE, fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, s));
+    TIMED(m, FWD_KERNEL_QKV_ROPE, fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, tl, s));
     const int64_t ldqkv = (int64_t)(Hq + 2 * Hkv) * D;
     TIMED(m, FWD_KERNEL_V_TRANSPOSE,
           fwdk::transpose_v(dt, qk + (int64_t)(Hq + Hkv) * D * g.esize, ldqkv, m->vt, ldvt, B, S, Hkv * D, s));
@@ -461,44 +491,45 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
     aa.Hkv = Hkv;
     aa.D = D;
     aa.window = m->kinds[l] == FWD_LAYER_LOCAL ? m->cfg.sliding_window : 0;
+    aa.o_tiled = tl;
     TIMED(m, FWD_KERNEL_ATTENTION, fwdk::attention(dt, aa, s));
     if (!sandwich) {
-      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_residual(dt, m->o, w.wo, xin, xmid, M, H, Hq * D, s));
-      TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, s));
+      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_residual(dt, m->o, w.wo, xin, xmid, M, H, Hq * D, tl, s));
+      TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, tl, s));
     } else {
-      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_store(dt, m->o, w.wo, m->u, H, M, H, Hq * D, 0.f, s));
-      TIMED(m, FWD_KERNEL_NORM, fwdk::add_norm(dt, xin, m->u, w.post_attn, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, s));
+      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_store(dt, m->o, w.wo, m->u, H, M, H, Hq * D, 0.f, tl, s));
+      TIMED(m, FWD_KERNEL_NORM, fwdk::add_norm(dt, xin, m->u, w.post_attn, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, tl, s));
     }
 
     // feed-forward sublayer
-    TIMED(m, FWD_KERNEL_GATE_UP, fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, s));
+    TIMED(m, FWD_KERNEL_GATE_UP, fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, tl, s));
     float* final32 = (last && hidden) ? hidden + (int64_t)(L + 1) * TH : nullptr;
     if (!sandwich) {
-      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, s));
-      TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xout, next_norm, m->n, final32, M, H, eps, s));
+      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, tl, s));
+      TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xout, next_norm, m->n, final32, M, H, eps, tl, s));
     } else {
-      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_store(dt, m->a, w.wdown, m->u, H, M, H, F, 0.f, s));
-      TIMED(m, FWD_KERNEL_NORM, fwdk::add_norm(dt, xmid, m->u, w.post_ffn, xout, next_norm, m->n, final32, M, H, eps, s));
+      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_store(dt, m->a, w.wdown, m->u, H, M, H, F, 0.f, tl, s));
+      TIMED(m, FWD_KERNEL_NORM, fwdk::add_norm(dt, xmid, m->u, w.post_ffn, xout, next_norm, m->n, final32, M, H, eps, tl, s));
     }
     cur = xout;
   }
   if (L == 0) {
     float* final32 = hidden ? hidden + TH : nullptr;
-    TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, cur, m->final_norm, m->n, final32, M, H, eps, s));
+    TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, cur, m->final_norm, m->n, final32, M, H, eps, tl, s));
   }
 
   // tied LM head (+ softcap) and argmax
   const float cap = m->cfg.final_logit_softcap;
   int32_t* am = o.argmax ? o.argmax : m->amax;
   if (o.logits) {
-    TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, m->n, m->embed, o.logits, V, M, V, H, cap, s));
+    TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, m->n, m->embed, o.logits, V, M, V, H, cap, tl, s));
     TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(o.logits, V, M, V, am, m->flag, s));
   } else {
     const int64_t chunk = g.logit_chunk;
     for (int64_t r0 = 0; r0 < T; r0 += chunk) {
       const int rows = (int)std::min<int64_t>(chunk, T - r0);
-      const char* nrow = (const char*)m->n + r0 * H * g.esize;
-      TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, nrow, m->embed, m->logits_ws, V, rows, V, H, cap, s));
+      const char* nrow = (const char*)m->n + r0 * H * g.esize;  // (r0 is a multiple of 16: a tile row)
+      TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, nrow, m->embed, m->logits_ws, V, rows, V, H, cap, tl, s));
       TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(m->logits_ws, V, rows, V, am + r0, m->flag, s));
     }
   }
@@ -518,7 +549,7 @@ int fwd_gemm(const void* X, const void* W, float* Y, int32_t P, int32_t in, int3
   if ((int64_t)P * out == 0) return FWD_OK;
   if (!X || !W || !Y) return fail(FWD_E_ARG, "NULL buffer");
   if (!device_is_gfx950()) return fail(FWD_E_UNAVAILABLE, "no gfx950 device is available");
-  HIP_TRY(fwdk::gemm_store(DType(dtype), X, W, Y, out, P, out, in, 0.f, (hipStream_t)hip_stream));
+  HIP_TRY(fwdk::gemm_store(DType(dtype), X, W, Y, out, P, out, in, 0.f, false, (hipStream_t)hip_stream));
   return FWD_OK;
 }
 
@@ -545,6 +576,7 @@ int fwd_attention(const void* q, const void* k, const void* v_t, void* o, int32_
   a.Hkv = n_kv_heads;
   a.D = head_dim;
   a.window = window;
+  a.o_tiled = false;
   HIP_TRY(fwdk::attention(DType(dtype), a, (hipStream_t)hip_stream));
   return FWD_OK;
 }
@@ -556,7 +588,8 @@ int fwd_rmsnorm(const float* x, const void* w, void* y, int32_t rows, int32_t hi
   if (rows == 0) return FWD_OK;
   if (!x || !w || !y) return fail(FWD_E_ARG, "NULL buffer");
   if (!device_is_gfx950()) return fail(FWD_E_UNAVAILABLE, "no gfx950 device is available");
-  HIP_TRY(fwdk::rmsnorm(DType(dtype), x, (const float*)w, y, nullptr, rows, hidden, eps, (hipStream_t)hip_stream));
+  HIP_TRY(fwdk::rmsnorm(DType(dtype), x, (const float*)w, y, nullptr, rows, hidden, eps, false,
+                        (hipStream_t)hip_stream));
   return FWD_OK;
 }
 

@@ -91,12 +91,13 @@ template <int C, typename T>
 struct EpiSwiGLU {
   T* a;
   int F;
+  bool tiled;  // a in the K-tiled layout (it is the next GEMM's X operand)
   __device__ __forceinline__ void pair(int row, int c, float g, float u, bool ok0, bool) const {
     if (!ok0) return;
     const int f = (c / (2 * C)) * C + (c % C);
     // silu(g) = g / (1 + e^{-g})
     const float s = g * fast_rcp(1.f + fast_exp2(-kLog2e * g));
-    Elem<T>::store(a + (int64_t)row * F + f, s * u);
+    Elem<T>::store(a + (tiled ? tiled_index(row, f, F) : (int64_t)row * F + f), s * u);
   }
   template <int R>
   __device__ __forceinline__ void batch(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
@@ -205,12 +206,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // buffer_load_dwordx4 ... lds (no VGPR staging): 64 lanes x 16 bytes. Lane l lands
 // at byte 16 l of block `blk`, i.e. tile row blk * (64 / CH) + l / CH and physical
 // chunk l % CH, so it fetches the logical chunk the swizzled layout keeps there.
-template <int BK>
+// Row-major operands: row r of the tile starts at r * K. K-tiled operands (BK = 32):
+// block `blk` of slice k0 is the 1 KiB tile (blk, k0 / 32) of the operand tile.
+template <int BK, bool TILED>
 __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, bf16_t* lds, int K, int k0, int blk, int lane) {
   constexpr int CH = BK / 8, RPB = 64 / CH;  // chunks per row, rows per 1 KiB block
+  static_assert(!TILED || BK == 32, "the K-tiled layout has 32-wide tiles");
   const int row = blk * RPB + lane / CH;
-  const int kk = k0 + swz<BK>(row, lane % CH) * 8;  // the swizzle is an involution
-  const uint32_t off = kk < K ? (uint32_t)(row * K + kk) * 2u : 0x80000000u;
+  const int ch = swz<BK>(row, lane % CH);  // the swizzle is an involution
+  uint32_t off;
+  if constexpr (TILED) {
+    off = (uint32_t)((blk * (K / 32) + k0 / 32) * 512 + (lane / CH) * 32 + ch * 8) * 2u;
+  } else {
+    const int kk = k0 + ch * 8;
+    off = kk < K ? (uint32_t)(row * K + kk) * 2u : 0x80000000u;
+  }
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + blk * 512), 16, off, 0, 0, 0);
 }
 
@@ -294,7 +304,7 @@ __device__ constexpr int need_frag(int n) {
   return n == 0 ? 0 : n == 1 ? TM : n <= TM ? n - 1 : n;
 }
 
-template <class C, class Epi>
+template <class C, class Epi, bool TILED>
 __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* __restrict__ X,
                                                                   const bf16_t* __restrict__ W, int M, int N, int K,
                                                                   Epi epi) {
@@ -310,8 +320,10 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
   int tm, tn;
   tile_coords(blockIdx.x, nTM, nTN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(X + (int64_t)m0 * K, (int64_t)min(BM, M - m0) * K * 2);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + (int64_t)n0 * K, (int64_t)min(BN, N - n0) * K * 2);
+  // (K-tiled operands are read in whole 16-row tiles: rows are padded to 16)
+  const int mr = TILED ? (M + 15) / 16 * 16 : M, nr = TILED ? (N + 15) / 16 * 16 : N;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(X + (int64_t)m0 * K, (int64_t)min(BM, mr - m0) * K * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + (int64_t)n0 * K, (int64_t)min(BN, nr - n0) * K * 2);
 
   floatx16_t acc[TM][TN];
 #pragma unroll
@@ -342,8 +354,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
   static_assert(WAIT_STEADY < 64, "vmcnt range");
   const int nk = (K + BK - 1) / BK;
   auto issue_load = [&](int p, bf16_t* buf, int k0) {  // load p of this wave's share of one slice
-    if (p < LA) load_block<BK>(ra, buf, K, k0, wave + p * NW, lane);
-    else load_block<BK>(rb, buf + BM * BK, K, k0, wave + (p - LA) * NW, lane);
+    if (p < LA) load_block<BK, TILED>(ra, buf, K, k0, wave + p * NW, lane);
+    else load_block<BK, TILED>(rb, buf + BM * BK, K, k0, wave + (p - LA) * NW, lane);
   };
 #pragma unroll
   for (int q = 0; q < ST - 1; ++q)
@@ -404,11 +416,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
   write_tile<TM, TN>(epi, acc, m0 + wm * WTM, n0 + wn * WTN, M, N, lane);
 }
 
-template <class C, class Epi>
+template <class C, class Epi, bool TILED = false>
 hipError_t launch_cfg(const void* X, const void* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   const int grid = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<C, Epi>), dim3(grid), dim3(C::NT), 0, s, (const bf16_t*)X, (const bf16_t*)W,
-                     M, N, K, epi);
+  hipLaunchKernelGGL((gemm_bf16_kernel<C, Epi, TILED>), dim3(grid), dim3(C::NT), 0, s, (const bf16_t*)X,
+                     (const bf16_t*)W, M, N, K, epi);
   return hipGetLastError();
 }
 
@@ -445,7 +457,7 @@ struct PPCfg {
   static_assert((STAGES - 2) * LOADS < 64, "vmcnt range");
 };
 
-template <class C, class Epi>
+template <class C, class Epi, bool TILED>
 __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
                                                         int M, int N, int K, Epi epi) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::STAGES, NW = C::NW;
@@ -461,12 +473,14 @@ __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict
   int tm, tn;
   tile_coords(blockIdx.x, nTM, nTN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(X + (int64_t)m0 * K, (int64_t)min(BM, M - m0) * K * 2);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + (int64_t)n0 * K, (int64_t)min(BN, N - n0) * K * 2);
+  // (K-tiled operands are read in whole 16-row tiles: rows are padded to 16)
+  const int mr = TILED ? (M + 15) / 16 * 16 : M, nr = TILED ? (N + 15) / 16 * 16 : N;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(X + (int64_t)m0 * K, (int64_t)min(BM, mr - m0) * K * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + (int64_t)n0 * K, (int64_t)min(BN, nr - n0) * K * 2);
   const int nk = (K + BK - 1) / BK;
   auto issue_load = [&](int p, bf16_t* buf, int k0) {
-    if (p < LA) load_block<BK>(ra, buf, K, k0, wave + p * NW, lane);
-    else load_block<BK>(rb, buf + BM * BK, K, k0, wave + (p - LA) * NW, lane);
+    if (p < LA) load_block<BK, TILED>(ra, buf, K, k0, wave + p * NW, lane);
+    else load_block<BK, TILED>(rb, buf + BM * BK, K, k0, wave + (p - LA) * NW, lane);
   };
   const int lr = lane & 31, lk = lane >> 5;
   const int arow = wm * WTM + lr, brow = BM + wn * WTN + lr;
@@ -596,11 +610,11 @@ __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict
 // 32 in flight
 using CfgBig = PPCfg<256, 256, 32, 4, 4, 2>;
 
-template <class C, class Epi>
+template <class C, class Epi, bool TILED = false>
 hipError_t launch_pp(const void* X, const void* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   const int grid = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL((gemm_pp_kernel<C, Epi>), dim3(grid), dim3(C::NT), 0, s, (const bf16_t*)X, (const bf16_t*)W,
-                     M, N, K, epi);
+  hipLaunchKernelGGL((gemm_pp_kernel<C, Epi, TILED>), dim3(grid), dim3(C::NT), 0, s, (const bf16_t*)X,
+                     (const bf16_t*)W, M, N, K, epi);
   return hipGetLastError();
 }
 
@@ -650,12 +664,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 // ------------------------------------------------------------------ dispatch
+// Both operands row-major, or both K-tiled (K a multiple of 32).
 template <class Epi>
-hipError_t launch_bf16(const void* X, const void* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
+hipError_t launch_bf16(const void* X, const void* W, int M, int N, int K, const Epi& epi, bool tiled, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (tiled && K % 32) return hipErrorInvalidValue;
   const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 256) return launch_pp<CfgBig>(X, W, M, N, K, epi, s);
-  return launch_cfg<CfgSmall>(X, W, M, N, K, epi, s);
+  if (tiled) {
+    if (big >= 256) return launch_pp<CfgBig, Epi, true>(X, W, M, N, K, epi, s);
+    return launch_cfg<CfgSmall, Epi, true>(X, W, M, N, K, epi, s);
+  }
+  if (big >= 256) return launch_pp<CfgBig, Epi, false>(X, W, M, N, K, epi, s);
+  return launch_cfg<CfgSmall, Epi, false>(X, W, M, N, K, epi, s);
 }
 
 template <class Epi>
@@ -670,26 +690,33 @@ hipError_t launch_f32(const void* X, const void* W, int M, int N, int K, const E
 }  // namespace
 
 hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K,
-                      float softcap, hipStream_t s) {
-  if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiStore<32>{Y, ldy, softcap}, s);
+                      float softcap, bool tiled, hipStream_t s) {
+  if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiStore<32>{Y, ldy, softcap}, tiled, s);
+  if (tiled) return hipErrorInvalidValue;
   return launch_f32(X, W, M, N, K, EpiStore<1>{Y, ldy, softcap}, s);
 }
 
 hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xin, float* xout, int M, int N,
-                         int K, hipStream_t s) {
-  if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiResidual<32>{xin, xout, N}, s);
+                         int K, bool tiled, hipStream_t s) {
+  if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiResidual<32>{xin, xout, N}, tiled, s);
+  if (tiled) return hipErrorInvalidValue;
   return launch_f32(X, W, M, N, K, EpiResidual<1>{xin, xout, N}, s);
 }
 
-hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, hipStream_t s) {
-  if (dt == DType::BF16) return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t>{(bf16_t*)a, F}, s);
-  return launch_f32(X, W, M, 2 * F, K, EpiSwiGLU<1, float>{(float*)a, F}, s);
+hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, bool tiled,
+                       hipStream_t s) {
+  if (dt == DType::BF16)
+    return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t>{(bf16_t*)a, F, tiled}, tiled, s);
+  if (tiled) return hipErrorInvalidValue;
+  return launch_f32(X, W, M, 2 * F, K, EpiSwiGLU<1, float>{(float*)a, F, false}, s);
 }
 
-hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, hipStream_t s) {
+hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, bool tiled,
+                         hipStream_t s) {
   const int N = (r.Hq + 2 * r.Hkv) * r.D;
   if (dt == DType::BF16)
-    return launch_bf16(X, W, M, N, K, EpiRope<32, bf16_t>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S}, s);
+    return launch_bf16(X, W, M, N, K, EpiRope<32, bf16_t>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S}, tiled, s);
+  if (tiled) return hipErrorInvalidValue;
   return launch_f32(X, W, M, N, K, EpiRope<1, float>{(float*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S}, s);
 }
 

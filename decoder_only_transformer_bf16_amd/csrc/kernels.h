@@ -14,15 +14,19 @@ enum class DType { F32 = 0, BF16 = 1 };
 // and the GEMM epilogues both follow it.
 inline int pair_chunk(DType dt) { return dt == DType::BF16 ? 32 : 1; }
 
-// ---- projections Y = X·Wᵀ (X [M, K], W [N, K], both row-major) ----
+// ---- projections Y = X·Wᵀ (X [M, K], W [N, K]) ----
+// `tiled`: X and W are both in the K-tiled layout of common.h (bf16 only, K a
+// multiple of 32, rows padded to 16 and readable); otherwise both are row-major.
 // Y fp32 [M, N] (ldy), optional softcap (0 = off).
 hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K,
-                      float softcap, hipStream_t s);
+                      float softcap, bool tiled, hipStream_t s);
 // xout[M, N] = xin + X·Wᵀ (fp32 residual stream, row stride N; xin may equal xout).
 hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xin, float* xout, int M, int N,
-                         int K, hipStream_t s);
-// a[M, F] = silu(g) * u with W packed as interleaved gate/up chunks (N = 2F).
-hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, hipStream_t s);
+                         int K, bool tiled, hipStream_t s);
+// a[M, F] = silu(g) * u with W packed as interleaved gate/up chunks (N = 2F); with
+// `tiled`, a is written K-tiled too (it is the down projection's X).
+hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, bool tiled,
+                       hipStream_t s);
 // QKV projection with RoPE on q and k; N = (Hq + 2 Hkv) D with packed q/k rows.
 // Writes qkv [M, (Hq + 2 Hkv) D]: rotated q heads, rotated k heads, then the value
 // heads, each in natural dim order. Rows are b * S + t (t = position).
@@ -31,7 +35,8 @@ struct RopeArgs {
   const float2* cs;  // [S_max, D / 2] (cos, sin)
   int Hq, Hkv, D, S;
 };
-hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, hipStream_t s);
+hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, bool tiled,
+                         hipStream_t s);
 
 // ---- attention ----
 struct AttnArgs {
@@ -42,6 +47,7 @@ struct AttnArgs {
   int64_t ldq, ldk, ldo;  // elements between consecutive tokens
   int ldvt;               // elements between consecutive dims of vt (>= S, multiple of 8)
   int B, S, Hq, Hkv, D, window;
+  bool o_tiled;           // o K-tiled (bf16) with row width ldo = Hq * D, rows padded to 16
 };
 hipError_t attention(DType dt, const AttnArgs& a, hipStream_t s);
 // vt[b, c, t] = src[(b * S + t) * ld + c] for c < C = Hkv * D (values transposed so that
@@ -51,14 +57,16 @@ hipError_t transpose_v(DType dt, const void* src, int64_t ld, void* vt, int ldvt
 bool attention_supported(DType dt, int D);
 
 // ---- row kernels ----
-// y = RMSNorm(x; w) (w fp32 gains); y of dtype dt; optional fp32 copy y32.
+// y = RMSNorm(x; w) (w fp32 gains); y of dtype dt (K-tiled with `tiled`: bf16, H a
+// multiple of 32); optional fp32 copy y32 (row-major).
 hipError_t rmsnorm(DType dt, const float* x, const float* w, void* y, float* y32, int rows, int H, float eps,
-                   hipStream_t s);
-// xout = xin + RMSNorm(u; wpost); y = RMSNorm(xout; wnext) (dtype dt), y32 optional fp32 copy of y.
+                   bool tiled, hipStream_t s);
+// xout = xin + RMSNorm(u; wpost); y = RMSNorm(xout; wnext) (dtype dt, K-tiled with
+// `tiled`), y32 optional row-major fp32 copy of y.
 hipError_t add_norm(DType dt, const float* xin, const float* u, const float* wpost, float* xout, const float* wnext,
-                    void* y, float* y32, int rows, int H, float eps, hipStream_t s);
-// x[t, :] = E[ids[t], :] * scale (fp32 out).
-hipError_t embed(DType dt, const int32_t* ids, const void* E, float* x, int rows, int H, float scale,
+                    void* y, float* y32, int rows, int H, float eps, bool tiled, hipStream_t s);
+// x[t, :] = E[ids[t], :] * scale (fp32 out); E K-tiled with `tiled`.
+hipError_t embed(DType dt, const int32_t* ids, const void* E, float* x, int rows, int H, float scale, bool tiled,
                  hipStream_t s);
 // out[r] = argmax_v z[r, v] (lowest index on ties); *flag = 1 if any z is not finite.
 hipError_t argmax_rows(const float* z, int64_t ldz, int rows, int V, int32_t* out, int* flag, hipStream_t s);
@@ -66,6 +74,9 @@ hipError_t argmax_rows(const float* z, int64_t ldz, int rows, int V, int32_t* ou
 // ---- packing ----
 // dst[map[r], :] = src[r, :] for r < rows; rows of `row_bytes` bytes (multiple of 4).
 hipError_t copy_rows(void* dst, const void* src, const int32_t* map, int rows, int64_t row_bytes, hipStream_t s);
+// K-tiled bf16 dst (rows padded to 16, cleared by the caller): row map[r] of dst =
+// row r of the row-major [rows, K] src; K a multiple of 32.
+hipError_t pack_tiled(void* dst, const void* src, const int32_t* map, int rows, int K, hipStream_t s);
 // dst[i] = float(src[i]) for a gain vector of dtype dt.
 hipError_t gains_to_f32(DType dt, const void* src, float* dst, int n, hipStream_t s);
 

@@ -39,7 +39,7 @@ constexpr int kMaxV = 16;
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ w,
                                                      T* __restrict__ y, float* __restrict__ y32, int rows, int H,
-                                                     float eps) {
+                                                     float eps, bool tiled) {
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float* xr = x + (int64_t)row * H;
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
       const int i = lane * 4 + j * 256;
       if (i >= H) continue;
       const float4 o = mul4(v[j], Vec4<float>::load(w + i), r);
-      Vec4<T>::store(y + (int64_t)row * H + i, o);
+      Vec4<T>::store(y + (tiled ? tiled_index(row, i, H) : (int64_t)row * H + i), o);
       if (y32) Vec4<float>::store(y32 + (int64_t)row * H + i, o);
     }
     return;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   const float r = fast_rsqrt(ss / (float)H + eps);
   for (int i = lane * 4; i < H; i += 256) {
     const float4 v = mul4(Vec4<float>::load(xr + i), Vec4<float>::load(w + i), r);
-    Vec4<T>::store(y + (int64_t)row * H + i, v);
+    Vec4<T>::store(y + (tiled ? tiled_index(row, i, H) : (int64_t)row * H + i), v);
     if (y32) Vec4<float>::store(y32 + (int64_t)row * H + i, v);
   }
 }
@@ -83,7 +83,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void add_norm_kernel(const float* __restrict__ xin, const float* __restrict__ u,
                                                       const float* __restrict__ wpost, float* __restrict__ xout,
                                                       const float* __restrict__ wnext, T* __restrict__ y,
-                                                      float* __restrict__ y32, int rows, int H, float eps) {
+                                                      float* __restrict__ y32, int rows, int H, float eps,
+                                                      bool tiled) {
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const int64_t off = (int64_t)row * H;
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) void add_norm_kernel(const float* __restrict__
       const int i = lane * 4 + j * 256;
       if (i >= H) continue;
       const float4 v = mul4(xv[j], Vec4<float>::load(wnext + i), rx);
-      Vec4<T>::store(y + off + i, v);
+      Vec4<T>::store(y + (tiled ? tiled_index(row, i, H) : off + i), v);
       if (y32) Vec4<float>::store(y32 + off + i, v);
     }
     return;
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(256) void add_norm_kernel(const float* __restrict__
   for (int i = lane * 4; i < H; i += 256) {
     // each lane re-reads only what it wrote itself
     const float4 v = mul4(Vec4<float>::load(xout + off + i), Vec4<float>::load(wnext + i), rx);
-    Vec4<T>::store(y + off + i, v);
+    Vec4<T>::store(y + (tiled ? tiled_index(row, i, H) : off + i), v);
     if (y32) Vec4<float>::store(y32 + off + i, v);
   }
 }
@@ -147,12 +148,12 @@ __global__ __launch_bounds__(256) void add_norm_kernel(const float* __restrict__
 // x[t] = E[ids[t]] * scale ("pegainfer issue #878", Proposed Plan: scaled embedding)
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids, const T* __restrict__ E,
-                                                   float* __restrict__ x, int rows, int H, float scale) {
+                                                   float* __restrict__ x, int rows, int H, float scale, bool tiled) {
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
-  const T* e = E + (int64_t)ids[row] * H;
+  const int64_t id = ids[row];
   for (int i = lane * 4; i < H; i += 256) {
-    const float4 v = Vec4<T>::load(e + i);
+    const float4 v = Vec4<T>::load(E + (tiled ? tiled_index(id, i, H) : id * H + i));
     Vec4<float>::store(x + (int64_t)row * H + i, float4{v.x * scale, v.y * scale, v.z * scale, v.w * scale});
   }
 }
@@ -236,6 +237,17 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(uint8_t* __restrict__ ds
   }
 }
 
+// dst (K-tiled, bf16) row map[r] = src row r (row-major, K elements); one 16-byte
+// piece (8 elements, inside one 32-wide tile) per thread.
+__global__ __launch_bounds__(256) void pack_tiled_kernel(bf16_t* __restrict__ dst, const bf16_t* __restrict__ src,
+                                                        const int32_t* __restrict__ map, int K) {
+  const int r = blockIdx.x;
+  const bf16_t* srow = src + (int64_t)r * K;
+  const int64_t d = map[r];
+  for (int c = threadIdx.x * 8; c < K; c += 256 * 8)
+    *reinterpret_cast<u32x4_t*>(dst + tiled_index(d, c, K)) = *reinterpret_cast<const u32x4_t*>(srow + c);
+}
+
 template <typename T>
 __global__ void gains_kernel(const T* __restrict__ src, float* __restrict__ dst, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -247,38 +259,41 @@ inline int row_blocks(int rows) { return (rows + kRowsPerBlock - 1) / kRowsPerBl
 }  // namespace
 
 hipError_t rmsnorm(DType dt, const float* x, const float* w, void* y, float* y32, int rows, int H, float eps,
-                   hipStream_t s) {
+                   bool tiled, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (tiled && (dt != DType::BF16 || H % 32)) return hipErrorInvalidValue;
   if (dt == DType::BF16)
     hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, x, w, (bf16_t*)y, y32,
-                       rows, H, eps);
+                       rows, H, eps, tiled);
   else
     hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(row_blocks(rows)), dim3(256), 0, s, x, w, (float*)y, y32, rows,
-                       H, eps);
+                       H, eps, false);
   return hipGetLastError();
 }
 
 hipError_t add_norm(DType dt, const float* xin, const float* u, const float* wpost, float* xout, const float* wnext,
-                    void* y, float* y32, int rows, int H, float eps, hipStream_t s) {
+                    void* y, float* y32, int rows, int H, float eps, bool tiled, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (tiled && (dt != DType::BF16 || H % 32)) return hipErrorInvalidValue;
   if (dt == DType::BF16)
     hipLaunchKernelGGL(add_norm_kernel<bf16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, xin, u, wpost, xout,
-                       wnext, (bf16_t*)y, y32, rows, H, eps);
+                       wnext, (bf16_t*)y, y32, rows, H, eps, tiled);
   else
     hipLaunchKernelGGL(add_norm_kernel<float>, dim3(row_blocks(rows)), dim3(256), 0, s, xin, u, wpost, xout, wnext,
-                       (float*)y, y32, rows, H, eps);
+                       (float*)y, y32, rows, H, eps, false);
   return hipGetLastError();
 }
 
-hipError_t embed(DType dt, const int32_t* ids, const void* E, float* x, int rows, int H, float scale,
+hipError_t embed(DType dt, const int32_t* ids, const void* E, float* x, int rows, int H, float scale, bool tiled,
                  hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (tiled && (dt != DType::BF16 || H % 32)) return hipErrorInvalidValue;
   if (dt == DType::BF16)
     hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, ids, (const bf16_t*)E, x,
-                       rows, H, scale);
+                       rows, H, scale, tiled);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(row_blocks(rows)), dim3(256), 0, s, ids, (const float*)E, x, rows,
-                       H, scale);
+                       H, scale, false);
   return hipGetLastError();
 }
 
@@ -292,6 +307,13 @@ hipError_t copy_rows(void* dst, const void* src, const int32_t* map, int rows, i
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(copy_rows_kernel, dim3(rows), dim3(256), 0, s, (uint8_t*)dst, (const uint8_t*)src, map,
                      row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t pack_tiled(void* dst, const void* src, const int32_t* map, int rows, int K, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (K % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_tiled_kernel, dim3(rows), dim3(256), 0, s, (bf16_t*)dst, (const bf16_t*)src, map, K);
   return hipGetLastError();
 }
 

@@ -72,7 +72,8 @@ extern "C" {
  *                       workspace that fwd_create allocates
  * Supported: bf16 needs head_dim in {64, 128, 256}; f32 needs head_dim <= 64;
  * hidden, Hq*D, Hkv*D and ffn multiples of 8 (bf16) or 4 (f32); bf16 additionally
- * needs Hq*D, Hkv*D and ffn multiples of 32.
+ * needs hidden, Hq*D, Hkv*D and ffn multiples of 32 (its GEMM operands are stored in
+ * 32-column tiles).
  */
 typedef struct fwd_config {
   int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
