@@ -217,7 +217,45 @@ struct fwd_model {
   }
 };
 
+// KV-cache session: per-layer K and V caches [Bmax, Hkv, Smax, D] and the chunk
+// partials of the decode attention; borrows its model.
+struct fwd_session {
+  fwd_model* m = nullptr;
+  int Bmax = 0, Smax = 0;
+  int B = 0, len = 0;  // sequences and their common length after the last call
+  std::vector<void*> allocs;
+  char* kc = nullptr;  // layer l at kc + l * layer_bytes
+  char* vc = nullptr;
+  int64_t layer_bytes = 0;
+  float* part = nullptr;
+  float2* rope = nullptr;  // [Smax, D / 2]
+  ~fwd_session() {
+    if (m && m->stream) (void)hipStreamSynchronize(m->stream);
+    else (void)hipDeviceSynchronize();
+    for (void* p : allocs) (void)hipFree(p);
+  }
+};
+
 namespace {
+
+// RoPE (cos, sin) table [rows, D/2]: angle(t, k) = t * theta^(-2k/D), computed in
+// double on the host ("N7 · model/forward-parity", intro: RoPE).
+int rope_table(fwd_model* m, float2** out, int64_t rows, std::vector<void*>& owner) {
+  const int64_t D = m->g.D;
+  std::vector<float2> cs((size_t)rows * (D / 2));
+  for (int64_t t = 0; t < rows; ++t)
+    for (int64_t k = 0; k < D / 2; ++k) {
+      const double ang = (double)t * std::pow(m->cfg.rope_theta, -2.0 * (double)k / (double)D);
+      cs[(size_t)t * (D / 2) + k] = float2{(float)std::cos(ang), (float)std::sin(ang)};
+    }
+  void* p = nullptr;
+  HIP_TRY(hipMalloc(&p, (size_t)round_up((int64_t)cs.size() * 8, 256)));
+  owner.push_back(p);
+  *out = (float2*)p;
+  HIP_TRY(hipMemcpyAsync(p, cs.data(), cs.size() * 8, hipMemcpyHostToDevice, m->stream));
+  HIP_TRY(hipStreamSynchronize(m->stream));  // the host table dies at scope end
+  return FWD_OK;
+}
 
 // Packed row order of a q or k projection: within each head, the rotate-half pair
 // (k, k + D/2) is placed C rows apart in the same 2C-row group, so the GEMM
@@ -384,18 +422,8 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     }
     HIP_TRY(hipStreamSynchronize(s));  // the row maps are freed at scope end
 
-    // ---- RoPE table: angle(t, k) = t * theta^(-2k/D), computed in double ----
-    {
-      std::vector<float2> cs((size_t)g.T * (g.D / 2));
-      for (int64_t t = 0; t < g.T; ++t)
-        for (int64_t k = 0; k < g.D / 2; ++k) {
-          const double ang = (double)t * std::pow(cfg->rope_theta, -2.0 * (double)k / (double)g.D);
-          cs[(size_t)t * (g.D / 2) + k] = float2{(float)std::cos(ang), (float)std::sin(ang)};
-        }
-      if (int rc = m->alloc((void**)&m->rope_cs, (int64_t)cs.size() * 8)) return rc;
-      HIP_TRY(hipMemcpyAsync(m->rope_cs, cs.data(), cs.size() * 8, hipMemcpyHostToDevice, s));
-      HIP_TRY(hipStreamSynchronize(s));  // host staging buffers die at scope end
-    }
+    // ---- RoPE table ----
+    if (int rc = rope_table(m, &m->rope_cs, g.T, m->allocs)) return rc;
 
     // ---- workspace ----
     const int64_t T = g.T;
@@ -424,19 +452,19 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
   return FWD_OK;
 }
 
-int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, const fwd_outputs* out) {
-  if (!m) return fail(FWD_E_ARG, "model is NULL");
-  if (B < 0 || S < 0) return fail(FWD_E_ARG, "B and S must be >= 0");
+}  // extern "C"
+
+namespace {
+
+// The forward pass over B sequences of S new tokens each, at positions pos0 .. pos0 +
+// S - 1. Without a session: the plain prefill (pos0 = 0). With one: every layer's
+// rotated keys and values are also stored in the cache; when `decode` is set (S = 1,
+// pos0 = the cached length) attention runs over the cache instead of the prefill
+// kernel. Shapes are checked by the callers.
+int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B, int32_t S, int pos0, bool decode,
+            const fwd_outputs* out) {
   const int64_t T = (int64_t)B * S;
-  if (T == 0) return FWD_OK;
-  if (!ids_host) return fail(FWD_E_ARG, "ids is NULL");
-  if (T > m->g.T) return fail(FWD_E_TOO_LARGE, "B*S = " + std::to_string(T) + " exceeds max_tokens " +
-                                                   std::to_string(m->g.T));
   const int V = (int)m->g.V;
-  for (int64_t i = 0; i < T; ++i)
-    if (ids_host[i] < 0 || ids_host[i] >= V)
-      return fail(FWD_E_TOKEN_RANGE, "token id " + std::to_string(ids_host[i]) + " at index " + std::to_string(i) +
-                                         " is outside [0, " + std::to_string(V) + ")");
   const fwd_outputs none{nullptr, nullptr, nullptr};
   const fwd_outputs& o = out ? *out : none;
 
@@ -472,9 +500,20 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
     const float* next_norm = last ? m->final_norm : m->layers[l + 1].attn_norm;
 
     // attention sublayer (its input norm is already in m->n)
-    fwdk::RopeArgs ra{m->qk, m->rope_cs, Hq, Hkv, D, S};
+    fwdk::RopeArgs ra{m->qk, sess ? sess->rope : m->rope_cs, Hq, Hkv, D, S, pos0};
     TIMED(m, FWD_KERNEL_QKV_ROPE, fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, tl, s));
     const int64_t ldqkv = (int64_t)(Hq + 2 * Hkv) * D;
+    const int window = m->kinds[l] == FWD_LAYER_LOCAL ? m->cfg.sliding_window : 0;
+    if (sess) {
+      void* kc = sess->kc + l * sess->layer_bytes;
+      void* vc = sess->vc + l * sess->layer_bytes;
+      TIMED(m, FWD_KERNEL_KV_STORE, fwdk::kv_store(dt, qk, ldqkv, Hq, Hkv, D, B, S, pos0, kc, vc, sess->Smax, s));
+      if (decode) {
+        TIMED(m, FWD_KERNEL_ATTENTION, fwdk::attention_decode(dt, qk, ldqkv, kc, vc, sess->Smax, pos0 + 1, B, Hq, Hkv,
+                                                              D, window, m->o, (int64_t)Hq * D, tl, sess->part, s));
+      }
+    }
+    if (!decode) {
     TIMED(m, FWD_KERNEL_V_TRANSPOSE,
           fwdk::transpose_v(dt, qk + (int64_t)(Hq + Hkv) * D * g.esize, ldqkv, m->vt, ldvt, B, S, Hkv * D, s));
     fwdk::AttnArgs aa{};
@@ -490,9 +529,10 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
     aa.Hq = Hq;
     aa.Hkv = Hkv;
     aa.D = D;
-    aa.window = m->kinds[l] == FWD_LAYER_LOCAL ? m->cfg.sliding_window : 0;
+    aa.window = window;
     aa.o_tiled = tl;
     TIMED(m, FWD_KERNEL_ATTENTION, fwdk::attention(dt, aa, s));
+    }
     if (!sandwich) {
       TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_residual(dt, m->o, w.wo, xin, xmid, M, H, Hq * D, tl, s));
       TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, tl, s));
@@ -540,6 +580,96 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
   if (flag) return fail(FWD_E_NONFINITE, "non-finite logits");
   return FWD_OK;
 }
+
+int check_ids(const int32_t* ids_host, int64_t T, int V) {
+  if (!ids_host) return fail(FWD_E_ARG, "ids is NULL");
+  for (int64_t i = 0; i < T; ++i)
+    if (ids_host[i] < 0 || ids_host[i] >= V)
+      return fail(FWD_E_TOKEN_RANGE, "token id " + std::to_string(ids_host[i]) + " at index " + std::to_string(i) +
+                                         " is outside [0, " + std::to_string(V) + ")");
+  return FWD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, const fwd_outputs* out) {
+  if (!m) return fail(FWD_E_ARG, "model is NULL");
+  if (B < 0 || S < 0) return fail(FWD_E_ARG, "B and S must be >= 0");
+  const int64_t T = (int64_t)B * S;
+  if (T == 0) return FWD_OK;
+  if (T > m->g.T) return fail(FWD_E_TOO_LARGE, "B*S = " + std::to_string(T) + " exceeds max_tokens " +
+                                                   std::to_string(m->g.T));
+  if (int rc = check_ids(ids_host, T, (int)m->g.V)) return rc;
+  return forward(m, nullptr, ids_host, B, S, 0, false, out);
+}
+
+int fwd_session_create(fwd_model* m, int32_t max_batch, int32_t max_seq, fwd_session** out) {
+  if (!out) return fail(FWD_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!m) return fail(FWD_E_ARG, "model is NULL");
+  if (max_batch <= 0 || max_seq <= 0) return fail(FWD_E_ARG, "max_batch and max_seq must be positive");
+  if (max_batch > m->g.T) return fail(FWD_E_TOO_LARGE, "max_batch exceeds the model's max_tokens");
+  const Geometry& g = m->g;
+  if (g.Hq / g.Hkv > 16) return fail(FWD_E_CONFIG, "decode supports at most 16 query heads per kv head");
+  fwd_session* se = new fwd_session();
+  se->m = m;
+  se->Bmax = max_batch;
+  se->Smax = max_seq;
+  auto run = [&]() -> int {
+    se->layer_bytes = round_up((int64_t)max_batch * g.Hkv * max_seq * g.D * g.esize, 256);
+    const int64_t cache = std::max<int64_t>(g.L, 1) * se->layer_bytes;
+    void* p = nullptr;
+    HIP_TRY(hipMalloc(&p, (size_t)cache));
+    se->allocs.push_back(p);
+    se->kc = (char*)p;
+    HIP_TRY(hipMalloc(&p, (size_t)cache));
+    se->allocs.push_back(p);
+    se->vc = (char*)p;
+    const int64_t nsplit = (max_seq + fwdk::kDecodeChunk - 1) / fwdk::kDecodeChunk;
+    HIP_TRY(hipMalloc(&p, (size_t)round_up((int64_t)max_batch * g.Hq * nsplit * (g.D + 2) * 4, 256)));
+    se->allocs.push_back(p);
+    se->part = (float*)p;
+    return rope_table(m, &se->rope, max_seq, se->allocs);
+  };
+  if (int rc = run()) {
+    delete se;
+    return rc;
+  }
+  *out = se;
+  return FWD_OK;
+}
+
+int fwd_session_prefill(fwd_session* se, const int32_t* ids_host, int32_t B, int32_t S, const fwd_outputs* out) {
+  if (!se) return fail(FWD_E_ARG, "session is NULL");
+  if (B <= 0 || S <= 0) return fail(FWD_E_ARG, "B and S must be positive");
+  if (B > se->Bmax || S > se->Smax)
+    return fail(FWD_E_TOO_LARGE, "B or S exceeds the session's max_batch / max_seq");
+  const int64_t T = (int64_t)B * S;
+  if (T > se->m->g.T) return fail(FWD_E_TOO_LARGE, "B*S exceeds the model's max_tokens");
+  if (int rc = check_ids(ids_host, T, (int)se->m->g.V)) return rc;
+  se->B = 0;
+  se->len = 0;
+  if (int rc = forward(se->m, se, ids_host, B, S, 0, false, out)) return rc;
+  se->B = B;
+  se->len = S;
+  return FWD_OK;
+}
+
+int fwd_session_decode(fwd_session* se, const int32_t* ids_host, const fwd_outputs* out) {
+  if (!se) return fail(FWD_E_ARG, "session is NULL");
+  if (se->len <= 0) return fail(FWD_E_ARG, "decode needs a prefilled session");
+  if (se->len >= se->Smax) return fail(FWD_E_TOO_LARGE, "the session is full (max_seq tokens)");
+  if (int rc = check_ids(ids_host, se->B, (int)se->m->g.V)) return rc;
+  if (int rc = forward(se->m, se, ids_host, se->B, 1, se->len, true, out)) return rc;
+  se->len += 1;
+  return FWD_OK;
+}
+
+int32_t fwd_session_length(const fwd_session* se) { return se ? se->len : -1; }
+
+void fwd_session_destroy(fwd_session* se) { delete se; }
 
 int fwd_gemm(const void* X, const void* W, float* Y, int32_t P, int32_t in, int32_t out, int32_t dtype,
              void* hip_stream) {

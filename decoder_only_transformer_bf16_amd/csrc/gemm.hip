@@ -110,7 +110,7 @@ template <int C, typename T>
 struct EpiRope {
   T* qkv;  // [M, (Hq + 2 Hkv) D]: rotated q, rotated k, plain v, natural dim order
   const float2* cs;
-  int Hq, Hkv, D, S;
+  int Hq, Hkv, D, S, pos0;  // row r is position pos0 + r % S
   template <int R>
   __device__ __forceinline__ void batch(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
                                         bool ok0, bool ok1) const {
@@ -127,7 +127,7 @@ struct EpiRope {
     float2 r[R];
 #pragma unroll
     for (int q = 0; q < R; ++q)  // all table loads first
-      r[q] = cs[(int64_t)((row[q] < 0 ? 0 : row[q]) % S) * (D / 2) + k];
+      r[q] = cs[(int64_t)((row[q] < 0 ? 0 : row[q]) % S + pos0) * (D / 2) + k];
 #pragma unroll
     for (int q = 0; q < R; ++q) {
       if (row[q] < 0) continue;
@@ -141,7 +141,7 @@ struct EpiRope {
     const int qsz = Hq * D, ksz = Hkv * D;
     T* out = qkv + (int64_t)row * (qsz + 2 * ksz);
     if (c < qsz + ksz) {
-      const int t = row % S;
+      const int t = row % S + pos0;
       const int sec = c < qsz ? 0 : qsz;
       const int cc = c - sec;
       const int head = cc / D, pd = cc - head * D;
@@ -715,9 +715,10 @@ hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs&
                          hipStream_t s) {
   const int N = (r.Hq + 2 * r.Hkv) * r.D;
   if (dt == DType::BF16)
-    return launch_bf16(X, W, M, N, K, EpiRope<32, bf16_t>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S}, tiled, s);
+    return launch_bf16(X, W, M, N, K, EpiRope<32, bf16_t>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0},
+                       tiled, s);
   if (tiled) return hipErrorInvalidValue;
-  return launch_f32(X, W, M, N, K, EpiRope<1, float>{(float*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S}, s);
+  return launch_f32(X, W, M, N, K, EpiRope<1, float>{(float*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0}, s);
 }
 
 }  // namespace fwdk

@@ -32,8 +32,9 @@ hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, i
 // heads, each in natural dim order. Rows are b * S + t (t = position).
 struct RopeArgs {
   void* qkv;
-  const float2* cs;  // [S_max, D / 2] (cos, sin)
+  const float2* cs;  // [positions, D / 2] (cos, sin)
   int Hq, Hkv, D, S;
+  int pos0;          // row r is at position pos0 + r % S (0 for a prefill)
 };
 hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, bool tiled,
                          hipStream_t s);
@@ -55,6 +56,22 @@ hipError_t attention(DType dt, const AttnArgs& a, hipStream_t s);
 hipError_t transpose_v(DType dt, const void* src, int64_t ld, void* vt, int ldvt, int B, int S, int C,
                        hipStream_t s);
 bool attention_supported(DType dt, int D);
+
+// ---- KV cache (decode) ----
+// Cache of one layer: K and V each [Bmax, Hkv, Smax, D] (dtype dt), positions contiguous.
+// Stores the rotated k and the v of token rows r = b * S + s (qkv as written by
+// gemm_qkv_rope, row stride ldqkv) at position pos0 + s of sequence b.
+hipError_t kv_store(DType dt, const void* qkv, int64_t ldqkv, int Hq, int Hkv, int D, int B, int S, int pos0,
+                    void* kc, void* vc, int Smax, hipStream_t s);
+// One query per sequence: o[b, h, :] = softmax over cached keys j < len (and
+// len - 1 - j < window when window > 0) of q·k_j / sqrt(D), times v_j. q rows b of
+// the qkv buffer (stride ldq); o bf16 K-tiled (o_tiled) or row-major with stride ldo.
+// Flash-decoding: key chunks of kDecodeChunk per workgroup, fp32 throughout, merged
+// by a second kernel. `part` holds B * Hq * ceil(len / kDecodeChunk) * (D + 2) floats.
+constexpr int kDecodeChunk = 256;
+hipError_t attention_decode(DType dt, const void* q, int64_t ldq, const void* kc, const void* vc, int Smax, int len,
+                            int B, int Hq, int Hkv, int D, int window, void* o, int64_t ldo, bool o_tiled,
+                            float* part, hipStream_t s);
 
 // ---- row kernels ----
 // y = RMSNorm(x; w) (w fp32 gains); y of dtype dt (K-tiled with `tiled`: bf16, H a

@@ -31,9 +31,11 @@ NORM = {"pre": 0, "sandwich": 1}
 LAYER = {"global": 0, "local": 1}
 
 EXPORTS = ("fwd_available", "fwd_create", "fwd_output_sizes", "fwd_prefill", "fwd_gemm", "fwd_attention",
-           "fwd_rmsnorm", "fwd_set_timing", "fwd_get_timing", "fwd_destroy", "fwd_last_error")
+           "fwd_rmsnorm", "fwd_set_timing", "fwd_get_timing", "fwd_destroy", "fwd_last_error",
+           "fwd_session_create", "fwd_session_prefill", "fwd_session_decode", "fwd_session_length",
+           "fwd_session_destroy")
 KERNEL_CLASSES = ("embed", "norm", "qkv_rope", "attention", "o_proj", "gate_up", "down_proj", "lm_head", "argmax",
-                  "v_transpose")
+                  "v_transpose", "kv_store")
 
 c_i32, c_i64, c_f32, c_f64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -100,6 +102,16 @@ def lib() -> ctypes.CDLL:
         L.fwd_destroy.argtypes = [c_vp]
         L.fwd_destroy.restype = None
         L.fwd_last_error.restype = ctypes.c_char_p
+        L.fwd_session_create.argtypes = [c_vp, c_i32, c_i32, ctypes.POINTER(c_vp)]
+        L.fwd_session_create.restype = c_i32
+        L.fwd_session_prefill.argtypes = [c_vp, c_vp, c_i32, c_i32, ctypes.POINTER(FwdOutputs)]
+        L.fwd_session_prefill.restype = c_i32
+        L.fwd_session_decode.argtypes = [c_vp, c_vp, ctypes.POINTER(FwdOutputs)]
+        L.fwd_session_decode.restype = c_i32
+        L.fwd_session_length.argtypes = [c_vp]
+        L.fwd_session_length.restype = c_i32
+        L.fwd_session_destroy.argtypes = [c_vp]
+        L.fwd_session_destroy.restype = None
         _lib = L
     return _lib
 
@@ -213,6 +225,59 @@ class Model:
             "argmax": torch.empty((B, S), dtype=torch.int32, device=dev) if argmax else None,
         }
         self.prefill_into(ids, res["logits"], res["hidden"], res["argmax"])
+        return res
+
+
+class Session:
+    """A KV-cache session on a Model (fwd_session_*): prefill, then one token per step."""
+
+    def __init__(self, model: Model, max_batch: int, max_seq: int):
+        self.model = model
+        h = c_vp()
+        _check(lib().fwd_session_create(model._h, max_batch, max_seq, ctypes.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) and self._h.value:
+            lib().fwd_session_destroy(self._h)
+            self._h = c_vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def length(self) -> int:
+        return int(lib().fwd_session_length(self._h))
+
+    def _outputs(self, B: int, S: int, logits: bool, hidden: bool, argmax: bool):
+        import torch
+        cfg = self.model.cfg
+        dev = torch.device("cuda", torch.cuda.current_device())
+        return {
+            "logits": torch.empty((B, S, cfg.vocab), dtype=torch.float32, device=dev) if logits else None,
+            "hidden": torch.empty((cfg.n_layers + 2, B, S, cfg.hidden), dtype=torch.float32, device=dev)
+            if hidden else None,
+            "argmax": torch.empty((B, S), dtype=torch.int32, device=dev) if argmax else None,
+        }
+
+    def prefill(self, ids: np.ndarray, logits: bool = True, hidden: bool = False, argmax: bool = True):
+        """fwd_session_prefill over ids [B, S]; outputs shaped as Model.prefill's."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        B, S = ids.shape
+        res = self._outputs(B, S, logits, hidden, argmax)
+        out = FwdOutputs(logits=_ptr(res["logits"]), hidden=_ptr(res["hidden"]), argmax=_ptr(res["argmax"]))
+        _check(lib().fwd_session_prefill(self._h, ids.ctypes.data, B, S, ctypes.byref(out)))
+        return res
+
+    def decode(self, ids: np.ndarray, logits: bool = True, hidden: bool = False, argmax: bool = True):
+        """fwd_session_decode of one token per sequence, ids [B]; outputs with S = 1."""
+        ids = np.ascontiguousarray(np.asarray(ids).reshape(-1), dtype=np.int32)
+        res = self._outputs(ids.size, 1, logits, hidden, argmax)
+        out = FwdOutputs(logits=_ptr(res["logits"]), hidden=_ptr(res["hidden"]), argmax=_ptr(res["argmax"]))
+        _check(lib().fwd_session_decode(self._h, ids.ctypes.data, ctypes.byref(out)))
         return res
 
 

@@ -227,7 +227,8 @@ int fwd_rmsnorm(const float* x, const void* w, void* y, int32_t rows, int32_t hi
 #define FWD_KERNEL_LM_HEAD 7       /* tied LM head (+ softcap)                     */
 #define FWD_KERNEL_ARGMAX 8        /* per-position argmax + non-finite check      */
 #define FWD_KERNEL_V_TRANSPOSE 9   /* values transposed to keys-contiguous order  */
-#define FWD_KERNEL_CLASSES 10
+#define FWD_KERNEL_KV_STORE 10     /* keys and values stored in a session's cache */
+#define FWD_KERNEL_CLASSES 11
 /* enable != 0 turns timing on and clears the accumulated totals; 0 turns it off. */
 int fwd_set_timing(fwd_model* m, int32_t enable);
 /* Accumulated milliseconds and launch count of one kernel class since the last
@@ -235,8 +236,54 @@ int fwd_set_timing(fwd_model* m, int32_t enable);
 int fwd_get_timing(const fwd_model* m, int32_t kernel_class, double* total_ms, int64_t* launches);
 
 /* Release a model and everything it allocated (waits for its stream first).
- * NULL is a no-op ("N9 · metalgemm", Theorem 1: Free / Reset reclaim the table). */
+ * NULL is a no-op ("N9 · metalgemm", Theorem 1: Free / Reset reclaim the table).
+ * Destroy the model's sessions first. */
 void fwd_destroy(fwd_model* m);
+
+/*
+ * ---- Cached sessions: prefill into a KV cache, then greedy decode ----
+ * ("N7 · model/forward-parity", Theorem 1: a cached session's prefill reproduces the
+ * cacheless forward's last-position logits, and the greedy continuation ids match
+ * token for token; "N9 · metalgemm", Theorem 1: argmax-exact and cosine-close at every
+ * prefill and greedy step.)
+ *
+ * A session borrows its model (destroy the session first) and owns, per layer, a
+ * key and a value cache of max_batch x n_kv_heads x max_seq x head_dim elements of
+ * the model's dtype, plus a RoPE table for max_seq positions. Work runs on the
+ * model's stream. Calls on one model (through any of its sessions or fwd_prefill)
+ * must not overlap; the model's workspace is shared.
+ * Errors: FWD_E_ARG, FWD_E_TOO_LARGE (max_batch above the model's max_tokens),
+ * FWD_E_CONFIG (more than 16 query heads per kv head), FWD_E_HIP.
+ */
+typedef struct fwd_session fwd_session;
+int fwd_session_create(fwd_model* m, int32_t max_batch, int32_t max_seq, fwd_session** out);
+
+/*
+ * Start the session over B prompts of S tokens each (host int32 [B, S], positions
+ * 0..S-1): the same forward pass and outputs as fwd_prefill, and every layer's
+ * rotated keys and values are stored in the cache. Replaces whatever the session
+ * held; afterwards it holds B sequences of length S.
+ * Errors: as fwd_prefill; FWD_E_TOO_LARGE if B > max_batch, S > max_seq or
+ * B*S > max_tokens. On an error the session is left empty.
+ */
+int fwd_session_prefill(fwd_session* s, const int32_t* ids_host, int32_t B, int32_t S, const fwd_outputs* out);
+
+/*
+ * Extend every sequence by one token: ids_host is host int32 [B] (B of the last
+ * prefill), placed at position len (the current length). Its keys and values are
+ * appended to the cache and attention runs over positions 0..len (or the last
+ * `sliding_window` of them on local layers). Outputs as for a prefill with S = 1:
+ * logits [B, V] fp32, hidden [n_layers + 2, B, H] fp32, argmax [B]; any may be NULL.
+ * Errors: FWD_E_ARG (no prefill yet), FWD_E_TOO_LARGE (len == max_seq),
+ * FWD_E_TOKEN_RANGE, FWD_E_NONFINITE, FWD_E_HIP.
+ */
+int fwd_session_decode(fwd_session* s, const int32_t* ids_host, const fwd_outputs* out);
+
+/* Current length of the session's sequences (0 before a prefill; -1 for NULL). */
+int32_t fwd_session_length(const fwd_session* s);
+
+/* Release a session's caches (waits for the model's stream). NULL is a no-op. */
+void fwd_session_destroy(fwd_session* s);
 
 /* Message of the last failure on the calling thread ("" if none). The pointer
  * stays valid until the next call into the library on that thread. */

@@ -24,6 +24,7 @@ from .forward import (  # noqa: F401
     embed_scale,
     forward,
     gemm,
+    greedy,
     rmsnorm,
     rope,
     silu,

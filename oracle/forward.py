@@ -295,3 +295,25 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
         return {"argmax": None, "hidden": hidden, "logits": None}
     z = softcap(gemm(rb(h), E), cfg.final_logit_softcap)                # tied head
     return {"argmax": argmax(z), "hidden": hidden, "logits": z}
+
+
+# ---------------------------------------------------------------- greedy continuation
+def greedy(cfg, weights, ids, n_tokens: int):
+    """Greedy continuation by repeated cacheless forwards ([fp] Theorem 1: the greedy
+    continuation ids; the cached session must reproduce the cacheless forward).
+
+    Token i (i = 0 .. n_tokens-1) of every row is the argmax of the last position's
+    logits of a forward over the prompt followed by tokens 0 .. i-1. Nothing is cached.
+    Returns (tokens int32 [B, n_tokens], logits f32 [n_tokens, B, V]); logits[i] are
+    the last-position logits that chose token i.
+    """
+    seq = np.asarray(ids, dtype=np.int32)
+    B = seq.shape[0]
+    toks = np.empty((B, n_tokens), dtype=np.int32)
+    logits = np.empty((n_tokens, B, cfg.vocab), dtype=np.float32)
+    for i in range(n_tokens):
+        z = forward(cfg, weights, seq, want_logits=True, want_hidden=False)["logits"][:, -1]
+        logits[i] = z
+        toks[:, i] = argmax(z)
+        seq = np.concatenate([seq, toks[:, i:i + 1]], axis=1)
+    return toks, logits

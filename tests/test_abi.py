@@ -17,7 +17,7 @@ HEADER = open(os.path.join(ROOT, "include", "fwd.h")).read()
 
 
 def _declared():
-    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(fwd_\w+)\s*\(", HEADER, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|void|const char\*)\s+(fwd_\w+)\s*\(", HEADER, re.M)))
 
 
 def test_header_declares_the_binding_exports():
@@ -90,3 +90,17 @@ def test_null_handle_and_empty_calls():
     # empty problems are no-ops even without a device
     assert L.fwd_gemm(None, None, None, 0, 8, 4, fwd.DTYPE["bf16"], None) == fwd.FWD_OK
     assert L.fwd_gemm(None, None, None, 4, 7, 4, fwd.DTYPE["bf16"], None) == fwd.FWD_E_ARG
+
+
+def test_session_entry_points_reject_null_handles():
+    L = fwd.lib()
+    h = ctypes.c_void_p()
+    assert L.fwd_session_create(None, 1, 16, ctypes.byref(h)) == fwd.FWD_E_ARG
+    assert not h.value
+    assert L.fwd_session_create(None, 1, 16, None) == fwd.FWD_E_ARG
+    ids = np.zeros(4, dtype=np.int32)
+    out = fwd.FwdOutputs()
+    assert L.fwd_session_prefill(None, ids.ctypes.data, 1, 4, ctypes.byref(out)) == fwd.FWD_E_ARG
+    assert L.fwd_session_decode(None, ids.ctypes.data, ctypes.byref(out)) == fwd.FWD_E_ARG
+    assert L.fwd_session_length(None) == -1
+    L.fwd_session_destroy(None)

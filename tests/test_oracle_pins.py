@@ -395,3 +395,22 @@ def test_forward_softcap_and_embed_scale_compose():
     assert np.allclose(a["logits"], 2.0 * np.tanh(b["logits"].astype(np.float64) / 2.0), rtol=1e-6, atol=1e-7)
     assert np.all(np.abs(a["logits"]) < 2.0)
     assert np.array_equal(a["argmax"], b["argmax"])
+
+
+def test_greedy_steps_are_cacheless_forwards():
+    """Greedy continuation: token i is the argmax of the last position of a forward over
+    the prompt plus tokens 0..i-1; pinned against the forward itself, a restart from the
+    extended prompt (catches an off-by-one in the append loop) and per-row independence."""
+    w = _weights(TINY)
+    ids = np.asarray(wl.draw_ids(TINY.replace(batch=2, seq=5)))
+    toks, logits = oracle.greedy(TINY, w, ids, 4)
+    first = oracle.forward(TINY, w, ids, want_hidden=False)["logits"][:, -1]
+    assert np.array_equal(logits[0], first)
+    assert np.array_equal(toks[:, 0], np.argmax(first, axis=-1))
+    again, again_logits = oracle.greedy(TINY, w, np.concatenate([ids, toks[:, :1]], axis=1), 3)
+    assert np.array_equal(again, toks[:, 1:])
+    assert np.array_equal(again_logits, logits[1:])
+    for b in range(2):
+        one, one_logits = oracle.greedy(TINY, w, ids[b:b + 1], 4)
+        assert np.array_equal(one[0], toks[b])
+        assert np.allclose(one_logits[:, 0], logits[:, b], rtol=0, atol=1e-6)
