@@ -82,6 +82,36 @@ def cpu_baseline(cfg, S):
     }
 
 
+def decode_leg(fwd, model, cfg, ids, steps, stream):
+    """Greedy decode on a cached session: prefill the batch's prompts, then `steps`
+    one-token steps for every row, each fed the previous step's argmax (host ids, as
+    the API takes them). Every step reads all weights and the whole cache: HBM-bound."""
+    import torch
+    B, S = ids.shape
+    with torch.cuda.stream(stream):
+        sess = fwd.Session(model, max_batch=B, max_seq=S + steps + 2)
+        first = sess.prefill(ids, logits=False, argmax=True)
+        tok = first["argmax"][:, -1].cpu().numpy()
+        tok = sess.decode(tok, logits=False, argmax=True)["argmax"][:, 0].cpu().numpy()   # warm-up step
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            tok = sess.decode(tok, logits=True, argmax=True)["argmax"][:, 0].cpu().numpy()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t
+        sess.close()
+    sizes = fwd.output_sizes(cfg, B, S)
+    ctx = S + 1 + steps / 2.0                      # mean cached length over the timed steps
+    kv = 2 * cfg.n_layers * B * cfg.n_kv_heads * ctx * cfg.head_dim * 2
+    per_step = sizes["weight_bytes"] + kv
+    ms = elapsed * 1000.0 / steps
+    log(f"decode: {steps} steps of {B} tokens at context {S}: {ms:.2f} ms/step")
+    return {"tokens_per_s": B * steps / elapsed, "ms_per_step": ms, "batch": B, "context": S, "steps": steps,
+            "bound": "hbm", "bytes_per_step": per_step, "achieved_gbs": per_step / (ms * 1e-3) / 1e9,
+            "peak_gbs": PEAK_HBM_GBS, "frac": per_step / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "note": "bytes = all packed weights + the cached keys and values read once per step"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,6 +120,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hidden", action="store_true", help="skip the hidden-slot output")
     ap.add_argument("--timing-steps", type=int, default=2, help="extra steps timed per kernel with HIP events")
+    ap.add_argument("--decode-steps", type=int, default=16,
+                    help="greedy decode steps timed on a cached session after the prefill (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -198,8 +230,12 @@ def main():
                        "frac_of_bf16_peak": total_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "kernels": kernels,
     }
+    if args.decode_steps > 0:
+        del logits, hidden
+        torch.cuda.empty_cache()
+        result["decode"] = decode_leg(fwd, model, cfg, ids, args.decode_steps, stream)
     model.close()
-    del logits, hidden, argmax
+    del argmax
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the oracle on a bounded sample")

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from synth import workloads as wl
-from tests.gpu_util import argmax_check, cosine, slot_parity, to_device
+from tests.gpu_util import COS_HALF_PRECISION, FLOOR_SLACK, argmax_check, cosine, slot_parity, to_device
 
 pytestmark = pytest.mark.gpu
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_values.json")))
@@ -104,6 +104,45 @@ def test_llama3_8b_full_batch_sampled(fwd):
     # a row alone reproduces the same row of the batch, bit for bit
     again = model.prefill(ids[7:8], logits=True, hidden=False, argmax=True)
     assert torch.equal(again["logits"][0], out["logits"][7])
+    # cached session at full size: prefill the first 2046 tokens of every row, then
+    # decode tokens 2046 and 2047 (teacher-forced) over the 8-chunk cache; each step
+    # must give the cacheless prefill's logits at that position
+    # Both are bf16 computations that round at different points (the cached step keeps
+    # the probabilities in fp32), so between them the half-precision gate applies. Row
+    # 0 at position 2046 is also checked against the oracle (a 2047-token, 32-layer
+    # forward on the host). That deep, the oracle itself rounded to bf16 at the GPU's
+    # rounding points sits near the 0.999 gate, so there the gate is the floor-relative
+    # one of the hidden slots without the 0.999 minimum.
+    ref_z = out["logits"][:, 2046:].cpu().numpy()
+    del out, again
+    torch.cuda.empty_cache()
+    _say("session: prefill 8 x 2046, decode positions 2046 and 2047")
+    sess = fwd.Session(model, max_batch=8, max_seq=2048)
+    sess.prefill(ids[:, :2046], logits=False, argmax=False)
+    cached = []
+    for i, pos in enumerate((2046, 2047)):
+        step = sess.decode(ids[:, pos], logits=True, argmax=True)
+        z = step["logits"][:, 0].cpu().numpy()
+        cached.append(z)
+        worst = min(cosine(z[b], ref_z[b, i]) for b in range(8))
+        assert worst >= COS_HALF_PRECISION, f"position {pos}: cosine {worst}"
+        pinned, near, fails = argmax_check(step["argmax"][:, 0].cpu().numpy(), ref_z[:, i], z)
+        assert not fails, fails[:5]
+        _say(f"  position {pos}: lowest row cosine cached vs cacheless {worst:.6f}, "
+             f"max|d| {np.abs(z - ref_z[:, i]).max():.3e}, argmax pinned {pinned} near-tie {near}")
+    sess.close()
+    _say("  oracle: row 0, positions 0..2046 (host forward, about a minute)")
+    zo = oracle.forward(cfg, host, ids[:1, :2047], want_hidden=False)["logits"][:, -1]
+    c_cached, c_plain = cosine(cached[0][:1], zo), cosine(ref_z[:1, 0], zo)
+    _say(f"  position 2046 vs oracle: cached {c_cached:.6f}, cacheless {c_plain:.6f}")
+    _say("  oracle rounded at the bf16 points, same row and positions (about two minutes)")
+    zb = oracle.forward(cfg, host, ids[:1, :2047], want_hidden=False, bf16_points=True)["logits"][:, -1]
+    floor = cosine(zb, zo)
+    _say(f"  bf16-rounded oracle vs oracle at position 2046: {floor:.6f}")
+    for c in (c_cached, c_plain):
+        assert (1.0 - c) <= FLOOR_SLACK * (1.0 - floor) + 2e-6, (c, floor)
+    pinned, near, fails = argmax_check(np.argmax(cached[0][:1], -1), zo, cached[0][:1])
+    assert not fails, fails
     model.close()
 
 
