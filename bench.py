@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=16,
                     help="greedy decode steps timed on a cached session after the prefill (0: skip)")
     args = ap.parse_args()
+    if args.timing_steps < 1:
+        ap.error("--timing-steps must be at least 1 (the roofline comes from those steps)")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the batch rows are independent: more GPUs would each run their own share)", file=sys.stderr)

@@ -50,6 +50,14 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 dword3: 32-bit data
+// format, the value untyped loads require). Loads whose offset lies past `bytes`
+// return zero, which pads the ragged edges of a tile without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
 // exp2 on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // 1/x and 1/sqrt(x) on the hardware units (v_rcp_f32, v_rsq_f32).

@@ -6,13 +6,22 @@
 // gives at its last position ("N7 · model/forward-parity", Theorem 1: the cached
 // session prefill agrees with the cacheless forward; greedy continuation). The cache
 // holds each layer's rotated keys and values, [B, Hkv, Smax, D] with positions
-// contiguous, written by kv_store from the QKV projection's output.
+// contiguous, written by the QKV projection's epilogue.
 //
 // attention_decode is flash-decoding: the visible keys of a sequence are cut into
 // chunks of kDecodeChunk, one workgroup per (chunk, kv head, sequence) computes the
 // scores of all Hq / Hkv query heads that share the kv head, their chunk-local
-// softmax statistics and the chunk's share of P·V, all in fp32; a second kernel merges
-// the chunks. The work is HBM-bound (each cached key and value is read once per step).
+// softmax statistics and the chunk's share of P·V, all in fp32, and the chunks are
+// merged by rescaling to a common maximum. The work is HBM-bound: each cached key
+// and value is read once per step.
+//
+// bf16 (at most 8 query heads per kv head): a wavefront reads its 64 keys and values
+// as 1 KiB pieces, D / 8 lanes per key row (16 bytes each), so every load is
+// contiguous; a lane's partial dot products are summed across its key's lanes with
+// DPP moves, and its share of P·V stays in registers until one LDS reduction. The
+// last workgroup of a (sequence, kv head) to finish merges the chunks itself. The
+// fp32 configuration (and wider groups) use a plain one-thread-per-key kernel and a
+// separate merge kernel.
 #include <algorithm>
 
 #include "common.h"
@@ -43,24 +52,6 @@ template <> struct Vec16<float> {
     v[3] = f.w;
   }
 };
-
-// k and v of token row r = b * S + s go to position pos0 + s of sequence b.
-template <typename T>
-__global__ __launch_bounds__(256) void kv_store_kernel(const T* __restrict__ qkv, int64_t ldqkv, int Hq, int Hkv,
-                                                      int D, int S, int pos0, T* __restrict__ kc, T* __restrict__ vc,
-                                                      int Smax) {
-  constexpr int E = 16 / sizeof(T);  // elements per 16-byte piece
-  const int r = blockIdx.x, b = r / S, s = r % S;
-  const int width = Hkv * D;
-  const T* krow = qkv + (int64_t)r * ldqkv + (int64_t)Hq * D;
-  const T* vrow = krow + width;
-  for (int c = threadIdx.x * E; c < width; c += 256 * E) {
-    const int g = c / D, d = c - g * D;
-    const int64_t at = (((int64_t)b * Hkv + g) * Smax + pos0 + s) * D + d;
-    *reinterpret_cast<u32x4_t*>(kc + at) = *reinterpret_cast<const u32x4_t*>(krow + c);
-    *reinterpret_cast<u32x4_t*>(vc + at) = *reinterpret_cast<const u32x4_t*>(vrow + c);
-  }
-}
 
 constexpr int kMaxGroup = 16;  // query heads per kv head
 
@@ -171,20 +162,236 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(const float* __r
   }
 }
 
-}  // namespace
 
-hipError_t kv_store(DType dt, const void* qkv, int64_t ldqkv, int Hq, int Hkv, int D, int B, int S, int pos0,
-                    void* kc, void* vc, int Smax, hipStream_t s) {
-  if (B <= 0 || S <= 0) return hipSuccess;
-  if (pos0 < 0 || pos0 + S > Smax || D % (dt == DType::BF16 ? 8 : 4)) return hipErrorInvalidValue;
-  if (dt == DType::BF16)
-    hipLaunchKernelGGL(kv_store_kernel<bf16_t>, dim3(B * S), dim3(256), 0, s, (const bf16_t*)qkv, ldqkv, Hq, Hkv, D,
-                       S, pos0, (bf16_t*)kc, (bf16_t*)vc, Smax);
-  else
-    hipLaunchKernelGGL(kv_store_kernel<float>, dim3(B * S), dim3(256), 0, s, (const float*)qkv, ldqkv, Hq, Hkv, D, S,
-                       pos0, (float*)kc, (float*)vc, Smax);
-  return hipGetLastError();
+// ------------------------------------------------------------------ bf16 kernel
+// Every lane of an aligned group of N lanes (N = 8, 16 or 32) gets the group's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16 || N == 32, "group of 8, 16 or 32 lanes");
+  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]: quad sums
+  v += dpp_mov<0x141>(v);  // row_half_mirror: lane i <- 7 - i within 8 lanes
+  if constexpr (N >= 16) v += dpp_mov<0x140>(v);  // row_mirror: lane i <- 15 - i
+  if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+  return v;
+}
+
+__device__ __forceinline__ void unpack8(const u32x4_t& u, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(u[i] << 16);
+    f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct DecodeArgs {
+  const bf16_t* q;
+  int64_t ldq;
+  const bf16_t *kc, *vc;
+  int Smax, len, Hq, Hkv, window, nsplit;
+  float scale_log2;
+  float* part;       // [B, Hq, nsplit, D + 2]: chunk outputs (unnormalised), max, sum
+  unsigned* count;   // [B, Hkv] arrival counters, zero between launches
+  bf16_t* o;
+  int64_t ldo;
+  bool o_tiled;
+};
+
+// Workgroup (chunk c, kv head g, sequence b), 4 wavefronts x 64 keys. Lane l of a
+// wavefront holds dims 8 (l % LPK) .. + 7 of key l / LPK of each 1 KiB piece.
+template <int D, int GM>
+__global__ __launch_bounds__(256) void attn_decode_bf16_kernel(DecodeArgs a) {
+  constexpr int CH = kDecodeChunk, LPK = D / 8, KPL = 64 / LPK, NL = 64 / KPL;
+  constexpr int NB = NL < 16 ? NL : 16;  // pieces per tensor in flight per lane
+  constexpr int RS = GM * D + 4;         // row stride of the partial outputs (floats)
+  static_assert(CH == 256 && D % 64 == 0 && D <= 256, "4 x 64 keys per chunk, D in {64, 128, 256}");
+  __shared__ float ps[CH][GM + 1];
+  __shared__ __align__(16) float ored[4 * KPL * RS];
+  __shared__ float stat[2][GM];
+  __shared__ int last;
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int sub = lane % LPK, kk = lane / LPK;
+  const int G = a.Hq / a.Hkv;
+  const int lo = a.window > 0 ? max(0, a.len - a.window) : 0;
+  const int j0 = lo + c * CH, j1 = min(a.len, j0 + CH);
+  const int64_t head = ((int64_t)b * a.Hkv + g) * a.Smax;
+  // keys at or past j1 (including cache rows not written yet) read as zeros
+  const auto krs = make_rsrc(a.kc + head * D, (int64_t)j1 * D * 2);
+  const auto vrs = make_rsrc(a.vc + head * D, (int64_t)j1 * D * 2);
+  auto piece = [&](int i) {  // byte offset of this lane's 16 bytes of piece i
+    return (uint32_t)(j0 + wave * 64 + i * KPL + kk) * (D * 2) + sub * 16;
+  };
+
+  // loads complete in issue order: the query first, then the keys, then the values,
+  // which arrive while the scores are computed
+  u32x4_t qv[GM];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {  // (heads past G load head 0 again, unused: no branch)
+    const int hh = h < G ? h : 0;
+    qv[h] = *reinterpret_cast<const u32x4_t*>(a.q + (int64_t)b * a.ldq + (int64_t)(g * G + hh) * D + sub * 8);
+  }
+  u32x4_t kv[NB], vv[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) kv[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, piece(i), 0, 0);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) vv[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, piece(i), 0, 0);
+  float qr[GM][8];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) unpack8(qv[h], qr[h]);
+
+  // scores (log2 units), -inf past the last key
+#pragma unroll
+  for (int i0 = 0; i0 < NL; i0 += NB) {
+    if (i0 > 0) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) kv[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, piece(i0 + i), 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      float k8[8];
+      unpack8(kv[i], k8);
+      const int jl = wave * 64 + (i0 + i) * KPL + kk;
+      const bool ok = j0 + jl < j1;
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h < G) {
+          float sdot = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sdot = fmaf(qr[h][e], k8[e], sdot);
+          sdot = group_sum<LPK>(sdot);
+          if (sub == 0) ps[jl][h] = ok ? sdot * a.scale_log2 : -INFINITY;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // chunk maximum and sum per head, one wavefront per head
+  for (int h = wave; h < G; h += 4) {
+    float m = -INFINITY;
+    for (int i = lane; i < CH; i += 64) m = fmaxf(m, ps[i][h]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int i = lane; i < CH; i += 64) {
+      const float p = ps[i][h] == -INFINITY ? 0.f : fast_exp2(ps[i][h] - m);
+      ps[i][h] = p;
+      l += p;
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      stat[0][h] = m;
+      stat[1][h] = l;
+    }
+  }
+  __syncthreads();
+
+  // P·V in registers
+  float acc[GM][8];
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int i0 = 0; i0 < NL; i0 += NB) {
+    if (i0 > 0) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) vv[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, piece(i0 + i), 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      float v8[8];
+      unpack8(vv[i], v8);
+      const int jl = wave * 64 + (i0 + i) * KPL + kk;
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h < G) {
+          const float p = ps[jl][h];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, v8[e], acc[h][e]);
+        }
+      }
+    }
+  }
+  float* orow = ored + (wave * KPL + kk) * RS + sub * 8;
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h < G) {
+      *reinterpret_cast<float4*>(orow + h * D) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *reinterpret_cast<float4*>(orow + h * D + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+  }
+  __syncthreads();
+
+  auto put_o = [&](int h, int d, float v) {
+    const int col = (g * G + h) * D + d;
+    Elem<bf16_t>::store(a.o + (a.o_tiled ? tiled_index(b, col, (int)a.ldo) : (int64_t)b * a.ldo + col), v);
+  };
+  const int items = G * D;
+  float* pbase = a.part + ((int64_t)b * a.Hq + g * G) * a.nsplit * (D + 2);  // head g * G + h at h * nsplit * (D + 2)
+  for (int it = tid; it < items; it += 256) {
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4 * KPL; ++r) sum += ored[r * RS + it];
+    const int h = it / D, d = it - h * D;
+    if (a.nsplit == 1) put_o(h, d, sum / stat[1][h]);
+    else store_agent(pbase + ((int64_t)h * a.nsplit + c) * (D + 2) + d, sum);
+  }
+  if (a.nsplit == 1) return;
+  if (tid < G) {
+    store_agent(pbase + ((int64_t)tid * a.nsplit + c) * (D + 2) + D, stat[0][tid]);
+    store_agent(pbase + ((int64_t)tid * a.nsplit + c) * (D + 2) + D + 1, stat[1][tid]);
+  }
+  // the last chunk of this (sequence, kv head) to finish merges all of them
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  unsigned* cnt = a.count + (int64_t)b * a.Hkv + g;
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(a.nsplit - 1);
+  __syncthreads();
+  if (!last) return;
+  // one pass over the chunks in order per (head, dim), rescaling to the running maximum
+  const int ns = a.nsplit;
+  for (int it = tid; it < items; it += 256) {
+    const int h = it / D, d = it - h * D;
+    const float* ph = pbase + (int64_t)h * ns * (D + 2);
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    constexpr int TB = 8;  // chunks loaded per round trip
+    for (int t0 = 0; t0 < ns; t0 += TB) {
+      float ov[TB], mv[TB], lv[TB];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const int t = t0 + u < ns ? t0 + u : t0;  // (surplus loads repeat t0, unused)
+        ov[u] = load_agent(ph + (int64_t)t * (D + 2) + d);
+        mv[u] = load_agent(ph + (int64_t)t * (D + 2) + D);
+        lv[u] = load_agent(ph + (int64_t)t * (D + 2) + D + 1);
+      }
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        if (t0 + u >= ns) break;
+        const float Mn = fmaxf(M, mv[u]);
+        const float r = fast_exp2(M - Mn), e = fast_exp2(mv[u] - Mn);  // (first chunk: r = 0)
+        O = O * r + ov[u] * e;
+        L = L * r + lv[u] * e;
+        M = Mn;
+      }
+    }
+    put_o(h, d, O / L);
+  }
+  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+}  // namespace
 
 namespace {
 template <typename T, int D>
@@ -199,14 +406,32 @@ hipError_t decode_impl(const void* q, int64_t ldq, const void* kc, const void* v
                      (T*)o, ldo, o_tiled);
   return hipGetLastError();
 }
+
+template <int D, int GM>
+hipError_t decode_bf16(const DecodeArgs& a, int B, hipStream_t s) {
+  hipLaunchKernelGGL((attn_decode_bf16_kernel<D, GM>), dim3(a.nsplit, a.Hkv, B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 }  // namespace
 
 hipError_t attention_decode(DType dt, const void* q, int64_t ldq, const void* kc, const void* vc, int Smax, int len,
                             int B, int Hq, int Hkv, int D, int window, void* o, int64_t ldo, bool o_tiled,
-                            float* part, hipStream_t s) {
+                            float* part, unsigned* count, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (len <= 0 || len > Smax || Hq % Hkv || Hq / Hkv > kMaxGroup) return hipErrorInvalidValue;
   if (o_tiled && (dt != DType::BF16 || ldo != (int64_t)Hq * D || ldo % 32)) return hipErrorInvalidValue;
+  const int G = Hq / Hkv;
+  if (dt == DType::BF16 && G <= 8 && count && (D == 64 || D == 128 || D == 256) && ldq % 8 == 0) {
+    DecodeArgs a{(const bf16_t*)q, ldq, (const bf16_t*)kc, (const bf16_t*)vc, Smax, len, Hq, Hkv, window, 0,
+                 kLog2e / sqrtf((float)D), part, count, (bf16_t*)o, ldo, o_tiled};
+    const int lo = window > 0 ? std::max(0, len - window) : 0;
+    a.nsplit = (len - lo + kDecodeChunk - 1) / kDecodeChunk;
+    switch (D) {
+      case 64: return G <= 4 ? decode_bf16<64, 4>(a, B, s) : decode_bf16<64, 8>(a, B, s);
+      case 128: return G <= 4 ? decode_bf16<128, 4>(a, B, s) : decode_bf16<128, 8>(a, B, s);
+      default: return G <= 4 ? decode_bf16<256, 4>(a, B, s) : decode_bf16<256, 8>(a, B, s);
+    }
+  }
   if (dt == DType::BF16) {
     switch (D) {
       case 64: return decode_impl<bf16_t, 64>(q, ldq, kc, vc, Smax, len, B, Hq, Hkv, window, o, ldo, o_tiled, part, s);

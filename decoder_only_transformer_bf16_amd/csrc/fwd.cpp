@@ -106,8 +106,19 @@ struct Geometry {
     w += r(T * 4) + r(T * 4) + 256;                     // ids, argmax, flag
     w += r(logit_chunk * V * 4);                        // logits when the caller wants none
     w += r(T * (D / 2) * 8);                            // RoPE cos/sin table
+    if (tiled) w += r(skinny_part_floats() * 4) + r(skinny_counters() * 4);
     return w;
   }
+  // Split-K workspace of the few-row products (bf16, at most kSkinnyRows rows):
+  // the largest partial set over the five projections, one counter per 64 outputs.
+  int64_t skinny_part_floats() const {
+    const int Mk = (int)std::min<int64_t>(T, fwdk::kSkinnyRows);
+    const int64_t nk[5][2] = {{qkv_rows, H}, {H, Hq * D}, {2 * F, H}, {H, F}, {V, H}};
+    int64_t f = 0;
+    for (const auto& p : nk) f = std::max(f, fwdk::skinny_part_floats(Mk, (int)p[0], (int)p[1]));
+    return f;
+  }
+  int64_t skinny_counters() const { return fwdk::skinny_groups((int)std::max({qkv_rows, H, 2 * F, V})); }
 };
 
 Geometry geometry(const fwd_config* c) {
@@ -159,6 +170,7 @@ struct fwd_model {
   int* flag = nullptr;
   float* logits_ws = nullptr;
   float2* rope_cs = nullptr;
+  fwdk::SplitK sk{};  // workspace of the few-row products (bf16)
 
   // per-kernel-class event timing (fwd_set_timing)
   bool timing = false;
@@ -228,6 +240,7 @@ struct fwd_session {
   char* vc = nullptr;
   int64_t layer_bytes = 0;
   float* part = nullptr;
+  unsigned* count = nullptr;  // [Bmax, Hkv] arrival counters of the decode attention
   float2* rope = nullptr;  // [Smax, D / 2]
   ~fwd_session() {
     if (m && m->stream) (void)hipStreamSynchronize(m->stream);
@@ -440,6 +453,13 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     if (int rc = m->alloc((void**)&m->amax, T * 4)) return rc;
     if (int rc = m->alloc((void**)&m->flag, 256)) return rc;
     if (int rc = m->alloc((void**)&m->logits_ws, g.logit_chunk * g.V * 4)) return rc;
+    if (g.tiled) {
+      m->sk.part_floats = g.skinny_part_floats();
+      m->sk.count_len = g.skinny_counters();
+      if (int rc = m->alloc((void**)&m->sk.part, std::max<int64_t>(m->sk.part_floats, 1) * 4)) return rc;
+      if (int rc = m->alloc((void**)&m->sk.count, m->sk.count_len * 4)) return rc;
+      HIP_TRY(hipMemsetAsync(m->sk.count, 0, m->sk.count_len * 4, s));  // the kernels leave them zero
+    }
     HIP_TRY(hipStreamSynchronize(s));
     return FWD_OK;
   };
@@ -478,6 +498,7 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
   const int64_t TH = T * H;
   float* hidden = o.hidden;
   const bool tl = g.tiled;
+  const fwdk::SplitK* sk = tl ? &m->sk : nullptr;  // used by products of at most kSkinnyRows rows
 
   m->marks.clear();
   m->events_used = 0;
@@ -500,17 +521,18 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
     const float* next_norm = last ? m->final_norm : m->layers[l + 1].attn_norm;
 
     // attention sublayer (its input norm is already in m->n)
-    fwdk::RopeArgs ra{m->qk, sess ? sess->rope : m->rope_cs, Hq, Hkv, D, S, pos0};
-    TIMED(m, FWD_KERNEL_QKV_ROPE, fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, tl, s));
+    // with a session, the epilogue also stores the rotated keys and the values in the cache
+    void* kc = sess ? sess->kc + l * sess->layer_bytes : nullptr;
+    void* vc = sess ? sess->vc + l * sess->layer_bytes : nullptr;
+    fwdk::RopeArgs ra{m->qk, sess ? sess->rope : m->rope_cs, Hq, Hkv, D, S, pos0, kc, vc, sess ? sess->Smax : 0};
+    TIMED(m, FWD_KERNEL_QKV_ROPE, fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, tl, s, sk));
     const int64_t ldqkv = (int64_t)(Hq + 2 * Hkv) * D;
     const int window = m->kinds[l] == FWD_LAYER_LOCAL ? m->cfg.sliding_window : 0;
     if (sess) {
-      void* kc = sess->kc + l * sess->layer_bytes;
-      void* vc = sess->vc + l * sess->layer_bytes;
-      TIMED(m, FWD_KERNEL_KV_STORE, fwdk::kv_store(dt, qk, ldqkv, Hq, Hkv, D, B, S, pos0, kc, vc, sess->Smax, s));
       if (decode) {
         TIMED(m, FWD_KERNEL_ATTENTION, fwdk::attention_decode(dt, qk, ldqkv, kc, vc, sess->Smax, pos0 + 1, B, Hq, Hkv,
-                                                              D, window, m->o, (int64_t)Hq * D, tl, sess->part, s));
+                                                              D, window, m->o, (int64_t)Hq * D, tl, sess->part, sess->count,
+                                                              s));
       }
     }
     if (!decode) {
@@ -534,21 +556,21 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
     TIMED(m, FWD_KERNEL_ATTENTION, fwdk::attention(dt, aa, s));
     }
     if (!sandwich) {
-      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_residual(dt, m->o, w.wo, xin, xmid, M, H, Hq * D, tl, s));
+      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_residual(dt, m->o, w.wo, xin, xmid, M, H, Hq * D, tl, s, sk));
       TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, tl, s));
     } else {
-      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_store(dt, m->o, w.wo, m->u, H, M, H, Hq * D, 0.f, tl, s));
+      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_store(dt, m->o, w.wo, m->u, H, M, H, Hq * D, 0.f, tl, s, sk));
       TIMED(m, FWD_KERNEL_NORM, fwdk::add_norm(dt, xin, m->u, w.post_attn, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, tl, s));
     }
 
     // feed-forward sublayer
-    TIMED(m, FWD_KERNEL_GATE_UP, fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, tl, s));
+    TIMED(m, FWD_KERNEL_GATE_UP, fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, tl, s, sk));
     float* final32 = (last && hidden) ? hidden + (int64_t)(L + 1) * TH : nullptr;
     if (!sandwich) {
-      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, tl, s));
+      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, tl, s, sk));
       TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xout, next_norm, m->n, final32, M, H, eps, tl, s));
     } else {
-      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_store(dt, m->a, w.wdown, m->u, H, M, H, F, 0.f, tl, s));
+      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_store(dt, m->a, w.wdown, m->u, H, M, H, F, 0.f, tl, s, sk));
       TIMED(m, FWD_KERNEL_NORM, fwdk::add_norm(dt, xmid, m->u, w.post_ffn, xout, next_norm, m->n, final32, M, H, eps, tl, s));
     }
     cur = xout;
@@ -562,14 +584,14 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
   const float cap = m->cfg.final_logit_softcap;
   int32_t* am = o.argmax ? o.argmax : m->amax;
   if (o.logits) {
-    TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, m->n, m->embed, o.logits, V, M, V, H, cap, tl, s));
+    TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, m->n, m->embed, o.logits, V, M, V, H, cap, tl, s, sk));
     TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(o.logits, V, M, V, am, m->flag, s));
   } else {
     const int64_t chunk = g.logit_chunk;
     for (int64_t r0 = 0; r0 < T; r0 += chunk) {
       const int rows = (int)std::min<int64_t>(chunk, T - r0);
       const char* nrow = (const char*)m->n + r0 * H * g.esize;  // (r0 is a multiple of 16: a tile row)
-      TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, nrow, m->embed, m->logits_ws, V, rows, V, H, cap, tl, s));
+      TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, nrow, m->embed, m->logits_ws, V, rows, V, H, cap, tl, s, sk));
       TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(m->logits_ws, V, rows, V, am + r0, m->flag, s));
     }
   }
@@ -631,6 +653,10 @@ int fwd_session_create(fwd_model* m, int32_t max_batch, int32_t max_seq, fwd_ses
     HIP_TRY(hipMalloc(&p, (size_t)round_up((int64_t)max_batch * g.Hq * nsplit * (g.D + 2) * 4, 256)));
     se->allocs.push_back(p);
     se->part = (float*)p;
+    HIP_TRY(hipMalloc(&p, (size_t)round_up((int64_t)max_batch * g.Hkv * 4, 256)));
+    se->allocs.push_back(p);
+    se->count = (unsigned*)p;
+    HIP_TRY(hipMemsetAsync(p, 0, (size_t)max_batch * g.Hkv * 4, m->stream));  // the kernel leaves them zero
     return rope_table(m, &se->rope, max_seq, se->allocs);
   };
   if (int rc = run()) {

@@ -7,6 +7,7 @@
 // (BM/WM) x (BN/WN) sub-tile, K staged through LDS in 64-wide slices, double
 // buffered, with the next slice's global loads in flight during the MFMAs.
 // f32 path: an LDS-tiled VALU kernel (the fp32 configuration is tiny).
+#include <algorithm>
 #include <utility>
 
 #include "common.h"
@@ -110,7 +111,12 @@ template <int C, typename T>
 struct EpiRope {
   T* qkv;  // [M, (Hq + 2 Hkv) D]: rotated q, rotated k, plain v, natural dim order
   const float2* cs;
-  int Hq, Hkv, D, S, pos0;  // row r is position pos0 + r % S
+  int Hq, Hkv, D, S, pos0;  // row r is sequence r / S at position pos0 + r % S
+  T *kc, *vc;               // optional KV cache [B, Hkv, Smax, D]: rotated k and v stored there too
+  int Smax;
+  __device__ __forceinline__ T* cache(T* base, int row, int head, int d) const {
+    return base + (((int64_t)(row / S) * Hkv + head) * Smax + pos0 + row % S) * D + d;
+  }
   template <int R>
   __device__ __forceinline__ void batch(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
                                         bool ok0, bool ok1) const {
@@ -132,11 +138,17 @@ struct EpiRope {
     for (int q = 0; q < R; ++q) {
       if (row[q] < 0) continue;
       T* dst = qkv + (int64_t)row[q] * (qsz + 2 * ksz) + sec + head * D + k;
-      Elem<T>::store(dst, v0[q] * r[q].x - v1[q] * r[q].y);
-      Elem<T>::store(dst + D / 2, v0[q] * r[q].y + v1[q] * r[q].x);
+      const float a = v0[q] * r[q].x - v1[q] * r[q].y, b = v0[q] * r[q].y + v1[q] * r[q].x;
+      Elem<T>::store(dst, a);
+      Elem<T>::store(dst + D / 2, b);
+      if (sec && kc) {
+        T* kd = cache(kc, row[q], head, k);
+        Elem<T>::store(kd, a);
+        Elem<T>::store(kd + D / 2, b);
+      }
     }
   }
-  __device__ __forceinline__ void pair(int row, int c, float v0, float v1, bool ok0, bool) const {
+  __device__ __forceinline__ void pair(int row, int c, float v0, float v1, bool ok0, bool ok1) const {
     if (!ok0) return;
     const int qsz = Hq * D, ksz = Hkv * D;
     T* out = qkv + (int64_t)row * (qsz + 2 * ksz);
@@ -148,11 +160,25 @@ struct EpiRope {
       const int k = (pd / (2 * C)) * C + (pd % C);  // rotation index in [0, D/2)
       const float2 r = cs[(int64_t)t * (D / 2) + k];
       T* dst = out + sec + head * D + k;
-      Elem<T>::store(dst, v0 * r.x - v1 * r.y);
-      Elem<T>::store(dst + D / 2, v0 * r.y + v1 * r.x);
+      const float a = v0 * r.x - v1 * r.y, b = v0 * r.y + v1 * r.x;
+      Elem<T>::store(dst, a);
+      Elem<T>::store(dst + D / 2, b);
+      if (sec && kc) {
+        T* kd = cache(kc, row, head, k);
+        Elem<T>::store(kd, a);
+        Elem<T>::store(kd + D / 2, b);
+      }
     } else {  // value columns are not permuted
       Elem<T>::store(out + c, v0);
-      Elem<T>::store(out + c + C, v1);
+      if (ok1) Elem<T>::store(out + c + C, v1);
+      if (vc) {
+        const int vcol = c - qsz - ksz, vh = vcol / D, vd = vcol - vh * D;
+        Elem<T>::store(cache(vc, row, vh, vd), v0);
+        if (ok1) {
+          const int vcol1 = vcol + C, vh1 = vcol1 / D, vd1 = vcol1 - vh1 * D;
+          Elem<T>::store(cache(vc, row, vh1, vd1), v1);
+        }
+      }
     }
   }
 };
@@ -192,14 +218,6 @@ __device__ __forceinline__ int swz(int r, int c) {
 template <int BK>
 __device__ __forceinline__ int lds_off(int r, int c) {
   return r * BK + (swz<BK>(r, c) << 3);
-}
-
-// Raw buffer resource over `bytes` bytes at `base` (gfx9 dword3: 32-bit data
-// format, the value untyped loads require). Loads whose offset lies past `bytes`
-// return zero, which pads the ragged edges of a tile without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
 // Global -> LDS copy of 1 KiB of a BK-wide K slice of a ROWS-row operand tile with
@@ -663,12 +681,191 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
+// ------------------------------------------------------------------ few rows (split K)
+// Products with at most 64 rows (one token per sequence in a decode step) are bound by
+// streaming W once from HBM, and a tiled kernel would start too few workgroups for
+// that. Here a workgroup owns a 64-column group (four 16-column blocks, so that packed
+// columns c and c + 32 meet in one thread for the pair epilogues) and a range of K
+// tiles; its four wavefronts take every fourth K tile of the range. Each 16 x 32 tile
+// of W (1 KiB, contiguous in the K-tiled layout) is one 16-byte load per lane and
+// feeds one v_mfma_f32_16x16x32_bf16 per 16-row block of X (lane l holds row or
+// column l % 16 and K elements 8 (l / 16) .. + 7 of both operands; the product's
+// register r of lane l is row 4 (l / 16) + r, column l % 16). The wavefronts' sums
+// meet in LDS. When K is split over several workgroups, each writes its fp32 partial
+// tile, and the last to arrive at the group's counter adds the partials in split
+// order (so the result does not depend on the arrival order), runs the epilogue and
+// re-arms the counter.
+constexpr int kSkUnroll = 8;     // K tiles per wavefront in flight
+constexpr int kSkTarget = 448;   // workgroups a launch aims for (about one resident round)
+constexpr int kSkMinTiles = 8;   // fewest K tiles per split
+
+struct SkinnyPlan {
+  int groups, nsplit, kps;  // 64-column groups, K splits, K tiles per split
+};
+SkinnyPlan skinny_plan(int N, int K) {
+  SkinnyPlan p;
+  const int KT = K / 32;
+  p.groups = (N + 63) / 64;
+  int ns = std::max(1, std::min((kSkTarget + p.groups - 1) / p.groups, KT / kSkMinTiles));
+  p.kps = (KT + ns - 1) / ns;
+  p.nsplit = (KT + p.kps - 1) / p.kps;
+  return p;
+}
+int skinny_blocks(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }  // 16-row blocks of the tile
+
+template <int MB, class Epi>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
+                                                         int M, int N, int K, int nsplit, int kps,
+                                                         float* __restrict__ part, unsigned* __restrict__ count,
+                                                         Epi epi) {
+  constexpr int RW = 16 * MB, LD = 64 + 4, U = kSkUnroll;
+  __shared__ float red[4][RW][LD];
+  __shared__ int last;
+  const int KT = K >> 5;
+  const int g = blockIdx.x / nsplit, sp = blockIdx.x - g * nsplit;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kt0 = sp * kps, kt1 = min(KT, kt0 + kps);
+  const int64_t npad = ((int64_t)N + 15) & ~(int64_t)15;  // W rows are padded to 16 (zeros)
+  const int64_t wrows = npad - (int64_t)g * 64 < 64 ? npad - (int64_t)g * 64 : 64;
+  const auto wrs = make_rsrc(W + (int64_t)g * 64 * K, wrows * K * 2);
+  const auto xrs = make_rsrc(X, (int64_t)((M + 15) & ~15) * K * 2);
+  const uint32_t lo = (uint32_t)((lane & 15) * 32 + (lane >> 4) * 8) * 2u;
+
+  floatx4_t acc[MB][4];
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[rb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int base = kt0 + wave; base < kt1; base += 4 * U) {
+    u32x4_t wv[U][4], xv[U][MB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // past the range the offsets leave the buffers: zeros
+      const int kt = base + 4 * u;
+      const bool ok = kt < kt1;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        wv[u][nb] = __builtin_amdgcn_raw_buffer_load_b128(wrs, ok ? (uint32_t)(nb * KT + kt) * 1024u + lo : 0x80000000u,
+                                                          0, 0);
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+        xv[u][rb] = __builtin_amdgcn_raw_buffer_load_b128(xrs, ok ? (uint32_t)(rb * KT + kt) * 1024u + lo : 0x80000000u,
+                                                          0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[rb][nb] = mfma_16x16x32_bf16(as_bf16x8(xv[u][rb]), as_bf16x8(wv[u][nb]), acc[rb][nb]);
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][rb * 16 + 4 * (lane >> 4) + r][nb * 16 + (lane & 15)] = acc[rb][nb][r];
+  __syncthreads();
+
+  // thread -> column pair (p, p + 32) and rows rq, rq + 8, ...
+  constexpr int R = RW / 8;
+  const int p = threadIdx.x & 31, rq = threadIdx.x >> 5;
+  float v0[R], v1[R];
+  int rows[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const int row = rq + 8 * q;
+    v0[q] = (red[0][row][p] + red[1][row][p]) + (red[2][row][p] + red[3][row][p]);
+    v1[q] = (red[0][row][p + 32] + red[1][row][p + 32]) + (red[2][row][p + 32] + red[3][row][p + 32]);
+    rows[q] = row < M ? row : -1;
+  }
+  if (nsplit > 1) {
+    // Partials travel as device-coherent (agent-scope) stores and loads, which the
+    // XCDs' separate L2s do not keep; the counter is bumped only after every store of
+    // the workgroup has completed, and read back before any partial is loaded. (A
+    // release/acquire fence pair would write back and invalidate the whole L2 in
+    // every workgroup instead.)
+    float* mine = part + ((int64_t)g * nsplit + sp) * RW * 64;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      __hip_atomic_store(mine + (rq + 8 * q) * 64 + p, v0[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mine + (rq + 8 * q) * 64 + p + 32, v1[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(count + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(nsplit - 1);
+    __syncthreads();
+    if (!last) return;
+    const float* all = part + (int64_t)g * nsplit * RW * 64;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      v0[q] = 0.f;
+      v1[q] = 0.f;
+    }
+    constexpr int TB = 8;  // partials loaded per round trip, then added in split order
+    for (int t0 = 0; t0 < nsplit; t0 += TB) {
+      float a0[TB][R], a1[TB][R];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const int t = t0 + u < nsplit ? t0 + u : t0;  // (surplus loads repeat t0, unused)
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+          const float* at = all + (int64_t)t * RW * 64 + (rq + 8 * q) * 64 + p;
+          a0[u][q] = __hip_atomic_load(at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          a1[u][q] = __hip_atomic_load(at + 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < TB; ++u)
+        if (t0 + u < nsplit)
+#pragma unroll
+          for (int q = 0; q < R; ++q) {
+            v0[q] += a0[u][q];
+            v1[q] += a1[u][q];
+          }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(count + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int c = g * 64 + p;
+  epi.batch(rows, c, v0, v1, c < N, c + 32 < N);
+}
+
+template <class Epi>
+hipError_t launch_skinny(const void* X, const void* W, int M, int N, int K, const Epi& epi, const SplitK& sk,
+                         hipStream_t s) {
+  const SkinnyPlan p = skinny_plan(N, K);
+  const int MB = skinny_blocks(M);
+  if (p.nsplit > 1 && ((int64_t)p.groups * p.nsplit * 16 * MB * 64 > sk.part_floats || p.groups > sk.count_len))
+    return hipErrorInvalidValue;  // workspace sized for fewer rows or outputs
+  const dim3 grid(p.groups * p.nsplit), block(256);
+  const bf16_t *x = (const bf16_t*)X, *w = (const bf16_t*)W;
+  switch (MB) {
+    case 1:
+      hipLaunchKernelGGL((gemm_skinny_kernel<1, Epi>), grid, block, 0, s, x, w, M, N, K, p.nsplit, p.kps, sk.part,
+                         sk.count, epi);
+      break;
+    case 2:
+      hipLaunchKernelGGL((gemm_skinny_kernel<2, Epi>), grid, block, 0, s, x, w, M, N, K, p.nsplit, p.kps, sk.part,
+                         sk.count, epi);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_skinny_kernel<4, Epi>), grid, block, 0, s, x, w, M, N, K, p.nsplit, p.kps, sk.part,
+                         sk.count, epi);
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ dispatch
 // Both operands row-major, or both K-tiled (K a multiple of 32).
 template <class Epi>
-hipError_t launch_bf16(const void* X, const void* W, int M, int N, int K, const Epi& epi, bool tiled, hipStream_t s) {
+hipError_t launch_bf16(const void* X, const void* W, int M, int N, int K, const Epi& epi, bool tiled, hipStream_t s,
+                       const SplitK* sk) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (tiled && K % 32) return hipErrorInvalidValue;
+  if (tiled && sk && M <= kSkinnyRows) return launch_skinny(X, W, M, N, K, epi, *sk, s);
   const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   if (tiled) {
     if (big >= 256) return launch_pp<CfgBig, Epi, true>(X, W, M, N, K, epi, s);
@@ -689,36 +886,48 @@ hipError_t launch_f32(const void* X, const void* W, int M, int N, int K, const E
 
 }  // namespace
 
+int64_t skinny_part_floats(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K < 32) return 0;
+  const SkinnyPlan p = skinny_plan(N, K);
+  return p.nsplit > 1 ? (int64_t)p.groups * p.nsplit * 16 * skinny_blocks(std::min(M, kSkinnyRows)) * 64 : 0;
+}
+int64_t skinny_groups(int N) { return N > 0 ? (N + 63) / 64 : 0; }
+
 hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K,
-                      float softcap, bool tiled, hipStream_t s) {
-  if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiStore<32>{Y, ldy, softcap}, tiled, s);
+                      float softcap, bool tiled, hipStream_t s, const SplitK* sk) {
+  if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiStore<32>{Y, ldy, softcap}, tiled, s, sk);
   if (tiled) return hipErrorInvalidValue;
   return launch_f32(X, W, M, N, K, EpiStore<1>{Y, ldy, softcap}, s);
 }
 
 hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xin, float* xout, int M, int N,
-                         int K, bool tiled, hipStream_t s) {
-  if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiResidual<32>{xin, xout, N}, tiled, s);
+                         int K, bool tiled, hipStream_t s, const SplitK* sk) {
+  if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiResidual<32>{xin, xout, N}, tiled, s, sk);
   if (tiled) return hipErrorInvalidValue;
   return launch_f32(X, W, M, N, K, EpiResidual<1>{xin, xout, N}, s);
 }
 
 hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, bool tiled,
-                       hipStream_t s) {
+                       hipStream_t s, const SplitK* sk) {
   if (dt == DType::BF16)
-    return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t>{(bf16_t*)a, F, tiled}, tiled, s);
+    return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t>{(bf16_t*)a, F, tiled}, tiled, s, sk);
   if (tiled) return hipErrorInvalidValue;
   return launch_f32(X, W, M, 2 * F, K, EpiSwiGLU<1, float>{(float*)a, F, false}, s);
 }
 
 hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, bool tiled,
-                         hipStream_t s) {
+                         hipStream_t s, const SplitK* sk) {
   const int N = (r.Hq + 2 * r.Hkv) * r.D;
   if (dt == DType::BF16)
-    return launch_bf16(X, W, M, N, K, EpiRope<32, bf16_t>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0},
-                       tiled, s);
+    return launch_bf16(X, W, M, N, K,
+                       EpiRope<32, bf16_t>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, (bf16_t*)r.kc,
+                                           (bf16_t*)r.vc, r.Smax},
+                       tiled, s, sk);
   if (tiled) return hipErrorInvalidValue;
-  return launch_f32(X, W, M, N, K, EpiRope<1, float>{(float*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0}, s);
+  return launch_f32(X, W, M, N, K,
+                    EpiRope<1, float>{(float*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, (float*)r.kc, (float*)r.vc,
+                                      r.Smax},
+                    s);
 }
 
 }  // namespace fwdk

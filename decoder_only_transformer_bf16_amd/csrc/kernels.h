@@ -17,16 +17,28 @@ inline int pair_chunk(DType dt) { return dt == DType::BF16 ? 32 : 1; }
 // ---- projections Y = X·Wᵀ (X [M, K], W [N, K]) ----
 // `tiled`: X and W are both in the K-tiled layout of common.h (bf16 only, K a
 // multiple of 32, rows padded to 16 and readable); otherwise both are row-major.
+// `sk`: workspace of the split-K kernel for few rows (bf16 K-tiled, M <= kSkinnyRows,
+// e.g. a decode step); without one every product takes the tiled kernels.
 // Y fp32 [M, N] (ldy), optional softcap (0 = off).
+constexpr int kSkinnyRows = 64;
+struct SplitK {
+  float* part;          // fp32 partial tiles, skinny_part_floats() of them
+  unsigned* count;      // one arrival counter per 64-column group; zero between launches
+  int64_t part_floats;  // capacity of part
+  int64_t count_len;    // capacity of count
+};
+// Partial floats and counters a product of M rows, N outputs and K inputs needs.
+int64_t skinny_part_floats(int M, int N, int K);
+int64_t skinny_groups(int N);
 hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K,
-                      float softcap, bool tiled, hipStream_t s);
+                      float softcap, bool tiled, hipStream_t s, const SplitK* sk = nullptr);
 // xout[M, N] = xin + X·Wᵀ (fp32 residual stream, row stride N; xin may equal xout).
 hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xin, float* xout, int M, int N,
-                         int K, bool tiled, hipStream_t s);
+                         int K, bool tiled, hipStream_t s, const SplitK* sk = nullptr);
 // a[M, F] = silu(g) * u with W packed as interleaved gate/up chunks (N = 2F); with
 // `tiled`, a is written K-tiled too (it is the down projection's X).
 hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, bool tiled,
-                       hipStream_t s);
+                       hipStream_t s, const SplitK* sk = nullptr);
 // QKV projection with RoPE on q and k; N = (Hq + 2 Hkv) D with packed q/k rows.
 // Writes qkv [M, (Hq + 2 Hkv) D]: rotated q heads, rotated k heads, then the value
 // heads, each in natural dim order. Rows are b * S + t (t = position).
@@ -35,9 +47,12 @@ struct RopeArgs {
   const float2* cs;  // [positions, D / 2] (cos, sin)
   int Hq, Hkv, D, S;
   int pos0;          // row r is at position pos0 + r % S (0 for a prefill)
+  void* kc = nullptr;  // optional KV cache of the layer, K and V each [B, Hkv, Smax, D]:
+  void* vc = nullptr;  // row r's rotated k and its v also go to sequence r / S, position pos0 + r % S
+  int Smax = 0;
 };
 hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, bool tiled,
-                         hipStream_t s);
+                         hipStream_t s, const SplitK* sk = nullptr);
 
 // ---- attention ----
 struct AttnArgs {
@@ -58,20 +73,20 @@ hipError_t transpose_v(DType dt, const void* src, int64_t ld, void* vt, int ldvt
 bool attention_supported(DType dt, int D);
 
 // ---- KV cache (decode) ----
-// Cache of one layer: K and V each [Bmax, Hkv, Smax, D] (dtype dt), positions contiguous.
-// Stores the rotated k and the v of token rows r = b * S + s (qkv as written by
-// gemm_qkv_rope, row stride ldqkv) at position pos0 + s of sequence b.
-hipError_t kv_store(DType dt, const void* qkv, int64_t ldqkv, int Hq, int Hkv, int D, int B, int S, int pos0,
-                    void* kc, void* vc, int Smax, hipStream_t s);
+// Cache of one layer: K and V each [Bmax, Hkv, Smax, D] (dtype dt), positions contiguous,
+// filled by gemm_qkv_rope (RopeArgs::kc / vc).
 // One query per sequence: o[b, h, :] = softmax over cached keys j < len (and
 // len - 1 - j < window when window > 0) of q·k_j / sqrt(D), times v_j. q rows b of
 // the qkv buffer (stride ldq); o bf16 K-tiled (o_tiled) or row-major with stride ldo.
 // Flash-decoding: key chunks of kDecodeChunk per workgroup, fp32 throughout, merged
-// by a second kernel. `part` holds B * Hq * ceil(len / kDecodeChunk) * (D + 2) floats.
+// by rescaling. `part` holds B * Hq * ceil(len / kDecodeChunk) * (D + 2) floats;
+// `count` B * Hkv arrival counters, zero between launches (each launch leaves them
+// zero), used by the bf16 kernel that merges in place (without it a second kernel
+// merges).
 constexpr int kDecodeChunk = 256;
 hipError_t attention_decode(DType dt, const void* q, int64_t ldq, const void* kc, const void* vc, int Smax, int len,
                             int B, int Hq, int Hkv, int D, int window, void* o, int64_t ldo, bool o_tiled,
-                            float* part, hipStream_t s);
+                            float* part, unsigned* count, hipStream_t s);
 
 // ---- row kernels ----
 // y = RMSNorm(x; w) (w fp32 gains); y of dtype dt (K-tiled with `tiled`: bf16, H a

@@ -35,7 +35,7 @@ EXPORTS = ("fwd_available", "fwd_create", "fwd_output_sizes", "fwd_prefill", "fw
            "fwd_session_create", "fwd_session_prefill", "fwd_session_decode", "fwd_session_length",
            "fwd_session_destroy")
 KERNEL_CLASSES = ("embed", "norm", "qkv_rope", "attention", "o_proj", "gate_up", "down_proj", "lm_head", "argmax",
-                  "v_transpose", "kv_store")
+                  "v_transpose")
 
 c_i32, c_i64, c_f32, c_f64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 

@@ -227,8 +227,7 @@ int fwd_rmsnorm(const float* x, const void* w, void* y, int32_t rows, int32_t hi
 #define FWD_KERNEL_LM_HEAD 7       /* tied LM head (+ softcap)                     */
 #define FWD_KERNEL_ARGMAX 8        /* per-position argmax + non-finite check      */
 #define FWD_KERNEL_V_TRANSPOSE 9   /* values transposed to keys-contiguous order  */
-#define FWD_KERNEL_KV_STORE 10     /* keys and values stored in a session's cache */
-#define FWD_KERNEL_CLASSES 11
+#define FWD_KERNEL_CLASSES 10
 /* enable != 0 turns timing on and clears the accumulated totals; 0 turns it off. */
 int fwd_set_timing(fwd_model* m, int32_t enable);
 /* Accumulated milliseconds and launch count of one kernel class since the last

@@ -201,3 +201,23 @@ def test_session_errors(fwd):
     sess.close()
     model.close()
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("shape", ["d128_g4", "d256_g2_window", "d64_g8"])
+def test_bf16_decode_head_shapes(fwd, shape):
+    """The decode attention's head geometries: 128-wide heads in groups of 4 (Llama-3
+    shape), 256-wide heads in pairs with a 64-key window on local layers (Gemma-style),
+    and 64-wide heads in groups of 8; a 300-token prompt spans two key chunks."""
+    base = {"d128_g4": wl.LLAMA3_8B.replace(n_heads=8, n_kv_heads=2, head_dim=128),
+            "d256_g2_window": wl.GEMMA3_STYLE.replace(n_heads=4, n_kv_heads=2, head_dim=256, sliding_window=64,
+                                                      layer_kind=("local", "global")),
+            "d64_g8": wl.SMOLLM2_135M.replace(n_heads=16, n_kv_heads=2, head_dim=64)}[shape]
+    cfg = base.replace(n_layers=2, hidden=512, ffn=1024, vocab=2048, batch=2, seq=300, name=f"session-{shape}")
+    _say(f"session bf16 {shape}: 2 x 300 prompt + 3 steps")
+    host = wl.draw_all(cfg)
+    prompt = np.asarray(wl.draw_ids(cfg))
+    model = fwd.Model(cfg, upload_weights(cfg, host), max_tokens=2 * 304)
+    toks, logits = _generate(fwd, model, prompt, 3, max_seq=304)
+    _check_cacheless(model, prompt, toks, logits, min_cos=0.9999)
+    _check_against_oracle(cfg, host, prompt[:1], toks[:1], logits[:, :1])
+    model.close()
