@@ -106,7 +106,7 @@ struct Geometry {
     w += r(T * 4) + r(T * 4) + 256;                     // ids, argmax, flag
     w += r(logit_chunk * V * 4);                        // logits when the caller wants none
     w += r(T * (D / 2) * 8);                            // RoPE cos/sin table
-    if (tiled) w += r(skinny_part_floats() * 4) + r(skinny_counters() * 4);
+    if (tiled) w += r(skinny_part_floats() * 4) + r(skinny_counters() * 4) + r(fwdk::skinny_groups((int)H) * 64 * 4);
     return w;
   }
   // Split-K workspace of the few-row products (bf16, at most kSkinnyRows rows):
@@ -171,6 +171,7 @@ struct fwd_model {
   float* logits_ws = nullptr;
   float2* rope_cs = nullptr;
   fwdk::SplitK sk{};  // workspace of the few-row products (bf16)
+  float* ssq = nullptr;  // [H / 64][kSkinnyRows] row sums of squares left by a few-row residual product
 
   // per-kernel-class event timing (fwd_set_timing)
   bool timing = false;
@@ -459,6 +460,7 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
       if (int rc = m->alloc((void**)&m->sk.part, std::max<int64_t>(m->sk.part_floats, 1) * 4)) return rc;
       if (int rc = m->alloc((void**)&m->sk.count, m->sk.count_len * 4)) return rc;
       HIP_TRY(hipMemsetAsync(m->sk.count, 0, m->sk.count_len * 4, s));  // the kernels leave them zero
+      if (int rc = m->alloc((void**)&m->ssq, fwdk::skinny_groups((int)g.H) * fwdk::kSkinnyRows * 4)) return rc;
     }
     HIP_TRY(hipStreamSynchronize(s));
     return FWD_OK;
@@ -509,6 +511,12 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
   TIMED(m, FWD_KERNEL_EMBED, fwdk::embed(dt, m->ids, m->embed, cur, M, H, m->embed_scale, tl, s));
   // first layer's input norm; every later sublayer input norm is fused below
   if (L > 0) TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, cur, m->layers[0].attn_norm, m->n, nullptr, M, H, eps, tl, s));
+  // Few rows, pre-norm, no hidden slots: each residual product also leaves its rows' sums
+  // of squares, and the next product normalises its input itself (no norm launches
+  // after the first).
+  const bool fuse = tl && M <= fwdk::kSkinnyRows && !sandwich && !hidden && L > 0;
+  const int ngroups = (int)fwdk::skinny_groups(H);
+  auto normx = [&](const float* x, const float* w) { return fwdk::RowNormX{x, w, m->ssq, ngroups, eps}; };
 
   const int ldvt = (int)round_up(S, 8);
   char* qk = (char*)m->qk;
@@ -525,7 +533,9 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
     void* kc = sess ? sess->kc + l * sess->layer_bytes : nullptr;
     void* vc = sess ? sess->vc + l * sess->layer_bytes : nullptr;
     fwdk::RopeArgs ra{m->qk, sess ? sess->rope : m->rope_cs, Hq, Hkv, D, S, pos0, kc, vc, sess ? sess->Smax : 0};
-    TIMED(m, FWD_KERNEL_QKV_ROPE, fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, tl, s, sk));
+    const fwdk::RowNormX nq = normx(xin, w.attn_norm);
+    TIMED(m, FWD_KERNEL_QKV_ROPE,
+          fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, tl, s, sk, fuse && l > 0 ? &nq : nullptr));
     const int64_t ldqkv = (int64_t)(Hq + 2 * Hkv) * D;
     const int window = m->kinds[l] == FWD_LAYER_LOCAL ? m->cfg.sliding_window : 0;
     if (sess) {
@@ -555,7 +565,9 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
     aa.o_tiled = tl;
     TIMED(m, FWD_KERNEL_ATTENTION, fwdk::attention(dt, aa, s));
     }
-    if (!sandwich) {
+    if (fuse) {
+      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_residual(dt, m->o, w.wo, xin, xmid, M, H, Hq * D, tl, s, sk, m->ssq));
+    } else if (!sandwich) {
       TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_residual(dt, m->o, w.wo, xin, xmid, M, H, Hq * D, tl, s, sk));
       TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, tl, s));
     } else {
@@ -564,9 +576,12 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
     }
 
     // feed-forward sublayer
-    TIMED(m, FWD_KERNEL_GATE_UP, fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, tl, s, sk));
+    const fwdk::RowNormX nf = normx(xmid, w.ffn_norm);
+    TIMED(m, FWD_KERNEL_GATE_UP, fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, tl, s, sk, fuse ? &nf : nullptr));
     float* final32 = (last && hidden) ? hidden + (int64_t)(L + 1) * TH : nullptr;
-    if (!sandwich) {
+    if (fuse) {
+      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, tl, s, sk, m->ssq));
+    } else if (!sandwich) {
       TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, tl, s, sk));
       TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xout, next_norm, m->n, final32, M, H, eps, tl, s));
     } else {
@@ -583,15 +598,18 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
   // tied LM head (+ softcap) and argmax
   const float cap = m->cfg.final_logit_softcap;
   int32_t* am = o.argmax ? o.argmax : m->amax;
+  const fwdk::RowNormX nh = normx(cur, m->final_norm);
+  const fwdk::RowNormX* nhp = fuse ? &nh : nullptr;
   if (o.logits) {
-    TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, m->n, m->embed, o.logits, V, M, V, H, cap, tl, s, sk));
+    TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, m->n, m->embed, o.logits, V, M, V, H, cap, tl, s, sk, nhp));
     TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(o.logits, V, M, V, am, m->flag, s));
   } else {
     const int64_t chunk = g.logit_chunk;
     for (int64_t r0 = 0; r0 < T; r0 += chunk) {
       const int rows = (int)std::min<int64_t>(chunk, T - r0);
       const char* nrow = (const char*)m->n + r0 * H * g.esize;  // (r0 is a multiple of 16: a tile row)
-      TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, nrow, m->embed, m->logits_ws, V, rows, V, H, cap, tl, s, sk));
+      TIMED(m, FWD_KERNEL_LM_HEAD,
+            fwdk::gemm_store(dt, nrow, m->embed, m->logits_ws, V, rows, V, H, cap, tl, s, sk, nhp));  // (fused: one chunk)
       TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(m->logits_ws, V, rows, V, am + r0, m->flag, s));
     }
   }

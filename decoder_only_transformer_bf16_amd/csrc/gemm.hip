@@ -8,6 +8,7 @@
 // buffered, with the next slice's global loads in flight during the MFMAs.
 // f32 path: an LDS-tiled VALU kernel (the fp32 configuration is tiny).
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -63,6 +64,34 @@ struct EpiResidual {
   const float* xin;
   float* xout;
   int64_t ld;
+  float* ssq = nullptr;  // optional [groups][kSkinnyRows]: per 64-column group, sum of squares of each stored row
+  // Same as batch(), and sq[q] = the sum of squares of the (up to two) values stored in row q.
+  template <int R>
+  __device__ __forceinline__ void batch_sq(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
+                                           bool ok0, bool ok1, float (&sq)[R]) const {
+    float a[R], b[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int64_t i = (int64_t)(row[q] < 0 ? 0 : row[q]) * ld + c;
+      a[q] = (row[q] >= 0 && ok0) ? xin[i] : 0.f;
+      b[q] = (row[q] >= 0 && ok1) ? xin[i + C] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      sq[q] = 0.f;
+      if (row[q] < 0) continue;
+      const int64_t i = (int64_t)row[q] * ld + c;
+      const float x0 = a[q] + v0[q], x1 = b[q] + v1[q];
+      if (ok0) {
+        xout[i] = x0;
+        sq[q] = x0 * x0;
+      }
+      if (ok1) {
+        xout[i + C] = x1;
+        sq[q] += x1 * x1;
+      }
+    }
+  }
   __device__ __forceinline__ void pair(int row, int c, float v0, float v1, bool ok0, bool ok1) const {
     const int64_t i = (int64_t)row * ld + c;
     if (ok0) xout[i] = xin[i] + v0;
@@ -107,12 +136,14 @@ struct EpiSwiGLU {
   }
 };
 
-template <int C, typename T>
+// KV: also store the rotated keys and the values in a KV cache (a separate
+// instantiation, so that the plain prefill keeps the lean epilogue).
+template <int C, typename T, bool KV>
 struct EpiRope {
   T* qkv;  // [M, (Hq + 2 Hkv) D]: rotated q, rotated k, plain v, natural dim order
   const float2* cs;
   int Hq, Hkv, D, S, pos0;  // row r is sequence r / S at position pos0 + r % S
-  T *kc, *vc;               // optional KV cache [B, Hkv, Smax, D]: rotated k and v stored there too
+  T *kc, *vc;               // with KV: the cache [B, Hkv, Smax, D]
   int Smax;
   __device__ __forceinline__ T* cache(T* base, int row, int head, int d) const {
     return base + (((int64_t)(row / S) * Hkv + head) * Smax + pos0 + row % S) * D + d;
@@ -141,7 +172,7 @@ struct EpiRope {
       const float a = v0[q] * r[q].x - v1[q] * r[q].y, b = v0[q] * r[q].y + v1[q] * r[q].x;
       Elem<T>::store(dst, a);
       Elem<T>::store(dst + D / 2, b);
-      if (sec && kc) {
+      if (KV && sec) {
         T* kd = cache(kc, row[q], head, k);
         Elem<T>::store(kd, a);
         Elem<T>::store(kd + D / 2, b);
@@ -163,7 +194,7 @@ struct EpiRope {
       const float a = v0 * r.x - v1 * r.y, b = v0 * r.y + v1 * r.x;
       Elem<T>::store(dst, a);
       Elem<T>::store(dst + D / 2, b);
-      if (sec && kc) {
+      if (KV && sec) {
         T* kd = cache(kc, row, head, k);
         Elem<T>::store(kd, a);
         Elem<T>::store(kd + D / 2, b);
@@ -171,7 +202,7 @@ struct EpiRope {
     } else {  // value columns are not permuted
       Elem<T>::store(out + c, v0);
       if (ok1) Elem<T>::store(out + c + C, v1);
-      if (vc) {
+      if (KV) {
         const int vcol = c - qsz - ksz, vh = vcol / D, vd = vcol - vh * D;
         Elem<T>::store(cache(vc, row, vh, vd), v0);
         if (ok1) {
@@ -699,6 +730,11 @@ constexpr int kSkUnroll = 8;     // K tiles per wavefront in flight
 constexpr int kSkTarget = 448;   // workgroups a launch aims for (about one resident round)
 constexpr int kSkMinTiles = 8;   // fewest K tiles per split
 
+template <class E, class = void>
+struct kHasSq : std::false_type {};
+template <class E>
+struct kHasSq<E, std::void_t<decltype(&E::template batch_sq<2>)>> : std::true_type {};
+
 struct SkinnyPlan {
   int groups, nsplit, kps;  // 64-column groups, K splits, K tiles per split
 };
@@ -713,13 +749,29 @@ SkinnyPlan skinny_plan(int N, int K) {
 }
 int skinny_blocks(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }  // 16-row blocks of the tile
 
-template <int MB, class Epi>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
-                                                         int M, int N, int K, int nsplit, int kps,
-                                                         float* __restrict__ part, unsigned* __restrict__ count,
+// X operand of the few-row kernel: bf16 K-tiled (XTiled) or RMSNorm(x; w) built on the
+// fly from fp32 rows (XNorm), whose per-row sums of squares a residual epilogue left
+// as partials over 64-column groups.
+struct XTiled {
+  const bf16_t* X;
+};
+struct XNorm {
+  const float* x;    // [M, K] fp32 row-major
+  const float* w;    // [K] gains
+  const float* ssq;  // [groups][kSkinnyRows] partial sums of squares of x's rows
+  int groups;
+  float eps;
+};
+
+template <int MB, class XOp, class Epi>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(XOp xop, const bf16_t* __restrict__ W, int M, int N, int K,
+                                                         int nsplit, int kps, float* __restrict__ part,
+                                                         unsigned* __restrict__ count, float* __restrict__ ssq_out,
                                                          Epi epi) {
-  constexpr int RW = 16 * MB, LD = 64 + 4, U = kSkUnroll;
+  constexpr bool kNorm = std::is_same<XOp, XNorm>::value;
+  constexpr int RW = 16 * MB, LD = 64 + 4, U = kNorm && MB > 1 ? kSkUnroll / MB : kSkUnroll;
   __shared__ float red[4][RW][LD];
+  __shared__ float rinv_s[RW];
   __shared__ int last;
   const int KT = K >> 5;
   const int g = blockIdx.x / nsplit, sp = blockIdx.x - g * nsplit;
@@ -728,8 +780,32 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16_t* __restri
   const int64_t npad = ((int64_t)N + 15) & ~(int64_t)15;  // W rows are padded to 16 (zeros)
   const int64_t wrows = npad - (int64_t)g * 64 < 64 ? npad - (int64_t)g * 64 : 64;
   const auto wrs = make_rsrc(W + (int64_t)g * 64 * K, wrows * K * 2);
-  const auto xrs = make_rsrc(X, (int64_t)((M + 15) & ~15) * K * 2);
   const uint32_t lo = (uint32_t)((lane & 15) * 32 + (lane >> 4) * 8) * 2u;
+
+  __amdgpu_buffer_rsrc_t xrs, grs;
+  float rinv[MB];
+  if constexpr (kNorm) {
+    // 1 / rms of each row from the partials, added in group order by every workgroup alike
+    constexpr int SL = 256 / RW;  // slices of the groups per row
+    float* sums = &red[0][0][0];  // [SL][RW], free until the K loop ends
+    const int r = threadIdx.x % RW, sl = threadIdx.x / RW;
+    float sacc = 0.f;
+    for (int j = sl; j < xop.groups; j += SL) sacc += xop.ssq[(int64_t)j * kSkinnyRows + r];
+    sums[sl * RW + r] = sacc;
+    __syncthreads();
+    if (threadIdx.x < RW) {
+      float t = 0.f;
+      for (int j = 0; j < SL; ++j) t += sums[j * RW + threadIdx.x];
+      rinv_s[threadIdx.x] = threadIdx.x < M ? fast_rsqrt(t / (float)K + xop.eps) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) rinv[rb] = rinv_s[rb * 16 + (lane & 15)];
+    xrs = make_rsrc(xop.x, (int64_t)M * K * 4);  // rows past M read as zeros
+    grs = make_rsrc(xop.w, (int64_t)K * 4);
+  } else {
+    xrs = make_rsrc(xop.X, (int64_t)((M + 15) & ~15) * K * 2);
+  }
 
   floatx4_t acc[MB][4];
 #pragma unroll
@@ -747,10 +823,33 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16_t* __restri
       for (int nb = 0; nb < 4; ++nb)
         wv[u][nb] = __builtin_amdgcn_raw_buffer_load_b128(wrs, ok ? (uint32_t)(nb * KT + kt) * 1024u + lo : 0x80000000u,
                                                           0, 0);
+      if constexpr (kNorm) {
+        // this lane's 8 elements k .. k + 7 of row rb * 16 + lane % 16, times gain and 1 / rms, to bf16
+        const int k = kt * 32 + (lane >> 4) * 8;
+        const uint32_t go = ok ? (uint32_t)k * 4u : 0x80000000u;
+        const u32x4_t g0 = __builtin_amdgcn_raw_buffer_load_b128(grs, go, 0, 0);
+        const u32x4_t g1 = __builtin_amdgcn_raw_buffer_load_b128(grs, go + 16u, 0, 0);
 #pragma unroll
-      for (int rb = 0; rb < MB; ++rb)
-        xv[u][rb] = __builtin_amdgcn_raw_buffer_load_b128(xrs, ok ? (uint32_t)(rb * KT + kt) * 1024u + lo : 0x80000000u,
-                                                          0, 0);
+        for (int rb = 0; rb < MB; ++rb) {
+          const uint32_t xo = ok ? (uint32_t)((rb * 16 + (lane & 15)) * K + k) * 4u : 0x80000000u;
+          const u32x4_t x0 = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, 0, 0);
+          const u32x4_t x1 = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16u, 0, 0);
+          u32x4_t packed;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            packed[e] = pack_bf16x2(__uint_as_float(x0[2 * e]) * __uint_as_float(g0[2 * e]) * rinv[rb],
+                                    __uint_as_float(x0[2 * e + 1]) * __uint_as_float(g0[2 * e + 1]) * rinv[rb]);
+            packed[e + 2] = pack_bf16x2(__uint_as_float(x1[2 * e]) * __uint_as_float(g1[2 * e]) * rinv[rb],
+                                        __uint_as_float(x1[2 * e + 1]) * __uint_as_float(g1[2 * e + 1]) * rinv[rb]);
+          }
+          xv[u][rb] = packed;
+        }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+          xv[u][rb] = __builtin_amdgcn_raw_buffer_load_b128(
+              xrs, ok ? (uint32_t)(rb * KT + kt) * 1024u + lo : 0x80000000u, 0, 0);
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -830,30 +929,44 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16_t* __restri
     if (threadIdx.x == 0) __hip_atomic_store(count + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int c = g * 64 + p;
+  if constexpr (kHasSq<Epi>::value) {
+    if (ssq_out) {
+      // per-row sums of squares of this group's stored values: 32 lanes per row, one store
+      float sq[R];
+      epi.batch_sq(rows, c, v0, v1, c < N, c + 32 < N, sq);
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) sq[q] += __shfl_xor(sq[q], o, 32);
+        if (p == 0) ssq_out[(int64_t)g * kSkinnyRows + rq + 8 * q] = sq[q];
+      }
+      return;
+    }
+  }
   epi.batch(rows, c, v0, v1, c < N, c + 32 < N);
 }
 
-template <class Epi>
-hipError_t launch_skinny(const void* X, const void* W, int M, int N, int K, const Epi& epi, const SplitK& sk,
-                         hipStream_t s) {
+template <class XOp, class Epi>
+hipError_t launch_skinny(const XOp& xop, const void* W, int M, int N, int K, const Epi& epi, const SplitK& sk,
+                         float* ssq_out, hipStream_t s) {
   const SkinnyPlan p = skinny_plan(N, K);
   const int MB = skinny_blocks(M);
   if (p.nsplit > 1 && ((int64_t)p.groups * p.nsplit * 16 * MB * 64 > sk.part_floats || p.groups > sk.count_len))
     return hipErrorInvalidValue;  // workspace sized for fewer rows or outputs
   const dim3 grid(p.groups * p.nsplit), block(256);
-  const bf16_t *x = (const bf16_t*)X, *w = (const bf16_t*)W;
+  const bf16_t* w = (const bf16_t*)W;
   switch (MB) {
     case 1:
-      hipLaunchKernelGGL((gemm_skinny_kernel<1, Epi>), grid, block, 0, s, x, w, M, N, K, p.nsplit, p.kps, sk.part,
-                         sk.count, epi);
+      hipLaunchKernelGGL((gemm_skinny_kernel<1, XOp, Epi>), grid, block, 0, s, xop, w, M, N, K, p.nsplit, p.kps,
+                         sk.part, sk.count, ssq_out, epi);
       break;
     case 2:
-      hipLaunchKernelGGL((gemm_skinny_kernel<2, Epi>), grid, block, 0, s, x, w, M, N, K, p.nsplit, p.kps, sk.part,
-                         sk.count, epi);
+      hipLaunchKernelGGL((gemm_skinny_kernel<2, XOp, Epi>), grid, block, 0, s, xop, w, M, N, K, p.nsplit, p.kps,
+                         sk.part, sk.count, ssq_out, epi);
       break;
     default:
-      hipLaunchKernelGGL((gemm_skinny_kernel<4, Epi>), grid, block, 0, s, x, w, M, N, K, p.nsplit, p.kps, sk.part,
-                         sk.count, epi);
+      hipLaunchKernelGGL((gemm_skinny_kernel<4, XOp, Epi>), grid, block, 0, s, xop, w, M, N, K, p.nsplit, p.kps,
+                         sk.part, sk.count, ssq_out, epi);
   }
   return hipGetLastError();
 }
@@ -862,10 +975,15 @@ hipError_t launch_skinny(const void* X, const void* W, int M, int N, int K, cons
 // Both operands row-major, or both K-tiled (K a multiple of 32).
 template <class Epi>
 hipError_t launch_bf16(const void* X, const void* W, int M, int N, int K, const Epi& epi, bool tiled, hipStream_t s,
-                       const SplitK* sk) {
+                       const SplitK* sk, const RowNormX* nx = nullptr, float* ssq_out = nullptr) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (tiled && K % 32) return hipErrorInvalidValue;
-  if (tiled && sk && M <= kSkinnyRows) return launch_skinny(X, W, M, N, K, epi, *sk, s);
+  const bool few = tiled && sk && M <= kSkinnyRows;
+  if ((nx || ssq_out) && !few) return hipErrorInvalidValue;  // only the few-row kernel fuses the norm
+  if (few) {
+    if (nx) return launch_skinny(XNorm{nx->x, nx->w, nx->ssq, nx->groups, nx->eps}, W, M, N, K, epi, *sk, ssq_out, s);
+    return launch_skinny(XTiled{(const bf16_t*)X}, W, M, N, K, epi, *sk, ssq_out, s);
+  }
   const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   if (tiled) {
     if (big >= 256) return launch_pp<CfgBig, Epi, true>(X, W, M, N, K, epi, s);
@@ -894,39 +1012,51 @@ int64_t skinny_part_floats(int M, int N, int K) {
 int64_t skinny_groups(int N) { return N > 0 ? (N + 63) / 64 : 0; }
 
 hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K,
-                      float softcap, bool tiled, hipStream_t s, const SplitK* sk) {
-  if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiStore<32>{Y, ldy, softcap}, tiled, s, sk);
-  if (tiled) return hipErrorInvalidValue;
+                      float softcap, bool tiled, hipStream_t s, const SplitK* sk, const RowNormX* nx) {
+  if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiStore<32>{Y, ldy, softcap}, tiled, s, sk, nx);
+  if (tiled || nx) return hipErrorInvalidValue;
   return launch_f32(X, W, M, N, K, EpiStore<1>{Y, ldy, softcap}, s);
 }
 
 hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xin, float* xout, int M, int N,
-                         int K, bool tiled, hipStream_t s, const SplitK* sk) {
-  if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiResidual<32>{xin, xout, N}, tiled, s, sk);
-  if (tiled) return hipErrorInvalidValue;
+                         int K, bool tiled, hipStream_t s, const SplitK* sk, float* ssq_out) {
+  if (dt == DType::BF16)
+    return launch_bf16(X, W, M, N, K, EpiResidual<32>{xin, xout, N}, tiled, s, sk, nullptr, ssq_out);
+  if (tiled || ssq_out) return hipErrorInvalidValue;
   return launch_f32(X, W, M, N, K, EpiResidual<1>{xin, xout, N}, s);
 }
 
 hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, bool tiled,
-                       hipStream_t s, const SplitK* sk) {
+                       hipStream_t s, const SplitK* sk, const RowNormX* nx) {
   if (dt == DType::BF16)
-    return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t>{(bf16_t*)a, F, tiled}, tiled, s, sk);
-  if (tiled) return hipErrorInvalidValue;
+    return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t>{(bf16_t*)a, F, tiled}, tiled, s, sk, nx);
+  if (tiled || nx) return hipErrorInvalidValue;
   return launch_f32(X, W, M, 2 * F, K, EpiSwiGLU<1, float>{(float*)a, F, false}, s);
 }
 
 hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, bool tiled,
-                         hipStream_t s, const SplitK* sk) {
+                         hipStream_t s, const SplitK* sk, const RowNormX* nx) {
   const int N = (r.Hq + 2 * r.Hkv) * r.D;
-  if (dt == DType::BF16)
-    return launch_bf16(X, W, M, N, K,
-                       EpiRope<32, bf16_t>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, (bf16_t*)r.kc,
-                                           (bf16_t*)r.vc, r.Smax},
-                       tiled, s, sk);
-  if (tiled) return hipErrorInvalidValue;
+  if ((r.kc == nullptr) != (r.vc == nullptr)) return hipErrorInvalidValue;
+  if (dt == DType::BF16) {
+    if (r.kc)
+      return launch_bf16(X, W, M, N, K,
+                         EpiRope<32, bf16_t, true>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, (bf16_t*)r.kc,
+                                                   (bf16_t*)r.vc, r.Smax},
+                         tiled, s, sk, nx);
+    return launch_bf16(
+        X, W, M, N, K,
+        EpiRope<32, bf16_t, false>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, nullptr, nullptr, 0}, tiled,
+        s, sk, nx);
+  }
+  if (tiled || nx) return hipErrorInvalidValue;
+  if (r.kc)
+    return launch_f32(X, W, M, N, K,
+                      EpiRope<1, float, true>{(float*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, (float*)r.kc,
+                                              (float*)r.vc, r.Smax},
+                      s);
   return launch_f32(X, W, M, N, K,
-                    EpiRope<1, float>{(float*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, (float*)r.kc, (float*)r.vc,
-                                      r.Smax},
+                    EpiRope<1, float, false>{(float*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, nullptr, nullptr, 0},
                     s);
 }
 

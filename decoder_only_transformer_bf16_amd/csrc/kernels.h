@@ -30,15 +30,27 @@ struct SplitK {
 // Partial floats and counters a product of M rows, N outputs and K inputs needs.
 int64_t skinny_part_floats(int M, int N, int K);
 int64_t skinny_groups(int N);
+// The few-row kernel can take X as RMSNorm(x; w) of fp32 rows instead of a bf16 operand
+// (`nx`), given the per-row sums of squares that a residual product over the same rows
+// left as partials (`ssq_out` of gemm_residual): ssq[g * kSkinnyRows + r] is row r's
+// sum over output columns [64 g, 64 g + 64). Both need `sk` and M <= kSkinnyRows.
+struct RowNormX {
+  const float* x;    // [M, K] fp32 row-major
+  const float* w;    // [K] gains
+  const float* ssq;  // [groups][kSkinnyRows]
+  int groups;        // ceil(K / 64)
+  float eps;
+};
 hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K,
-                      float softcap, bool tiled, hipStream_t s, const SplitK* sk = nullptr);
+                      float softcap, bool tiled, hipStream_t s, const SplitK* sk = nullptr,
+                      const RowNormX* nx = nullptr);
 // xout[M, N] = xin + X·Wᵀ (fp32 residual stream, row stride N; xin may equal xout).
 hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xin, float* xout, int M, int N,
-                         int K, bool tiled, hipStream_t s, const SplitK* sk = nullptr);
+                         int K, bool tiled, hipStream_t s, const SplitK* sk = nullptr, float* ssq_out = nullptr);
 // a[M, F] = silu(g) * u with W packed as interleaved gate/up chunks (N = 2F); with
 // `tiled`, a is written K-tiled too (it is the down projection's X).
 hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, bool tiled,
-                       hipStream_t s, const SplitK* sk = nullptr);
+                       hipStream_t s, const SplitK* sk = nullptr, const RowNormX* nx = nullptr);
 // QKV projection with RoPE on q and k; N = (Hq + 2 Hkv) D with packed q/k rows.
 // Writes qkv [M, (Hq + 2 Hkv) D]: rotated q heads, rotated k heads, then the value
 // heads, each in natural dim order. Rows are b * S + t (t = position).
@@ -52,7 +64,7 @@ struct RopeArgs {
   int Smax = 0;
 };
 hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, bool tiled,
-                         hipStream_t s, const SplitK* sk = nullptr);
+                         hipStream_t s, const SplitK* sk = nullptr, const RowNormX* nx = nullptr);
 
 // ---- attention ----
 struct AttnArgs {

@@ -98,3 +98,28 @@ def test_few_rows_bitwise_repeatable(fwd, setup):
         again = _prefill(model, ids[:4])
         for k in ("logits", "hidden", "argmax"):
             assert np.array_equal(first[k], again[k]), f"run {i + 1}: {k} differs"
+
+
+def test_fused_norm_matches_unfused_and_oracle(fwd, setup):
+    """Without hidden slots, the few-row path normalises inside the products (each
+    residual product leaves its rows' sums of squares, the next one builds its bf16
+    input from the fp32 rows); with slots requested it runs the separate norm kernels.
+    The two differ only in summation order: logits to cosine >= 0.9999 and the same
+    argmax up to near ties, both against the oracle too; the fused run repeats bitwise."""
+    model, host, ids = setup
+    for rows in (1, 2, 4):
+        part = ids[:rows] if rows > 1 else ids[:1, :1]
+        out = model.prefill(part, logits=True, hidden=False, argmax=True)
+        fused = {k: out[k].cpu().numpy() for k in ("logits", "argmax")}
+        plain = _prefill(model, part)
+        c = cosine(fused["logits"], plain["logits"])
+        assert c >= COS_MIN, f"{part.shape}: cosine fused vs unfused {c}"
+        ref = oracle.forward(CFG, wl.HostWeights(host), part, want_hidden=False)
+        c_ref = cosine(fused["logits"], ref["logits"])
+        assert c_ref >= COS_MIN, f"{part.shape}: cosine vs oracle {c_ref}"
+        pinned, near, fails = argmax_check(fused["argmax"], ref["logits"], fused["logits"])
+        assert not fails, fails[:5]
+        again = model.prefill(part, logits=True, hidden=False, argmax=True)
+        assert np.array_equal(again["logits"].cpu().numpy(), fused["logits"])
+        _say(f"  {part.shape}: fused vs unfused cosine {c:.7f}, vs oracle {c_ref:.7f}, "
+             f"max|d| {np.abs(fused['logits'] - plain['logits']).max():.2e}")
