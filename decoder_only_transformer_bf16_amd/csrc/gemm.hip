@@ -727,8 +727,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // order (so the result does not depend on the arrival order), runs the epilogue and
 // re-arms the counter.
 constexpr int kSkUnroll = 8;     // K tiles per wavefront in flight
+constexpr int kSkUnrollNorm = 4; // the same with the normalised X operand (three times the loads)
 constexpr int kSkTarget = 448;   // workgroups a launch aims for (about one resident round)
 constexpr int kSkMinTiles = 8;   // fewest K tiles per split
+constexpr int kSkWaves = 4;      // wavefronts per workgroup, each on every kSkWaves-th K tile
 
 template <class E, class = void>
 struct kHasSq : std::false_type {};
@@ -764,13 +766,15 @@ struct XNorm {
 };
 
 template <int MB, class XOp, class Epi>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(XOp xop, const bf16_t* __restrict__ W, int M, int N, int K,
+__global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(XOp xop, const bf16_t* __restrict__ W, int M,
+                                                                   int N, int K,
                                                          int nsplit, int kps, float* __restrict__ part,
                                                          unsigned* __restrict__ count, float* __restrict__ ssq_out,
                                                          Epi epi) {
   constexpr bool kNorm = std::is_same<XOp, XNorm>::value;
-  constexpr int RW = 16 * MB, LD = 64 + 4, U = kNorm && MB > 1 ? kSkUnroll / MB : kSkUnroll;
-  __shared__ float red[4][RW][LD];
+  constexpr int RW = 16 * MB, LD = 64 + 4, U = kNorm ? kSkUnrollNorm / MB : kSkUnroll;
+  constexpr int NW = kSkWaves, NT = 64 * NW;
+  __shared__ float red[NW][RW][LD];
   __shared__ float rinv_s[RW];
   __shared__ int last;
   const int KT = K >> 5;
@@ -786,7 +790,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(XOp xop, const bf16_t*
   float rinv[MB];
   if constexpr (kNorm) {
     // 1 / rms of each row from the partials, added in group order by every workgroup alike
-    constexpr int SL = 256 / RW;  // slices of the groups per row
+    constexpr int SL = NT / RW;  // slices of the groups per row
     float* sums = &red[0][0][0];  // [SL][RW], free until the K loop ends
     const int r = threadIdx.x % RW, sl = threadIdx.x / RW;
     float sacc = 0.f;
@@ -813,36 +817,31 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(XOp xop, const bf16_t*
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[rb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int base = kt0 + wave; base < kt1; base += 4 * U) {
+  for (int base = kt0 + wave; base < kt1; base += NW * U) {
+    // every load of the batch first (past the range the offsets leave the buffers:
+    // zeros), then conversions and products; the scheduling barrier keeps the
+    // compiler from trading loads in flight for registers
     u32x4_t wv[U][4], xv[U][MB];
+    u32x4_t xa[kNorm ? U : 1][kNorm ? MB : 1][2], ga[kNorm ? U : 1][2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {  // past the range the offsets leave the buffers: zeros
-      const int kt = base + 4 * u;
+    for (int u = 0; u < U; ++u) {
+      const int kt = base + NW * u;
       const bool ok = kt < kt1;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
         wv[u][nb] = __builtin_amdgcn_raw_buffer_load_b128(wrs, ok ? (uint32_t)(nb * KT + kt) * 1024u + lo : 0x80000000u,
                                                           0, 0);
       if constexpr (kNorm) {
-        // this lane's 8 elements k .. k + 7 of row rb * 16 + lane % 16, times gain and 1 / rms, to bf16
+        // this lane's elements k .. k + 7 of row rb * 16 + lane % 16, and their gains
         const int k = kt * 32 + (lane >> 4) * 8;
         const uint32_t go = ok ? (uint32_t)k * 4u : 0x80000000u;
-        const u32x4_t g0 = __builtin_amdgcn_raw_buffer_load_b128(grs, go, 0, 0);
-        const u32x4_t g1 = __builtin_amdgcn_raw_buffer_load_b128(grs, go + 16u, 0, 0);
+        ga[u][0] = __builtin_amdgcn_raw_buffer_load_b128(grs, go, 0, 0);
+        ga[u][1] = __builtin_amdgcn_raw_buffer_load_b128(grs, go + 16u, 0, 0);
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb) {
           const uint32_t xo = ok ? (uint32_t)((rb * 16 + (lane & 15)) * K + k) * 4u : 0x80000000u;
-          const u32x4_t x0 = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, 0, 0);
-          const u32x4_t x1 = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16u, 0, 0);
-          u32x4_t packed;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            packed[e] = pack_bf16x2(__uint_as_float(x0[2 * e]) * __uint_as_float(g0[2 * e]) * rinv[rb],
-                                    __uint_as_float(x0[2 * e + 1]) * __uint_as_float(g0[2 * e + 1]) * rinv[rb]);
-            packed[e + 2] = pack_bf16x2(__uint_as_float(x1[2 * e]) * __uint_as_float(g1[2 * e]) * rinv[rb],
-                                        __uint_as_float(x1[2 * e + 1]) * __uint_as_float(g1[2 * e + 1]) * rinv[rb]);
-          }
-          xv[u][rb] = packed;
+          xa[u][rb][0] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, 0, 0);
+          xa[u][rb][1] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16u, 0, 0);
         }
       } else {
 #pragma unroll
@@ -851,13 +850,29 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(XOp xop, const bf16_t*
               xrs, ok ? (uint32_t)(rb * KT + kt) * 1024u + lo : 0x80000000u, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      if constexpr (kNorm) {  // x * gain * (1 / rms), rounded to bf16
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+          u32x4_t packed;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              packed[2 * h + e] = pack_bf16x2(
+                  __uint_as_float(xa[u][rb][h][2 * e]) * __uint_as_float(ga[u][h][2 * e]) * rinv[rb],
+                  __uint_as_float(xa[u][rb][h][2 * e + 1]) * __uint_as_float(ga[u][h][2 * e + 1]) * rinv[rb]);
+          xv[u][rb] = packed;
+        }
+      }
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
           acc[rb][nb] = mfma_16x16x32_bf16(as_bf16x8(xv[u][rb]), as_bf16x8(wv[u][nb]), acc[rb][nb]);
+    }
   }
 
 #pragma unroll
@@ -869,15 +884,20 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(XOp xop, const bf16_t*
   __syncthreads();
 
   // thread -> column pair (p, p + 32) and rows rq, rq + 8, ...
-  constexpr int R = RW / 8;
+  constexpr int NR = NT / 32, R = RW / NR;  // row slots, rows per thread
   const int p = threadIdx.x & 31, rq = threadIdx.x >> 5;
   float v0[R], v1[R];
   int rows[R];
 #pragma unroll
   for (int q = 0; q < R; ++q) {
-    const int row = rq + 8 * q;
-    v0[q] = (red[0][row][p] + red[1][row][p]) + (red[2][row][p] + red[3][row][p]);
-    v1[q] = (red[0][row][p + 32] + red[1][row][p + 32]) + (red[2][row][p + 32] + red[3][row][p + 32]);
+    const int row = rq + NR * q;
+    v0[q] = 0.f;
+    v1[q] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      v0[q] += red[w][row][p];
+      v1[q] += red[w][row][p + 32];
+    }
     rows[q] = row < M ? row : -1;
   }
   if (nsplit > 1) {
@@ -889,8 +909,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(XOp xop, const bf16_t*
     float* mine = part + ((int64_t)g * nsplit + sp) * RW * 64;
 #pragma unroll
     for (int q = 0; q < R; ++q) {
-      __hip_atomic_store(mine + (rq + 8 * q) * 64 + p, v0[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(mine + (rq + 8 * q) * 64 + p + 32, v1[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mine + (rq + NR * q) * 64 + p, v0[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mine + (rq + NR * q) * 64 + p + 32, v1[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -912,7 +932,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(XOp xop, const bf16_t*
         const int t = t0 + u < nsplit ? t0 + u : t0;  // (surplus loads repeat t0, unused)
 #pragma unroll
         for (int q = 0; q < R; ++q) {
-          const float* at = all + (int64_t)t * RW * 64 + (rq + 8 * q) * 64 + p;
+          const float* at = all + (int64_t)t * RW * 64 + (rq + NR * q) * 64 + p;
           a0[u][q] = __hip_atomic_load(at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           a1[u][q] = __hip_atomic_load(at + 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -938,7 +958,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(XOp xop, const bf16_t*
       for (int q = 0; q < R; ++q) {
 #pragma unroll
         for (int o = 16; o > 0; o >>= 1) sq[q] += __shfl_xor(sq[q], o, 32);
-        if (p == 0) ssq_out[(int64_t)g * kSkinnyRows + rq + 8 * q] = sq[q];
+        if (p == 0) ssq_out[(int64_t)g * kSkinnyRows + rq + NR * q] = sq[q];
       }
       return;
     }
@@ -953,7 +973,7 @@ hipError_t launch_skinny(const XOp& xop, const void* W, int M, int N, int K, con
   const int MB = skinny_blocks(M);
   if (p.nsplit > 1 && ((int64_t)p.groups * p.nsplit * 16 * MB * 64 > sk.part_floats || p.groups > sk.count_len))
     return hipErrorInvalidValue;  // workspace sized for fewer rows or outputs
-  const dim3 grid(p.groups * p.nsplit), block(256);
+  const dim3 grid(p.groups * p.nsplit), block(64 * kSkWaves);
   const bf16_t* w = (const bf16_t*)W;
   switch (MB) {
     case 1:
