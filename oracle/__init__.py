@@ -23,10 +23,14 @@ from .forward import (  # noqa: F401
     embed,
     embed_scale,
     forward,
+    gated_ffn,
+    gelu_tanh,
     gemm,
     greedy,
     rmsnorm,
     rope,
+    rope_frequencies,
+    rotate,
     silu,
     softcap,
     swiglu,

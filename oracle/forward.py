@@ -11,6 +11,13 @@ Sources (page title, then the passage):
   [mg]  "N9 · metalgemm" — Theorem 1 (Y = X·Wᵀ with W[out, in]; reference GEMM is a
         float64-accumulated f32 triple loop; err/scale error model).
 
+  Architecture variants: [fp] Theorem statement names the family axes the forward
+  must cover (qwen3 QK-norm, gemma3 local/global attention with sandwich norm,
+  llama3 rope scaling, phi3 longrope) but gives no formula for them. Those functions
+  below follow the families' published definitions, each restated where it is used:
+  QK-norm, (1 + w) norm gains, the tanh-approximated GELU gate, a separate RoPE base
+  for local layers, the llama3 frequency bands and the longrope per-frequency factors.
+
 Every function takes float32 arrays, computes in float64 and returns float32.
 Where the pages leave a point open this file takes the plainest reading: rotate-half
 RoPE pairs, attention scale 1/sqrt(D), a window W keeps keys with 0 <= i - j < W,
@@ -94,31 +101,78 @@ def embed(E, ids, scale: float) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- normalisation
-def rmsnorm(x, w, eps: float) -> np.ndarray:
-    """y_i = x_i * w_i / sqrt(mean_j x_j^2 + eps) over the last axis — [fp] intro, [mg] intro."""
+def rmsnorm(x, w, eps: float, offset: float = 0.0) -> np.ndarray:
+    """y_i = x_i * (offset + w_i) / sqrt(mean_j x_j^2 + eps) over the last axis — [fp]
+    intro, [mg] intro. offset = 1 is the (1 + w) gain of the gemma3 family."""
     x64 = _f64(x)
     ms = np.mean(x64 * x64, axis=-1, keepdims=True)
-    return _f32(x64 / np.sqrt(ms + eps) * _f64(w))
+    return _f32(x64 / np.sqrt(ms + eps) * (offset + _f64(w)))
 
 
 # ---------------------------------------------------------------- rotary embedding
-def rope(x, positions, theta: float) -> np.ndarray:
-    """Rotary position embedding of x[..., S, nheads, D] — [fp] intro (RoPE).
-
-    Rotate-half pairing (the HF convention the forward-parity oracle exports): for
-    k in [0, D/2) the pair (x_k, x_{k+D/2}) at position p turns by the angle
-    p * theta^(-2k/D).
-    """
+def rotate(x, positions, inv_freq, mult: float = 1.0) -> np.ndarray:
+    """Rotary embedding of x[..., S, nheads, D] with per-pair frequencies inv_freq[D/2]
+    — [fp] intro (RoPE). Rotate-half pairing (the HF convention the forward-parity
+    oracle exports): the pair (x_k, x_{k+D/2}) at position p turns by p * inv_freq[k],
+    and both cos and sin carry the multiplier `mult` (1 except under longrope)."""
     x64 = _f64(x)
-    D = x64.shape[-1]
-    half = D // 2
-    k = np.arange(half, dtype=np.float64)
-    inv_freq = theta ** (-2.0 * k / D)
-    ang = _f64(positions)[:, None] * inv_freq[None, :]          # [S, D/2]
-    c = np.cos(ang)[:, None, :]
-    s = np.sin(ang)[:, None, :]
+    half = x64.shape[-1] // 2
+    ang = _f64(positions)[:, None] * _f64(inv_freq)[None, :]    # [S, D/2]
+    c = mult * np.cos(ang)[:, None, :]
+    s = mult * np.sin(ang)[:, None, :]
     a, b = x64[..., :half], x64[..., half:]
     return _f32(np.concatenate([a * c - b * s, a * s + b * c], axis=-1))
+
+
+def rope(x, positions, theta: float) -> np.ndarray:
+    """Plain RoPE: pair k turns by p * theta^(-2k/D) — [fp] intro (RoPE)."""
+    D = np.asarray(x).shape[-1]
+    k = np.arange(D // 2, dtype=np.float64)
+    return rotate(x, positions, theta ** (-2.0 * k / D))
+
+
+def rope_frequencies(cfg, kind: str, seq_len: int):
+    """(inv_freq [D/2] float64, multiplier) of a layer of `kind` in a forward whose
+    sequence is seq_len tokens long.
+
+    Family axes of [fp] Theorem statement, with the published definitions:
+    - base: rope_theta, or rope_theta_local on local layers when it is set (gemma3
+      local/global layers use different bases);
+    - "llama3" scaling of the base frequencies f_k = theta^(-2k/D), with wavelength
+      2 pi / f_k, original context L0, factors lo < hi and s: wavelengths below L0 / hi
+      keep f_k, wavelengths above L0 / lo become f_k / s, and in between
+      t = (L0 / wavelength - lo) / (hi - lo) blends them as (1 - t) f_k / s + t f_k;
+    - "longrope" (phi3): f_k = 1 / (e_k theta^(2k/D)) with e the long factors when the
+      sequence is longer than L0 and the short factors otherwise; cos and sin are
+      scaled by sqrt(1 + ln s / ln L0) when s = rope_factor > 1.
+    """
+    D = cfg.head_dim
+    theta = cfg.rope_theta
+    local_base = getattr(cfg, "rope_theta_local", 0.0)
+    if kind == "local" and local_base > 0:
+        theta = local_base
+    k = np.arange(D // 2, dtype=np.float64)
+    f = theta ** (-2.0 * k / D)
+    mode = getattr(cfg, "rope_scaling", "none")
+    if mode == "none":
+        return f, 1.0
+    L0 = float(cfg.rope_original_max_pos)
+    s = float(cfg.rope_factor)
+    if mode == "llama3":
+        lo, hi = float(cfg.rope_low_freq_factor), float(cfg.rope_high_freq_factor)
+        wavelen = 2.0 * math.pi / f
+        t = (L0 / wavelen - lo) / (hi - lo)
+        blended = (1.0 - t) * f / s + t * f
+        out = np.where(wavelen < L0 / hi, f, np.where(wavelen > L0 / lo, f / s, blended))
+        return out, 1.0
+    if mode == "longrope":
+        e = np.asarray(cfg.rope_long_factor if seq_len > L0 else cfg.rope_short_factor, dtype=np.float64)
+        if e.shape != (D // 2,):
+            raise ValueError("longrope factors need head_dim / 2 values")
+        out = 1.0 / (e * theta ** (2.0 * k / D))
+        mult = math.sqrt(1.0 + math.log(s) / math.log(L0)) if s > 1.0 else 1.0
+        return out, mult
+    raise ValueError(f"rope_scaling {mode!r}")
 
 
 # ---------------------------------------------------------------- attention
@@ -205,6 +259,22 @@ def swiglu(g, u) -> np.ndarray:
     return _f32(silu(g) * _f64(u))
 
 
+def gelu_tanh(z) -> np.ndarray:
+    """GELU in its tanh form, 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))), float64
+    (the gated FFN activation of the gemma3 family, published definition)."""
+    z64 = _f64(z)
+    return 0.5 * z64 * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z64 + 0.044715 * z64 ** 3)))
+
+
+def gated_ffn(g, u, act: str = "silu") -> np.ndarray:
+    """a = act(g) * u with act silu (SwiGLU) or gelu_tanh."""
+    if act == "silu":
+        return swiglu(g, u)
+    if act == "gelu_tanh":
+        return _f32(gelu_tanh(g) * _f64(u))
+    raise ValueError(f"ffn_act {act!r}")
+
+
 # ---------------------------------------------------------------- head
 def softcap(z, cap: float) -> np.ndarray:
     """z <- cap * tanh(z / cap) when cap > 0 — [pi] Description (final-logit softcap)."""
@@ -254,6 +324,9 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
         raise ValueError("norm_placement")
     kinds = cfg.kinds()
     positions = np.arange(S)
+    goff = float(getattr(cfg, "norm_gain_offset", 0))
+    act = getattr(cfg, "ffn_act", "silu")
+    qk_norm = bool(getattr(cfg, "qk_norm", False))
 
     E = weights["embed"]
     x = embed(E, ids, embed_scale(cfg.embed_scale_mode, H))            # [B, S, H]
@@ -266,29 +339,33 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
         p = f"layers.{l}."
         window = cfg.sliding_window if kinds[l] == "local" else 0
         # attention sublayer
-        n = rb(rmsnorm(x, weights[p + "attn_norm"], eps))
+        n = rb(rmsnorm(x, weights[p + "attn_norm"], eps, goff))
         q = gemm(n, weights[p + "wq"]).reshape(B, S, Hq, D)
         k = gemm(n, weights[p + "wk"]).reshape(B, S, Hkv, D)
         v = rb(gemm(n, weights[p + "wv"]).reshape(B, S, Hkv, D))
-        q = rb(np.stack([rope(q[b], positions, cfg.rope_theta) for b in range(B)]))
-        k = rb(np.stack([rope(k[b], positions, cfg.rope_theta) for b in range(B)]))
+        if qk_norm:  # each head's q and k normalised over its D dims, before RoPE (qwen3 / gemma3)
+            q = rmsnorm(rb(q), weights[p + "q_norm"], eps, goff)
+            k = rmsnorm(rb(k), weights[p + "k_norm"], eps, goff)
+        f, mult = rope_frequencies(cfg, kinds[l], S)
+        q = rb(np.stack([rotate(q[b], positions, f, mult) for b in range(B)]))
+        k = rb(np.stack([rotate(k[b], positions, f, mult) for b in range(B)]))
         o = rb(_attention_rounded(q, k, v, window) if bf16_points else attention(q, k, v, window))
         o = o.reshape(B, S, Hq * D)
         u = gemm(o, weights[p + "wo"])
         if sandwich:
-            u = rmsnorm(u, weights[p + "post_attn_norm"], eps)
+            u = rmsnorm(u, weights[p + "post_attn_norm"], eps, goff)
         x = _f32(_f64(x) + _f64(u))
         # feed-forward sublayer
-        n = rb(rmsnorm(x, weights[p + "ffn_norm"], eps))
-        a = rb(swiglu(gemm(n, weights[p + "w_gate"]), gemm(n, weights[p + "w_up"])))
+        n = rb(rmsnorm(x, weights[p + "ffn_norm"], eps, goff))
+        a = rb(gated_ffn(gemm(n, weights[p + "w_gate"]), gemm(n, weights[p + "w_up"]), act))
         d = gemm(a, weights[p + "w_down"])
         if sandwich:
-            d = rmsnorm(d, weights[p + "post_ffn_norm"], eps)
+            d = rmsnorm(d, weights[p + "post_ffn_norm"], eps, goff)
         x = _f32(_f64(x) + _f64(d))
         if want_hidden:
             hidden[l + 1] = x
 
-    h = rmsnorm(x, weights["final_norm"], eps)
+    h = rmsnorm(x, weights["final_norm"], eps, goff)
     if want_hidden:
         hidden[L + 1] = h
     if not want_logits:                          # hidden slots only: the head is not needed

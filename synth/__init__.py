@@ -101,6 +101,12 @@ def raw_bits(seed: int, name: str, n: int, offset: int = 0) -> np.ndarray:
     return out
 
 
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> uint16 bf16 bits, round to nearest, ties to even (finite inputs)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float32."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)

@@ -21,7 +21,7 @@ from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
-from . import SEED_GEMM, SEED_IDS, SEED_WEIGHTS, WEIGHT_SIGMA, bf16_bits_to_f32, normal, token_ids
+from . import SEED_GEMM, SEED_IDS, SEED_WEIGHTS, WEIGHT_SIGMA, bf16_bits_to_f32, normal, to_bf16_bits, token_ids
 
 
 @dataclasses.dataclass(frozen=True)
@@ -44,6 +44,20 @@ class ModelConfig:
     dtype: str = "bf16"                   # "f32" | "bf16"
     batch: int = 1
     seq: int = 16
+    # architecture variants (family axes: QK-norm, (1 + w) gains, gated-GELU FFN,
+    # per-kind RoPE base, RoPE frequency scaling)
+    qk_norm: bool = False                 # RMSNorm over each q and k head (gains q_norm / k_norm [D])
+    norm_gain_offset: int = 0             # 0: norms scale by w; 1: by (1 + w)
+    ffn_act: str = "silu"                 # "silu" | "gelu_tanh"
+    rope_theta_local: float = 0.0         # RoPE base of local layers (0 = rope_theta)
+    rope_scaling: str = "none"            # "none" | "llama3" | "longrope"
+    rope_factor: float = 1.0
+    rope_low_freq_factor: float = 1.0     # llama3
+    rope_high_freq_factor: float = 4.0    # llama3
+    rope_original_max_pos: int = 0        # llama3 / longrope
+    rope_short_factor: Tuple[float, ...] = ()  # longrope, D / 2 values
+    rope_long_factor: Tuple[float, ...] = ()   # longrope, D / 2 values
+    gain_sigma: float = 0.0               # > 0: norm gains drawn as neutral + N(0, sigma^2)
 
     def kinds(self) -> Tuple[str, ...]:
         return self.layer_kind if self.layer_kind else ("global",) * self.n_layers
@@ -91,6 +105,9 @@ def weight_shapes(cfg: ModelConfig) -> Dict[str, Tuple[Tuple[int, ...], str]]:
         if cfg.norm_placement == "sandwich":
             out[p + "post_attn_norm"] = ((H,), "gain")
             out[p + "post_ffn_norm"] = ((H,), "gain")
+        if cfg.qk_norm:
+            out[p + "q_norm"] = ((D,), "gain")
+            out[p + "k_norm"] = ((D,), "gain")
     return out
 
 
@@ -98,8 +115,13 @@ def draw_weight(cfg: ModelConfig, name: str, seed: int = SEED_WEIGHTS) -> np.nda
     """One weight tensor in the config's storage type: float32, or uint16 bf16 bits."""
     shape, kind = weight_shapes(cfg)[name]
     if kind == "gain":
-        one = np.ones(shape, dtype=np.float32)
-        return one if cfg.dtype == "f32" else (one.view(np.uint32) >> 16).astype(np.uint16)
+        # the neutral gain is 1 (or 0 when norms scale by 1 + w); gain_sigma > 0 spreads it
+        neutral = 0.0 if cfg.norm_gain_offset else 1.0
+        if cfg.gain_sigma > 0:
+            g = normal(seed, name, shape, cfg.gain_sigma, "f32") + np.float32(neutral)
+        else:
+            g = np.full(shape, neutral, dtype=np.float32)
+        return g if cfg.dtype == "f32" else to_bf16_bits(g)
     return normal(seed, name, shape, WEIGHT_SIGMA, cfg.dtype)
 
 

@@ -414,3 +414,140 @@ def test_greedy_steps_are_cacheless_forwards():
         one, one_logits = oracle.greedy(TINY, w, ids[b:b + 1], 4)
         assert np.array_equal(one[0], toks[b])
         assert np.allclose(one_logits[:, 0], logits[:, b], rtol=0, atol=1e-6)
+
+
+# ---------------------------------------------------------------- architecture variants
+# [fp] Theorem statement names the family axes (qwen3 QK-norm, gemma3 local/global,
+# llama3 rope scaling, phi3 longrope) without formulas; these pins fix the structure
+# of the published definitions the oracle restates.
+
+def _llama3_cfg(**kw):
+    base = dict(rope_theta=500000.0, rope_scaling="llama3", rope_factor=8.0, rope_low_freq_factor=1.0,
+                rope_high_freq_factor=4.0, rope_original_max_pos=8192)
+    base.update(kw)
+    return wl.LLAMA3_8B.replace(**base)
+
+
+def test_llama3_scaling_bands():
+    cfg = _llama3_cfg()
+    D = cfg.head_dim
+    plain = 500000.0 ** (-2.0 * np.arange(D // 2) / D)
+    f, mult = oracle.rope_frequencies(cfg, "global", 16)
+    assert mult == 1.0
+    wavelen = 2 * math.pi / plain
+    hi_band = wavelen < 8192 / 4.0
+    lo_band = wavelen > 8192 / 1.0
+    mid = ~hi_band & ~lo_band
+    assert hi_band.any() and lo_band.any() and mid.any()     # all three bands occur at D = 128
+    assert np.array_equal(f[hi_band], plain[hi_band])        # short wavelengths untouched
+    np.testing.assert_allclose(f[lo_band], plain[lo_band] / 8.0, rtol=1e-15)
+    assert np.all(f[mid] < plain[mid]) and np.all(f[mid] > plain[mid] / 8.0)
+    assert np.all(np.diff(f) < 0)                            # still strictly decreasing in k
+    # continuity at both band edges: move the edges onto a pair and compare the limits
+    k_edge = int(np.argmax(mid))                             # first blended pair
+    for L0 in (wavelen[k_edge] * 4.0, wavelen[k_edge] * 1.0):
+        a, _ = oracle.rope_frequencies(_llama3_cfg(rope_original_max_pos=L0 * (1 + 1e-12)), "global", 16)
+        b, _ = oracle.rope_frequencies(_llama3_cfg(rope_original_max_pos=L0 * (1 - 1e-12)), "global", 16)
+        assert abs(a[k_edge] - b[k_edge]) <= 1e-9 * plain[k_edge]
+    # factor 1 is the plain RoPE
+    g, _ = oracle.rope_frequencies(_llama3_cfg(rope_factor=1.0), "global", 16)
+    np.testing.assert_allclose(g, plain, rtol=1e-15)
+
+
+def test_longrope_factors_divide_each_frequency_and_switch_at_l0():
+    D, L0 = 16, 64
+    rng = np.random.default_rng(3)
+    short = tuple(float(v) for v in rng.uniform(1.0, 3.0, D // 2))
+    long = tuple(float(v) for v in rng.uniform(2.0, 9.0, D // 2))
+    cfg = wl.TINY_F32.replace(rope_scaling="longrope", rope_factor=4.0, rope_original_max_pos=L0,
+                              rope_short_factor=short, rope_long_factor=long)
+    fs, m_s = oracle.rope_frequencies(cfg, "global", L0)
+    fl, m_l = oracle.rope_frequencies(cfg, "global", L0 + 1)
+    plain = 10000.0 ** (-2.0 * np.arange(D // 2) / D)
+    np.testing.assert_allclose(fs, plain / np.array(short), rtol=1e-14)
+    np.testing.assert_allclose(fl, plain / np.array(long), rtol=1e-14)
+    assert m_s == m_l == pytest.approx(math.sqrt(1 + math.log(4.0) / math.log(L0)), rel=1e-15)
+    # pair k rotated at position p equals the plain rotation at position p / e_k
+    x = rng.standard_normal((1, 1, D)).astype(np.float32)
+    p = 37
+    got = oracle.rotate(x, np.array([p]), fs, 1.0)
+    for k in range(D // 2):
+        ref = oracle.rope(x, np.array([p / short[k]]), 10000.0)
+        assert got[0, 0, k] == pytest.approx(ref[0, 0, k], abs=1e-6)
+        assert got[0, 0, k + D // 2] == pytest.approx(ref[0, 0, k + D // 2], abs=1e-6)
+    # the multiplier scales each pair's norm by mult
+    y = oracle.rotate(x, np.array([p]), fs, m_s).astype(np.float64)[0, 0]
+    x64 = x.astype(np.float64)[0, 0]
+    for k in range(D // 2):
+        n_in = math.hypot(x64[k], x64[k + D // 2])
+        assert math.hypot(y[k], y[k + D // 2]) == pytest.approx(m_s * n_in, rel=1e-6)
+    # no extension (s <= 1) means no multiplier
+    _, m1 = oracle.rope_frequencies(cfg.replace(rope_factor=1.0), "global", 8)
+    assert m1 == 1.0
+
+
+def test_local_rope_base_applies_to_local_layers_only():
+    cfg = wl.TINY_F32.replace(rope_theta=1e6, rope_theta_local=1e4)
+    D = cfg.head_dim
+    fg, _ = oracle.rope_frequencies(cfg, "global", 8)
+    fl, _ = oracle.rope_frequencies(cfg, "local", 8)
+    k = np.arange(D // 2)
+    np.testing.assert_allclose(fg, 1e6 ** (-2.0 * k / D), rtol=1e-15)
+    np.testing.assert_allclose(fl, 1e4 ** (-2.0 * k / D), rtol=1e-15)
+    same, _ = oracle.rope_frequencies(cfg.replace(rope_theta_local=0.0), "local", 8)
+    np.testing.assert_allclose(same, fg, rtol=1e-15)
+
+
+def _f32_weights(cfg):
+    return {n: np.asarray(a, np.float32) for n, a in wl.draw_all(cfg).items()}
+
+
+def test_qk_norm_makes_the_forward_invariant_to_query_and_key_scale():
+    cfg = wl.TINY_F32.replace(qk_norm=True, gain_sigma=0.2, rms_eps=1e-12, name="tiny-qknorm")
+    w = _f32_weights(cfg)
+    ids = wl.draw_ids(cfg)
+    base = oracle.forward(cfg, w, ids)["logits"]
+    w2 = dict(w)
+    for l in range(cfg.n_layers):
+        w2[f"layers.{l}.wq"] = w[f"layers.{l}.wq"] * np.float32(4.0)
+        w2[f"layers.{l}.wk"] = w[f"layers.{l}.wk"] * np.float32(0.5)
+    np.testing.assert_allclose(oracle.forward(cfg, w2, ids)["logits"], base, rtol=0, atol=2e-6)
+    # without QK-norm the same scaling changes the scores (non-vacuous)
+    plain = cfg.replace(qk_norm=False)
+    wp = {n: a for n, a in w.items() if "q_norm" not in n and "k_norm" not in n}
+    wp2 = {n: a for n, a in w2.items() if "q_norm" not in n and "k_norm" not in n}
+    d = np.abs(oracle.forward(plain, wp2, ids)["logits"] - oracle.forward(plain, wp, ids)["logits"]).max()
+    assert d > 1e-3
+    # the q / k gains matter: unit gains give a different forward
+    w3 = dict(w)
+    for l in range(cfg.n_layers):
+        w3[f"layers.{l}.q_norm"] = np.ones_like(w[f"layers.{l}.q_norm"])
+    assert np.abs(oracle.forward(cfg, w3, ids)["logits"] - base).max() > 1e-4
+
+
+def test_gain_offset_equals_explicit_one_plus_w():
+    cfg = wl.TINY_F32.replace(norm_gain_offset=1, gain_sigma=0.3, qk_norm=True, norm_placement="sandwich",
+                              name="tiny-offset")
+    w = _f32_weights(cfg)
+    ids = wl.draw_ids(cfg)
+    got = oracle.forward(cfg, w, ids)
+    explicit = {n: (np.float64(1.0) + a.astype(np.float64)).astype(np.float32) if a.ndim == 1 else a
+                for n, a in w.items()}
+    ref = oracle.forward(cfg.replace(norm_gain_offset=0), explicit, ids)
+    for s in range(cfg.n_layers + 2):
+        np.testing.assert_allclose(got["hidden"][s], ref["hidden"][s], rtol=1e-6, atol=1e-6)
+
+
+def test_gelu_tanh_closed_forms_and_gate():
+    z = np.linspace(-8, 8, 3201)
+    g = oracle.gelu_tanh(z)
+    np.testing.assert_allclose(g - oracle.gelu_tanh(-z), z, atol=1e-12)   # odd part is z / 2
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+    erf_gelu = 0.5 * z * (1 + np.array([math.erf(v / math.sqrt(2)) for v in z]))
+    assert np.abs(g - erf_gelu).max() < 1e-3                            # tanh approximation of GELU
+    assert oracle.gelu_tanh(np.array([30.0]))[0] == pytest.approx(30.0)
+    # the gated FFN multiplies by the up projection and is not symmetric in (g, u)
+    a = oracle.gated_ffn(np.array([1.5], np.float32), np.array([-2.0], np.float32), "gelu_tanh")
+    assert a[0] == pytest.approx(float(oracle.gelu_tanh(np.array([1.5]))[0]) * -2.0, rel=1e-6)
+    b = oracle.gated_ffn(np.array([-2.0], np.float32), np.array([1.5], np.float32), "gelu_tanh")
+    assert abs(a[0] - b[0]) > 0.1
