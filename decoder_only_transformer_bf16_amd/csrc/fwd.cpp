@@ -79,13 +79,36 @@ int check_config(const fwd_config* c) {
       if (c->layer_kind[l] != FWD_LAYER_GLOBAL && c->layer_kind[l] != FWD_LAYER_LOCAL)
         return fail(FWD_E_CONFIG, "layer_kind entries must be FWD_LAYER_GLOBAL or FWD_LAYER_LOCAL");
   if (c->max_tokens <= 0) return fail(FWD_E_CONFIG, "max_tokens must be positive");
+  if ((c->qk_norm != 0 && c->qk_norm != 1) || (c->norm_gain_offset != 0 && c->norm_gain_offset != 1))
+    return fail(FWD_E_CONFIG, "qk_norm and norm_gain_offset must be 0 or 1");
+  if (c->ffn_act != FWD_FFN_SILU && c->ffn_act != FWD_FFN_GELU_TANH) return fail(FWD_E_CONFIG, "ffn_act");
+  if (c->rope_theta_local != 0.0 && (!(c->rope_theta_local > 1.0) || !std::isfinite(c->rope_theta_local)))
+    return fail(FWD_E_CONFIG, "rope_theta_local must be > 1, or 0 for rope_theta");
+  if (c->rope_scaling != FWD_ROPE_NONE) {
+    if (c->rope_scaling != FWD_ROPE_LLAMA3 && c->rope_scaling != FWD_ROPE_LONGROPE)
+      return fail(FWD_E_CONFIG, "rope_scaling");
+    if (!(c->rope_factor > 0.f) || !std::isfinite(c->rope_factor) || c->rope_original_max_pos <= 0)
+      return fail(FWD_E_CONFIG, "rope scaling needs rope_factor > 0 and rope_original_max_pos > 0");
+    if (c->rope_scaling == FWD_ROPE_LLAMA3 &&
+        !(c->rope_low_freq_factor > 0.f && c->rope_high_freq_factor > c->rope_low_freq_factor &&
+          std::isfinite(c->rope_high_freq_factor)))
+      return fail(FWD_E_CONFIG, "llama3 rope scaling needs 0 < rope_low_freq_factor < rope_high_freq_factor");
+    if (c->rope_scaling == FWD_ROPE_LONGROPE) {
+      if (!c->rope_short_factor || !c->rope_long_factor)
+        return fail(FWD_E_CONFIG, "longrope needs rope_short_factor and rope_long_factor");
+      for (int k = 0; k < c->head_dim / 2; ++k)
+        if (!(c->rope_short_factor[k] > 0.f) || !(c->rope_long_factor[k] > 0.f) ||
+            !std::isfinite(c->rope_short_factor[k]) || !std::isfinite(c->rope_long_factor[k]))
+          return fail(FWD_E_CONFIG, "longrope factors must be positive and finite");
+    }
+  }
   return FWD_OK;
 }
 
 // bf16 GEMM operands (weights, normalised activations, attention and SwiGLU
 // outputs) are kept K-tiled (16 x 32 tiles, rows padded to 16); f32 is row-major.
 struct Geometry {
-  int64_t esize, H, Hq, Hkv, D, F, V, L, T, qkv_rows, logit_chunk;
+  int64_t esize, H, Hq, Hkv, D, F, V, L, T, qkv_rows, logit_chunk, rope_tables;
   bool tiled;
   int64_t rows(int64_t r) const { return tiled ? round_up(r, 16) : r; }  // allocated rows of an operand
   int64_t weight_bytes() const {
@@ -105,7 +128,7 @@ struct Geometry {
     if (sandwich) w += r(T * H * 4);                    // sublayer output before its norm
     w += r(T * 4) + r(T * 4) + 256;                     // ids, argmax, flag
     w += r(logit_chunk * V * 4);                        // logits when the caller wants none
-    w += r(T * (D / 2) * 8);                            // RoPE cos/sin table
+    w += rope_tables * r(T * (D / 2) * 8);              // RoPE cos/sin tables
     if (tiled) w += r(skinny_part_floats() * 4) + r(skinny_counters() * 4) + r(fwdk::skinny_groups((int)H) * 64 * 4);
     return w;
   }
@@ -135,6 +158,10 @@ Geometry geometry(const fwd_config* c) {
   g.qkv_rows = (g.Hq + 2 * g.Hkv) * g.D;
   g.logit_chunk = std::min<int64_t>(g.T, 1024);  // a multiple of 16 whenever it splits T
   g.tiled = c->dtype == FWD_DTYPE_BF16;
+  bool any_local = false;
+  for (int l = 0; c->layer_kind && l < c->n_layers; ++l) any_local |= c->layer_kind[l] == FWD_LAYER_LOCAL;
+  g.rope_tables = (any_local && c->rope_theta_local > 0.0 && c->rope_theta_local != c->rope_theta ? 2 : 1) *
+                  (c->rope_scaling == FWD_ROPE_LONGROPE ? 2 : 1);
   return g;
 }
 
@@ -152,7 +179,7 @@ struct fwd_model {
   void* embed = nullptr;
   float* final_norm = nullptr;
   struct Layer {
-    float *attn_norm, *ffn_norm, *post_attn, *post_ffn;
+    float *attn_norm, *ffn_norm, *post_attn, *post_ffn, *q_norm, *k_norm;
     void *wqkv, *wo, *wgu, *wdown;
   };
   std::vector<Layer> layers;
@@ -169,7 +196,8 @@ struct fwd_model {
   int32_t* amax = nullptr;
   int* flag = nullptr;
   float* logits_ws = nullptr;
-  float2* rope_cs = nullptr;
+  float2* rope_tab[4] = {};  // [2 * local + long factors]: RoPE (cos, sin) tables of max_tokens rows
+  std::vector<float> rope_short, rope_long;  // longrope factors (the config's arrays are borrowed)
   fwdk::SplitK sk{};  // workspace of the few-row products (bf16)
   float* ssq = nullptr;  // [H / 64][kSkinnyRows] row sums of squares left by a few-row residual product
 
@@ -242,7 +270,7 @@ struct fwd_session {
   int64_t layer_bytes = 0;
   float* part = nullptr;
   unsigned* count = nullptr;  // [Bmax, Hkv] arrival counters of the decode attention
-  float2* rope = nullptr;  // [Smax, D / 2]
+  float2* rope_tab[4] = {};   // as the model's, [Smax, D / 2] each
   ~fwd_session() {
     if (m && m->stream) (void)hipStreamSynchronize(m->stream);
     else (void)hipDeviceSynchronize();
@@ -252,22 +280,68 @@ struct fwd_session {
 
 namespace {
 
-// RoPE (cos, sin) table [rows, D/2]: angle(t, k) = t * theta^(-2k/D), computed in
-// double on the host ("N7 · model/forward-parity", intro: RoPE).
-int rope_table(fwd_model* m, float2** out, int64_t rows, std::vector<void*>& owner) {
-  const int64_t D = m->g.D;
-  std::vector<float2> cs((size_t)rows * (D / 2));
-  for (int64_t t = 0; t < rows; ++t)
-    for (int64_t k = 0; k < D / 2; ++k) {
-      const double ang = (double)t * std::pow(m->cfg.rope_theta, -2.0 * (double)k / (double)D);
-      cs[(size_t)t * (D / 2) + k] = float2{(float)std::cos(ang), (float)std::sin(ang)};
+// RoPE (cos, sin) tables [rows, D/2] for one layer kind and longrope factor set:
+// angle(t, k) = t * f_k with f_k from the base (rope_theta, or rope_theta_local on
+// local layers) and the scaling of the config, both entries times the longrope
+// multiplier; computed in double on the host ("N7 · model/forward-parity", intro:
+// RoPE; Theorem statement: llama3 rope scaling, phi3 longrope, gemma3 local layers).
+std::vector<double> rope_frequencies(const fwd_model* m, bool local, bool long_set, double* mult) {
+  const fwd_config& c = m->cfg;
+  const int64_t D = m->g.D, half = D / 2;
+  const double theta = local && c.rope_theta_local > 0.0 ? c.rope_theta_local : c.rope_theta;
+  std::vector<double> f(half);
+  for (int64_t k = 0; k < half; ++k) f[k] = std::pow(theta, -2.0 * (double)k / (double)D);
+  *mult = 1.0;
+  if (c.rope_scaling == FWD_ROPE_LLAMA3) {
+    const double L0 = c.rope_original_max_pos, s = c.rope_factor;
+    const double lo = c.rope_low_freq_factor, hi = c.rope_high_freq_factor;
+    for (double& fk : f) {
+      const double wavelen = 2.0 * M_PI / fk;
+      if (wavelen < L0 / hi) continue;  // high frequencies unchanged
+      if (wavelen > L0 / lo) {
+        fk /= s;
+      } else {
+        const double t = (L0 / wavelen - lo) / (hi - lo);
+        fk = (1.0 - t) * fk / s + t * fk;
+      }
     }
-  void* p = nullptr;
-  HIP_TRY(hipMalloc(&p, (size_t)round_up((int64_t)cs.size() * 8, 256)));
-  owner.push_back(p);
-  *out = (float2*)p;
-  HIP_TRY(hipMemcpyAsync(p, cs.data(), cs.size() * 8, hipMemcpyHostToDevice, m->stream));
-  HIP_TRY(hipStreamSynchronize(m->stream));  // the host table dies at scope end
+  } else if (c.rope_scaling == FWD_ROPE_LONGROPE) {
+    const std::vector<float>& e = long_set ? m->rope_long : m->rope_short;
+    for (int64_t k = 0; k < half; ++k) f[k] = 1.0 / ((double)e[k] * std::pow(theta, 2.0 * (double)k / (double)D));
+    const double s = c.rope_factor;
+    if (s > 1.0) *mult = std::sqrt(1.0 + std::log(s) / std::log((double)c.rope_original_max_pos));
+  }
+  return f;
+}
+
+int rope_tables(fwd_model* m, float2* (&out)[4], int64_t rows, std::vector<void*>& owner) {
+  const int64_t half = m->g.D / 2;
+  bool any_local = false;
+  for (int32_t k : m->kinds) any_local |= k == FWD_LAYER_LOCAL;
+  const bool two_bases = any_local && m->cfg.rope_theta_local > 0.0 && m->cfg.rope_theta_local != m->cfg.rope_theta;
+  const bool two_sets = m->cfg.rope_scaling == FWD_ROPE_LONGROPE;
+  for (int i = 0; i < 4; ++i) out[i] = nullptr;
+  for (int local = 0; local < (two_bases ? 2 : 1); ++local)
+    for (int set = 0; set < (two_sets ? 2 : 1); ++set) {
+      double mult = 1.0;
+      const std::vector<double> f = rope_frequencies(m, local, set, &mult);
+      std::vector<float2> cs((size_t)rows * half);
+      for (int64_t t = 0; t < rows; ++t)
+        for (int64_t k = 0; k < half; ++k) {
+          const double ang = (double)t * f[k];
+          cs[(size_t)t * half + k] = float2{(float)(mult * std::cos(ang)), (float)(mult * std::sin(ang))};
+        }
+      void* p = nullptr;
+      HIP_TRY(hipMalloc(&p, (size_t)round_up((int64_t)cs.size() * 8, 256)));
+      owner.push_back(p);
+      out[2 * local + set] = (float2*)p;
+      HIP_TRY(hipMemcpyAsync(p, cs.data(), cs.size() * 8, hipMemcpyHostToDevice, m->stream));
+      HIP_TRY(hipStreamSynchronize(m->stream));  // the host table dies at scope end
+    }
+  // a kind or set without a table of its own uses the one it equals
+  for (int local = 0; local < 2; ++local)
+    for (int set = 0; set < 2; ++set)
+      if (!out[2 * local + set]) out[2 * local + set] = out[2 * (two_bases ? local : 0) + (two_sets ? set : 0)];
   return FWD_OK;
 }
 
@@ -340,7 +414,7 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
   for (int l = 0; l < cfg->n_layers; ++l) {
     const fwd_layer_weights& L = w->layers[l];
     if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.ffn_norm || !L.w_gate || !L.w_up || !L.w_down ||
-        (sandwich && (!L.post_attn_norm || !L.post_ffn_norm)))
+        (sandwich && (!L.post_attn_norm || !L.post_ffn_norm)) || (cfg->qk_norm && (!L.q_norm || !L.k_norm)))
       return fail(FWD_E_WEIGHTS, "layer " + std::to_string(l) + " is missing a weight pointer");
   }
   if (!device_is_gfx950()) return fail(FWD_E_UNAVAILABLE, "no gfx950 device is available");
@@ -350,6 +424,11 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
   m->kinds.assign(cfg->n_layers, FWD_LAYER_GLOBAL);
   if (cfg->layer_kind) m->kinds.assign(cfg->layer_kind, cfg->layer_kind + cfg->n_layers);
   m->cfg.layer_kind = nullptr;
+  if (cfg->rope_scaling == FWD_ROPE_LONGROPE) {
+    m->rope_short.assign(cfg->rope_short_factor, cfg->rope_short_factor + cfg->head_dim / 2);
+    m->rope_long.assign(cfg->rope_long_factor, cfg->rope_long_factor + cfg->head_dim / 2);
+  }
+  m->cfg.rope_short_factor = m->cfg.rope_long_factor = nullptr;
   m->dt = DType(cfg->dtype);
   m->g = geometry(cfg);
   m->stream = (hipStream_t)hip_stream;
@@ -397,7 +476,8 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     if (int rc = alloc_operand(&m->embed, g.V, g.H)) return rc;
     if (int rc = place(m->embed, g.V, w->embed, mid, (int)g.V, g.H)) return rc;
     if (int rc = m->alloc((void**)&m->final_norm, g.H * 4)) return rc;
-    HIP_TRY(fwdk::gains_to_f32(m->dt, w->final_norm, m->final_norm, (int)g.H, s));
+    const float goff = (float)cfg->norm_gain_offset;
+    HIP_TRY(fwdk::gains_to_f32(m->dt, w->final_norm, m->final_norm, (int)g.H, goff, s));
 
     m->layers.resize(g.L);
     for (int l = 0; l < g.L; ++l) {
@@ -406,13 +486,19 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
       L = fwd_model::Layer{};
       if (int rc = m->alloc((void**)&L.attn_norm, g.H * 4)) return rc;
       if (int rc = m->alloc((void**)&L.ffn_norm, g.H * 4)) return rc;
-      HIP_TRY(fwdk::gains_to_f32(m->dt, W.attn_norm, L.attn_norm, (int)g.H, s));
-      HIP_TRY(fwdk::gains_to_f32(m->dt, W.ffn_norm, L.ffn_norm, (int)g.H, s));
+      HIP_TRY(fwdk::gains_to_f32(m->dt, W.attn_norm, L.attn_norm, (int)g.H, goff, s));
+      HIP_TRY(fwdk::gains_to_f32(m->dt, W.ffn_norm, L.ffn_norm, (int)g.H, goff, s));
+      if (cfg->qk_norm) {
+        if (int rc = m->alloc((void**)&L.q_norm, g.D * 4)) return rc;
+        if (int rc = m->alloc((void**)&L.k_norm, g.D * 4)) return rc;
+        HIP_TRY(fwdk::gains_to_f32(m->dt, W.q_norm, L.q_norm, (int)g.D, goff, s));
+        HIP_TRY(fwdk::gains_to_f32(m->dt, W.k_norm, L.k_norm, (int)g.D, goff, s));
+      }
       if (sandwich) {
         if (int rc = m->alloc((void**)&L.post_attn, g.H * 4)) return rc;
         if (int rc = m->alloc((void**)&L.post_ffn, g.H * 4)) return rc;
-        HIP_TRY(fwdk::gains_to_f32(m->dt, W.post_attn_norm, L.post_attn, (int)g.H, s));
-        HIP_TRY(fwdk::gains_to_f32(m->dt, W.post_ffn_norm, L.post_ffn, (int)g.H, s));
+        HIP_TRY(fwdk::gains_to_f32(m->dt, W.post_attn_norm, L.post_attn, (int)g.H, goff, s));
+        HIP_TRY(fwdk::gains_to_f32(m->dt, W.post_ffn_norm, L.post_ffn, (int)g.H, goff, s));
       }
       if (int rc = alloc_operand(&L.wqkv, g.qkv_rows, g.H)) return rc;
       if (g.tiled) HIP_TRY(hipMemsetAsync(L.wqkv, 0, g.rows(g.qkv_rows) * g.H * g.esize, s));
@@ -437,7 +523,7 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     HIP_TRY(hipStreamSynchronize(s));  // the row maps are freed at scope end
 
     // ---- RoPE table ----
-    if (int rc = rope_table(m, &m->rope_cs, g.T, m->allocs)) return rc;
+    if (int rc = rope_tables(m, m->rope_tab, g.T, m->allocs)) return rc;
 
     // ---- workspace ----
     const int64_t T = g.T;
@@ -515,6 +601,10 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
   // of squares, and the next product normalises its input itself (no norm launches
   // after the first).
   const bool fuse = tl && M <= fwdk::kSkinnyRows && !sandwich && !hidden && L > 0;
+  // RoPE tables of this call: per layer kind, and the longrope factor set its length selects
+  float2* const* rope_tabs = sess ? sess->rope_tab : m->rope_tab;
+  const int rope_set =
+      m->cfg.rope_scaling == FWD_ROPE_LONGROPE && (int64_t)pos0 + S > m->cfg.rope_original_max_pos ? 1 : 0;
   const int ngroups = (int)fwdk::skinny_groups(H);
   auto normx = [&](const float* x, const float* w) { return fwdk::RowNormX{x, w, m->ssq, ngroups, eps}; };
 
@@ -529,15 +619,25 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
     const float* next_norm = last ? m->final_norm : m->layers[l + 1].attn_norm;
 
     // attention sublayer (its input norm is already in m->n)
-    // with a session, the epilogue also stores the rotated keys and the values in the cache
+    // with a session, the rotated keys and the values are also stored in the cache: by
+    // the QKV epilogue, or with QK-norm by the pass that normalises and rotates
     void* kc = sess ? sess->kc + l * sess->layer_bytes : nullptr;
     void* vc = sess ? sess->vc + l * sess->layer_bytes : nullptr;
-    fwdk::RopeArgs ra{m->qk, sess ? sess->rope : m->rope_cs, Hq, Hkv, D, S, pos0, kc, vc, sess ? sess->Smax : 0};
+    const bool local = m->kinds[l] == FWD_LAYER_LOCAL;
+    const float2* cs = rope_tabs[2 * (local ? 1 : 0) + rope_set];
+    const bool qkn = m->cfg.qk_norm != 0;
+    fwdk::RopeArgs ra{m->qk, cs, Hq, Hkv, D, S, pos0, qkn ? nullptr : kc, qkn ? nullptr : vc,
+                      sess && !qkn ? sess->Smax : 0, !qkn};
     const fwdk::RowNormX nq = normx(xin, w.attn_norm);
     TIMED(m, FWD_KERNEL_QKV_ROPE,
           fwdk::gemm_qkv_rope(dt, m->n, w.wqkv, ra, M, H, tl, s, sk, fuse && l > 0 ? &nq : nullptr));
     const int64_t ldqkv = (int64_t)(Hq + 2 * Hkv) * D;
-    const int window = m->kinds[l] == FWD_LAYER_LOCAL ? m->cfg.sliding_window : 0;
+    if (qkn) {
+      fwdk::QkNormArgs qa{m->qk, ldqkv, Hq, Hkv, D, S, pos0, cs, w.q_norm, w.k_norm, eps, kc, vc,
+                          sess ? sess->Smax : 0};
+      TIMED(m, FWD_KERNEL_QK_NORM, fwdk::qk_norm_rope(dt, qa, M, s));
+    }
+    const int window = local ? m->cfg.sliding_window : 0;
     if (sess) {
       if (decode) {
         TIMED(m, FWD_KERNEL_ATTENTION, fwdk::attention_decode(dt, qk, ldqkv, kc, vc, sess->Smax, pos0 + 1, B, Hq, Hkv,
@@ -577,7 +677,8 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
 
     // feed-forward sublayer
     const fwdk::RowNormX nf = normx(xmid, w.ffn_norm);
-    TIMED(m, FWD_KERNEL_GATE_UP, fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, tl, s, sk, fuse ? &nf : nullptr));
+    TIMED(m, FWD_KERNEL_GATE_UP,
+          fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, tl, s, sk, fuse ? &nf : nullptr, m->cfg.ffn_act));
     float* final32 = (last && hidden) ? hidden + (int64_t)(L + 1) * TH : nullptr;
     if (fuse) {
       TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, tl, s, sk, m->ssq));
@@ -675,7 +776,7 @@ int fwd_session_create(fwd_model* m, int32_t max_batch, int32_t max_seq, fwd_ses
     se->allocs.push_back(p);
     se->count = (unsigned*)p;
     HIP_TRY(hipMemsetAsync(p, 0, (size_t)max_batch * g.Hkv * 4, m->stream));  // the kernel leaves them zero
-    return rope_table(m, &se->rope, max_seq, se->allocs);
+    return rope_tables(m, se->rope_tab, max_seq, se->allocs);
   };
   if (int rc = run()) {
     delete se;

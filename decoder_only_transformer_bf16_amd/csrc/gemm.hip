@@ -117,7 +117,9 @@ struct EpiResidual {
   }
 };
 
-template <int C, typename T>
+// ACT 0: silu(g) = g / (1 + e^-g) (SwiGLU); ACT 1: GELU in its tanh form,
+// 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))), tanh(y) = 1 - 2 / (1 + e^{2y}).
+template <int C, typename T, int ACT = 0>
 struct EpiSwiGLU {
   T* a;
   int F;
@@ -125,8 +127,13 @@ struct EpiSwiGLU {
   __device__ __forceinline__ void pair(int row, int c, float g, float u, bool ok0, bool) const {
     if (!ok0) return;
     const int f = (c / (2 * C)) * C + (c % C);
-    // silu(g) = g / (1 + e^{-g})
-    const float s = g * fast_rcp(1.f + fast_exp2(-kLog2e * g));
+    float s;
+    if constexpr (ACT == 0) {
+      s = g * fast_rcp(1.f + fast_exp2(-kLog2e * g));
+    } else {
+      const float y = 0.7978845608028654f * (g + 0.044715f * g * g * g);
+      s = 0.5f * g * (2.f - 2.f * fast_rcp(1.f + fast_exp2(2.f * kLog2e * y)));
+    }
     Elem<T>::store(a + (tiled ? tiled_index(row, f, F) : (int64_t)row * F + f), s * u);
   }
   template <int R>
@@ -138,7 +145,7 @@ struct EpiSwiGLU {
 
 // KV: also store the rotated keys and the values in a KV cache (a separate
 // instantiation, so that the plain prefill keeps the lean epilogue).
-template <int C, typename T, bool KV>
+template <int C, typename T, bool KV, bool ROT = true>
 struct EpiRope {
   T* qkv;  // [M, (Hq + 2 Hkv) D]: rotated q, rotated k, plain v, natural dim order
   const float2* cs;
@@ -161,6 +168,16 @@ struct EpiRope {
     const int cc = c - sec;
     const int head = cc / D, pd = cc - head * D;
     const int k = (pd / (2 * C)) * C + (pd % C);  // rotation index in [0, D/2)
+    if constexpr (!ROT) {  // projected q / k in natural order
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        if (row[q] < 0) continue;
+        T* dst = qkv + (int64_t)row[q] * (qsz + 2 * ksz) + sec + head * D + k;
+        Elem<T>::store(dst, v0[q]);
+        Elem<T>::store(dst + D / 2, v1[q]);
+      }
+      return;
+    }
     float2 r[R];
 #pragma unroll
     for (int q = 0; q < R; ++q)  // all table loads first
@@ -189,8 +206,13 @@ struct EpiRope {
       const int cc = c - sec;
       const int head = cc / D, pd = cc - head * D;
       const int k = (pd / (2 * C)) * C + (pd % C);  // rotation index in [0, D/2)
-      const float2 r = cs[(int64_t)t * (D / 2) + k];
       T* dst = out + sec + head * D + k;
+      if constexpr (!ROT) {
+        Elem<T>::store(dst, v0);
+        Elem<T>::store(dst + D / 2, v1);
+        return;
+      }
+      const float2 r = cs[(int64_t)t * (D / 2) + k];
       const float a = v0 * r.x - v1 * r.y, b = v0 * r.y + v1 * r.x;
       Elem<T>::store(dst, a);
       Elem<T>::store(dst + D / 2, b);
@@ -1047,17 +1069,34 @@ hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xi
 }
 
 hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, bool tiled,
-                       hipStream_t s, const SplitK* sk, const RowNormX* nx) {
-  if (dt == DType::BF16)
+                       hipStream_t s, const SplitK* sk, const RowNormX* nx, int act) {
+  if (act != 0 && act != 1) return hipErrorInvalidValue;
+  if (dt == DType::BF16) {
+    if (act == 1)
+      return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t, 1>{(bf16_t*)a, F, tiled}, tiled, s, sk, nx);
     return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t>{(bf16_t*)a, F, tiled}, tiled, s, sk, nx);
+  }
   if (tiled || nx) return hipErrorInvalidValue;
+  if (act == 1) return launch_f32(X, W, M, 2 * F, K, EpiSwiGLU<1, float, 1>{(float*)a, F, false}, s);
   return launch_f32(X, W, M, 2 * F, K, EpiSwiGLU<1, float>{(float*)a, F, false}, s);
 }
 
 hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, bool tiled,
                          hipStream_t s, const SplitK* sk, const RowNormX* nx) {
   const int N = (r.Hq + 2 * r.Hkv) * r.D;
-  if ((r.kc == nullptr) != (r.vc == nullptr)) return hipErrorInvalidValue;
+  if ((r.kc == nullptr) != (r.vc == nullptr) || (!r.rotate && r.kc)) return hipErrorInvalidValue;
+  if (!r.rotate) {  // projections only (a QK-norm pass rotates afterwards)
+    if (dt == DType::BF16)
+      return launch_bf16(X, W, M, N, K,
+                         EpiRope<32, bf16_t, false, false>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0,
+                                                           nullptr, nullptr, 0},
+                         tiled, s, sk, nx);
+    if (tiled || nx) return hipErrorInvalidValue;
+    return launch_f32(X, W, M, N, K,
+                      EpiRope<1, float, false, false>{(float*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, nullptr,
+                                                      nullptr, 0},
+                      s);
+  }
   if (dt == DType::BF16) {
     if (r.kc)
       return launch_bf16(X, W, M, N, K,

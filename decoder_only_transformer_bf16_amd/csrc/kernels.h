@@ -49,8 +49,9 @@ hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xi
                          int K, bool tiled, hipStream_t s, const SplitK* sk = nullptr, float* ssq_out = nullptr);
 // a[M, F] = silu(g) * u with W packed as interleaved gate/up chunks (N = 2F); with
 // `tiled`, a is written K-tiled too (it is the down projection's X).
+// act 0: silu(g) (SwiGLU); 1: GELU in its tanh form.
 hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, int F, int K, bool tiled,
-                       hipStream_t s, const SplitK* sk = nullptr, const RowNormX* nx = nullptr);
+                       hipStream_t s, const SplitK* sk = nullptr, const RowNormX* nx = nullptr, int act = 0);
 // QKV projection with RoPE on q and k; N = (Hq + 2 Hkv) D with packed q/k rows.
 // Writes qkv [M, (Hq + 2 Hkv) D]: rotated q heads, rotated k heads, then the value
 // heads, each in natural dim order. Rows are b * S + t (t = position).
@@ -62,6 +63,7 @@ struct RopeArgs {
   void* kc = nullptr;  // optional KV cache of the layer, K and V each [B, Hkv, Smax, D]:
   void* vc = nullptr;  // row r's rotated k and its v also go to sequence r / S, position pos0 + r % S
   int Smax = 0;
+  bool rotate = true;  // false: q and k stored as projected (natural order), no cache stores
 };
 hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs& r, int M, int K, bool tiled,
                          hipStream_t s, const SplitK* sk = nullptr, const RowNormX* nx = nullptr);
@@ -121,7 +123,25 @@ hipError_t copy_rows(void* dst, const void* src, const int32_t* map, int rows, i
 // K-tiled bf16 dst (rows padded to 16, cleared by the caller): row map[r] of dst =
 // row r of the row-major [rows, K] src; K a multiple of 32.
 hipError_t pack_tiled(void* dst, const void* src, const int32_t* map, int rows, int K, hipStream_t s);
-// dst[i] = float(src[i]) for a gain vector of dtype dt.
-hipError_t gains_to_f32(DType dt, const void* src, float* dst, int n, hipStream_t s);
+// dst[i] = offset + float(src[i]) for a gain vector of dtype dt (offset 1: (1 + w) gains).
+hipError_t gains_to_f32(DType dt, const void* src, float* dst, int n, float offset, hipStream_t s);
+
+// ---- QK-norm ----
+// In place on qkv [rows, ld] (as gemm_qkv_rope writes it without rotation): every q head
+// (gains gq [D]) and k head (gains gk [D]) is RMS-normalised over its D values, then
+// rotated by RoPE at position pos0 + row % S (table cs [positions, D / 2]); with kc / vc
+// (KV cache [B, Hkv, Smax, D]) the rotated k heads and the v heads of row r are stored
+// for sequence r / S at that position.
+struct QkNormArgs {
+  void* qkv;
+  int64_t ld;
+  int Hq, Hkv, D, S, pos0;
+  const float2* cs;
+  const float *gq, *gk;
+  float eps;
+  void *kc, *vc;
+  int Smax;
+};
+hipError_t qk_norm_rope(DType dt, const QkNormArgs& a, int rows, hipStream_t s);
 
 }  // namespace fwdk

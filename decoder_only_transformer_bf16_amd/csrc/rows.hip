@@ -249,9 +249,53 @@ __global__ __launch_bounds__(256) void pack_tiled_kernel(bf16_t* __restrict__ ds
 }
 
 template <typename T>
-__global__ void gains_kernel(const T* __restrict__ src, float* __restrict__ dst, int n) {
+__global__ void gains_kernel(const T* __restrict__ src, float* __restrict__ dst, int n, float offset) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = Elem<T>::load(src + i);
+  if (i < n) dst[i] = offset + Elem<T>::load(src + i);
+}
+
+// QK-norm then RoPE, in place on the q and k heads of each token row (qwen3 / gemma3
+// family axis of "N7 · model/forward-parity", Theorem statement): a head's D values
+// are scaled by gain / sqrt(mean of squares + eps), then each pair (k, k + D/2) turns
+// by the row's table entry. With a cache, the rotated k heads and the v heads are also
+// stored at the row's position. One wavefront per head, a lane per pair.
+template <typename T>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkNormArgs a) {
+  const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int half = a.D / 2, nh = a.Hq + a.Hkv, heads = nh + (a.vc ? a.Hkv : 0);
+  const int b = row / a.S, pos = a.pos0 + row % a.S;
+  T* base = (T*)a.qkv + (int64_t)row * a.ld;
+  for (int h = blockIdx.y * 4 + wave; h < heads; h += gridDim.y * 4) {
+    T* x = base + (int64_t)h * a.D;
+    if (h >= nh) {  // a value head: cache copy only
+      const int g = h - nh;
+      T* dst = (T*)a.vc + (((int64_t)b * a.Hkv + g) * a.Smax + pos) * a.D;
+      for (int d = lane; d < a.D; d += 64) dst[d] = x[d];
+      continue;
+    }
+    const bool is_k = h >= a.Hq;
+    const float* gain = is_k ? a.gk : a.gq;
+    float ss = 0.f;
+    for (int k = lane; k < half; k += 64) {
+      const float u = Elem<T>::load(x + k), v = Elem<T>::load(x + k + half);
+      ss += u * u + v * v;
+    }
+    ss = wave_sum(ss);
+    const float r = fast_rsqrt(ss / (float)a.D + a.eps);
+    const float2* cs = a.cs + (int64_t)pos * half;
+    T* kd = is_k && a.kc ? (T*)a.kc + (((int64_t)b * a.Hkv + (h - a.Hq)) * a.Smax + pos) * a.D : nullptr;
+    for (int k = lane; k < half; k += 64) {
+      const float u = Elem<T>::load(x + k) * r * gain[k], v = Elem<T>::load(x + k + half) * r * gain[k + half];
+      const float2 c = cs[k];
+      const float o0 = u * c.x - v * c.y, o1 = u * c.y + v * c.x;
+      Elem<T>::store(x + k, o0);
+      Elem<T>::store(x + k + half, o1);
+      if (kd) {
+        Elem<T>::store(kd + k, o0);
+        Elem<T>::store(kd + k + half, o1);
+      }
+    }
+  }
 }
 
 inline int row_blocks(int rows) { return (rows + kRowsPerBlock - 1) / kRowsPerBlock; }
@@ -317,12 +361,24 @@ hipError_t pack_tiled(void* dst, const void* src, const int32_t* map, int rows, 
   return hipGetLastError();
 }
 
-hipError_t gains_to_f32(DType dt, const void* src, float* dst, int n, hipStream_t s) {
+hipError_t gains_to_f32(DType dt, const void* src, float* dst, int n, float offset, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (dt == DType::BF16)
-    hipLaunchKernelGGL(gains_kernel<bf16_t>, dim3((n + 255) / 256), dim3(256), 0, s, (const bf16_t*)src, dst, n);
+    hipLaunchKernelGGL(gains_kernel<bf16_t>, dim3((n + 255) / 256), dim3(256), 0, s, (const bf16_t*)src, dst, n,
+                       offset);
   else
-    hipLaunchKernelGGL(gains_kernel<float>, dim3((n + 255) / 256), dim3(256), 0, s, (const float*)src, dst, n);
+    hipLaunchKernelGGL(gains_kernel<float>, dim3((n + 255) / 256), dim3(256), 0, s, (const float*)src, dst, n,
+                       offset);
+  return hipGetLastError();
+}
+
+hipError_t qk_norm_rope(DType dt, const QkNormArgs& a, int rows, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (a.D % 2 || a.D > 512 || (a.kc == nullptr) != (a.vc == nullptr)) return hipErrorInvalidValue;
+  const int heads = a.Hq + a.Hkv + (a.vc ? a.Hkv : 0);
+  const dim3 grid(rows, (heads + 3) / 4);
+  if (dt == DType::BF16) hipLaunchKernelGGL(qk_norm_rope_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(qk_norm_rope_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

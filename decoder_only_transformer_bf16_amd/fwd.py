@@ -29,13 +29,15 @@ DTYPE = {"f32": 0, "bf16": 1}
 EMBED_SCALE = {"none": 0, "bf16_sqrt_hidden": 1}
 NORM = {"pre": 0, "sandwich": 1}
 LAYER = {"global": 0, "local": 1}
+FFN_ACT = {"silu": 0, "gelu_tanh": 1}
+ROPE_SCALING = {"none": 0, "llama3": 1, "longrope": 2}
 
 EXPORTS = ("fwd_available", "fwd_create", "fwd_output_sizes", "fwd_prefill", "fwd_gemm", "fwd_attention",
            "fwd_rmsnorm", "fwd_set_timing", "fwd_get_timing", "fwd_destroy", "fwd_last_error",
            "fwd_session_create", "fwd_session_prefill", "fwd_session_decode", "fwd_session_length",
            "fwd_session_destroy")
 KERNEL_CLASSES = ("embed", "norm", "qkv_rope", "attention", "o_proj", "gate_up", "down_proj", "lm_head", "argmax",
-                  "v_transpose")
+                  "v_transpose", "qk_norm")
 
 c_i32, c_i64, c_f32, c_f64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -45,12 +47,16 @@ class FwdConfig(ctypes.Structure):
                 ("head_dim", c_i32), ("ffn", c_i32), ("vocab", c_i32), ("rms_eps", c_f32),
                 ("final_logit_softcap", c_f32), ("rope_theta", c_f64), ("embed_scale_mode", c_i32),
                 ("sliding_window", c_i32), ("layer_kind", ctypes.POINTER(c_i32)), ("norm_placement", c_i32),
-                ("dtype", c_i32), ("max_tokens", c_i32)]
+                ("dtype", c_i32), ("max_tokens", c_i32),
+                ("qk_norm", c_i32), ("norm_gain_offset", c_i32), ("ffn_act", c_i32), ("rope_theta_local", c_f64),
+                ("rope_scaling", c_i32), ("rope_factor", c_f32), ("rope_low_freq_factor", c_f32),
+                ("rope_high_freq_factor", c_f32), ("rope_original_max_pos", c_i32),
+                ("rope_short_factor", ctypes.POINTER(c_f32)), ("rope_long_factor", ctypes.POINTER(c_f32))]
 
 
 class FwdLayerWeights(ctypes.Structure):
     _fields_ = [(n, c_vp) for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down",
-                                    "post_attn_norm", "post_ffn_norm")]
+                                    "post_attn_norm", "post_ffn_norm", "q_norm", "k_norm")]
 
 
 class FwdWeights(ctypes.Structure):
@@ -137,7 +143,23 @@ def make_config(cfg, max_tokens: int):
                   embed_scale_mode=EMBED_SCALE[cfg.embed_scale_mode], sliding_window=cfg.sliding_window,
                   layer_kind=ctypes.cast(kind_arr, ctypes.POINTER(c_i32)),
                   norm_placement=NORM[cfg.norm_placement], dtype=DTYPE[cfg.dtype], max_tokens=max_tokens)
-    return c, kind_arr
+    keep = [kind_arr]
+    c.qk_norm = 1 if getattr(cfg, "qk_norm", False) else 0
+    c.norm_gain_offset = int(getattr(cfg, "norm_gain_offset", 0))
+    c.ffn_act = FFN_ACT[getattr(cfg, "ffn_act", "silu")]
+    c.rope_theta_local = float(getattr(cfg, "rope_theta_local", 0.0))
+    c.rope_scaling = ROPE_SCALING[getattr(cfg, "rope_scaling", "none")]
+    c.rope_factor = float(getattr(cfg, "rope_factor", 1.0))
+    c.rope_low_freq_factor = float(getattr(cfg, "rope_low_freq_factor", 1.0))
+    c.rope_high_freq_factor = float(getattr(cfg, "rope_high_freq_factor", 4.0))
+    c.rope_original_max_pos = int(getattr(cfg, "rope_original_max_pos", 0))
+    for field in ("rope_short_factor", "rope_long_factor"):
+        vals = tuple(getattr(cfg, field, ()) or ())
+        if vals:
+            arr = (c_f32 * len(vals))(*vals)
+            keep.append(arr)
+            setattr(c, field, ctypes.cast(arr, ctypes.POINTER(c_f32)))
+    return c, keep
 
 
 def output_sizes(cfg, B: int, S: int, max_tokens: Optional[int] = None) -> Dict[str, int]:
@@ -162,7 +184,7 @@ class Model:
     """A model on the current GPU: fwd_create at construction, fwd_destroy on close()."""
 
     LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down",
-                    "post_attn_norm", "post_ffn_norm")
+                    "post_attn_norm", "post_ffn_norm", "q_norm", "k_norm")
 
     def __init__(self, cfg, weights: Mapping[str, "object"], max_tokens: int, stream=None):
         self.cfg = cfg

@@ -52,6 +52,11 @@ extern "C" {
 #define FWD_NORM_SANDWICH 1 /* RMSNorm on the sublayer input and on its output */
 #define FWD_LAYER_GLOBAL 0
 #define FWD_LAYER_LOCAL 1   /* sliding-window attention layer                 */
+#define FWD_FFN_SILU 0      /* a = silu(g) * u (SwiGLU)                        */
+#define FWD_FFN_GELU_TANH 1 /* a = gelu(g) * u, GELU in its tanh form          */
+#define FWD_ROPE_NONE 0
+#define FWD_ROPE_LLAMA3 1   /* llama3 frequency bands                          */
+#define FWD_ROPE_LONGROPE 2 /* phi3 longrope per-frequency factors             */
 
 /*
  * Model description ("pegainfer issue #878", Proposed Plan: one typed config,
@@ -70,6 +75,32 @@ extern "C" {
  *                       FWD_DTYPE_F32 (everything fp32)
  *  max_tokens           largest B*S a later fwd_prefill may request; sizes the
  *                       workspace that fwd_create allocates
+ *
+ * Architecture variants ("N7 · model/forward-parity", Theorem statement names these
+ * family axes: qwen3 QK-norm, gemma3 local/global attention, llama3 rope scaling,
+ * phi3 longrope; the pages give no formulas, so each follows its family's published
+ * definition). Zero-initialised fields give the plain model above.
+ *  qk_norm              1: each q and k head is RMS-normalised over its head_dim
+ *                       values (gains q_norm / k_norm, eps rms_eps) before RoPE
+ *  norm_gain_offset     0: every RMSNorm scales by its gain w; 1: by (1 + w)
+ *  ffn_act              FWD_FFN_*: the gate activation of the feed-forward
+ *  rope_theta_local     RoPE base of local layers; 0 = rope_theta
+ *  rope_scaling         FWD_ROPE_*. With base frequencies f_k = theta^(-2k/D):
+ *    LLAMA3    wavelengths 2 pi / f_k below original_max_pos / high_freq_factor keep
+ *              f_k, those above original_max_pos / low_freq_factor become f_k /
+ *              factor, and in between t = (original_max_pos / wavelength -
+ *              low) / (high - low) blends them as (1 - t) f_k / factor + t f_k
+ *    LONGROPE  f_k = 1 / (e_k theta^(2k/D)) with e = long_factor when the sequence of
+ *              the call (its last position + 1) exceeds original_max_pos, else
+ *              short_factor; cos and sin are scaled by sqrt(1 + ln factor / ln
+ *              original_max_pos) when factor > 1. A cached session keeps each key
+ *              rotated as its own call rotated it.
+ *  rope_factor, rope_low_freq_factor, rope_high_freq_factor, rope_original_max_pos
+ *                       the parameters above (factor > 0; llama3: 0 < low < high)
+ *  rope_short_factor, rope_long_factor
+ *                       host arrays of head_dim / 2 positive floats (longrope), read
+ *                       during fwd_create only
+ *
  * Supported: bf16 needs head_dim in {64, 128, 256}; f32 needs head_dim <= 64;
  * hidden, Hq*D, Hkv*D and ffn multiples of 8 (bf16) or 4 (f32); bf16 additionally
  * needs hidden, Hq*D, Hkv*D and ffn multiples of 32 (its GEMM operands are stored in
@@ -86,6 +117,18 @@ typedef struct fwd_config {
   int32_t norm_placement;
   int32_t dtype;
   int32_t max_tokens;
+  /* architecture variants (appended; zero = off) */
+  int32_t qk_norm;
+  int32_t norm_gain_offset;
+  int32_t ffn_act;
+  double rope_theta_local;
+  int32_t rope_scaling;
+  float rope_factor;
+  float rope_low_freq_factor;
+  float rope_high_freq_factor;
+  int32_t rope_original_max_pos;
+  const float* rope_short_factor;
+  const float* rope_long_factor;
 } fwd_config;
 
 /*
@@ -93,7 +136,8 @@ typedef struct fwd_config {
  * bf16 or f32 according to fwd_config.dtype (norm gains too).
  *  wq [Hq*D, H], wk [Hkv*D, H], wv [Hkv*D, H], wo [H, Hq*D],
  *  w_gate [F, H], w_up [F, H], w_down [H, F], *_norm [H].
- *  post_attn_norm / post_ffn_norm are read only for FWD_NORM_SANDWICH.
+ *  post_attn_norm / post_ffn_norm are read only for FWD_NORM_SANDWICH;
+ *  q_norm / k_norm [D] only with qk_norm.
  */
 typedef struct fwd_layer_weights {
   const void* attn_norm;
@@ -107,6 +151,8 @@ typedef struct fwd_layer_weights {
   const void* w_down;
   const void* post_attn_norm;
   const void* post_ffn_norm;
+  const void* q_norm;
+  const void* k_norm;
 } fwd_layer_weights;
 
 /* embed [V, H] (also the tied LM head), final_norm [H]: device pointers;
@@ -227,7 +273,8 @@ int fwd_rmsnorm(const float* x, const void* w, void* y, int32_t rows, int32_t hi
 #define FWD_KERNEL_LM_HEAD 7       /* tied LM head (+ softcap)                     */
 #define FWD_KERNEL_ARGMAX 8        /* per-position argmax + non-finite check      */
 #define FWD_KERNEL_V_TRANSPOSE 9   /* values transposed to keys-contiguous order  */
-#define FWD_KERNEL_CLASSES 10
+#define FWD_KERNEL_QK_NORM 10      /* QK-norm + RoPE pass (qk_norm models)        */
+#define FWD_KERNEL_CLASSES 11
 /* enable != 0 turns timing on and clears the accumulated totals; 0 turns it off. */
 int fwd_set_timing(fwd_model* m, int32_t enable);
 /* Accumulated milliseconds and launch count of one kernel class since the last

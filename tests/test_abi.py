@@ -30,13 +30,36 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
-def test_struct_layouts_match_header_order():
-    cfg_fields = re.search(r"typedef struct fwd_config \{(.*?)\} fwd_config;", HEADER, re.S).group(1)
-    names = re.findall(r"(\w+)(?:,|;)", cfg_fields.replace("const int32_t*", ""))
-    assert names == [f for f, _ in fwd.FwdConfig._fields_]
-    assert ctypes.sizeof(fwd.FwdConfig) == 80
-    lw = re.search(r"typedef struct fwd_layer_weights \{(.*?)\}", HEADER, re.S).group(1)
-    assert re.findall(r"\*\s*(\w+);", lw) == [f for f, _ in fwd.FwdLayerWeights._fields_]
+def _c_layout(struct, fields):
+    """(sizeof, [offsetof ...]) of a header struct, from a C program compiled against fwd.h."""
+    import shutil
+    import subprocess
+    import tempfile
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"fwd.h\"\nint main(void) {\n"
+    src += f'  printf("%zu\\n", sizeof({struct}));\n'
+    for f in fields:
+        src += f'  printf("%zu\\n", offsetof({struct}, {f}));\n'
+    src += "  return 0;\n}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c_path, exe = os.path.join(d, "layout.c"), os.path.join(d, "layout")
+        open(c_path, "w").write(src)
+        subprocess.run([cc, "-I", os.path.join(ROOT, "include"), c_path, "-o", exe], check=True)
+        out = [int(v) for v in subprocess.run([exe], stdout=subprocess.PIPE, check=True).stdout.split()]
+    return out[0], out[1:]
+
+
+@pytest.mark.parametrize("struct,ctype", [("fwd_config", "FwdConfig"), ("fwd_layer_weights", "FwdLayerWeights"),
+                                          ("fwd_weights", "FwdWeights"), ("fwd_outputs", "FwdOutputs"),
+                                          ("fwd_sizes", "FwdSizes")])
+def test_struct_layouts_match_header(struct, ctype):
+    cls = getattr(fwd, ctype)
+    names = [f for f, _ in cls._fields_]
+    size, offsets = _c_layout(struct, names)
+    assert size == ctypes.sizeof(cls)
+    assert offsets == [getattr(cls, f).offset for f in names]
 
 
 def test_no_device_here_means_unavailable_not_fallback():
@@ -63,9 +86,35 @@ def _create_rc(cfg, max_tokens=16):
     dict(final_logit_softcap=-1.0), dict(final_logit_softcap=float("nan")), dict(final_logit_softcap=float("inf")),
     dict(n_kv_heads=3), dict(head_dim=24), dict(rms_eps=0.0), dict(rope_theta=1.0), dict(sliding_window=-1),
     dict(dtype="bf16"),  # tiny geometry is not a supported bf16 shape (head_dim 16)
+    dict(rope_theta_local=0.5),
+    dict(rope_scaling="llama3", rope_factor=8.0, rope_original_max_pos=0),
+    dict(rope_scaling="llama3", rope_factor=8.0, rope_original_max_pos=64, rope_low_freq_factor=4.0,
+         rope_high_freq_factor=1.0),
+    dict(rope_scaling="llama3", rope_factor=0.0, rope_original_max_pos=64),
+    dict(rope_scaling="longrope", rope_factor=2.0, rope_original_max_pos=64),  # no factor arrays
+    dict(rope_scaling="longrope", rope_factor=2.0, rope_original_max_pos=64,
+         rope_short_factor=(1.0,) * 7 + (0.0,), rope_long_factor=(2.0,) * 8),
 ])
 def test_bad_configs_are_rejected(bad):
     assert _create_rc(wl.TINY_F32.replace(**bad)) == fwd.FWD_E_CONFIG
+
+
+@pytest.mark.parametrize("field,value", [("qk_norm", 2), ("norm_gain_offset", -1), ("ffn_act", 7),
+                                         ("rope_scaling", 9)])
+def test_out_of_range_variant_fields_are_rejected(field, value):
+    c, keep = fwd.make_config(wl.TINY_F32, 16)
+    setattr(c, field, value)
+    s = fwd.FwdSizes()
+    assert fwd.lib().fwd_output_sizes(ctypes.byref(c), 1, 16, ctypes.byref(s)) == fwd.FWD_E_CONFIG
+
+
+def test_variant_configs_are_accepted():
+    for kw in (dict(qk_norm=True, norm_gain_offset=1, ffn_act="gelu_tanh", rope_theta_local=1e4,
+                    layer_kind=("local", "global")),
+               dict(rope_scaling="llama3", rope_factor=8.0, rope_original_max_pos=64),
+               dict(rope_scaling="longrope", rope_factor=2.0, rope_original_max_pos=64,
+                    rope_short_factor=(1.0,) * 8, rope_long_factor=(2.0,) * 8)):
+        assert _create_rc(wl.TINY_F32.replace(**kw)) == fwd.FWD_OK, kw
 
 
 def test_output_sizes_are_the_one_source_of_truth():
