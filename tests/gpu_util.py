@@ -78,3 +78,30 @@ def slot_parity(got, ref, ref_bf16_fn):
     floor = cosine(ref_bf16_fn(), ref)
     ok = c >= COS_HALF_PRECISION and (1.0 - c) <= FLOOR_SLACK * (1.0 - floor) + 2e-6
     return ok, c, floor
+
+
+def distributional_gate(got_logits, ref_logits, top: int, top1_floor: float, logprob_ceiling: float):
+    """Window-edge gate of "pegainfer issue #878" (Description, Proposed Plan): log-
+    probabilities compared at the reference's top-`top` ids per position, a global
+    top-1 agreement floor, the same floor on each quarter of the positions (a failed
+    quarter cannot hide inside a passing global rate) and a ceiling on the largest
+    log-probability gap. Non-finite values fail outright. Returns the statistics;
+    raises AssertionError when a gate fails."""
+    g = np.asarray(got_logits, np.float64).reshape(-1, np.shape(got_logits)[-1])
+    r = np.asarray(ref_logits, np.float64).reshape(-1, np.shape(ref_logits)[-1])
+    assert np.isfinite(g).all() and np.isfinite(r).all(), "non-finite logits"
+
+    def log_softmax(z):
+        m = z.max(-1, keepdims=True)
+        return z - m - np.log(np.exp(z - m).sum(-1, keepdims=True))
+
+    lg, lr = log_softmax(g), log_softmax(r)
+    ids = np.argsort(-r, axis=-1, kind="stable")[:, :top]
+    gap = np.abs(np.take_along_axis(lg, ids, -1) - np.take_along_axis(lr, ids, -1))
+    agree = np.argmax(g, -1) == np.argmax(r, -1)
+    quarters = [float(q.mean()) for q in np.array_split(agree, 4)]
+    stats = {"top1": float(agree.mean()), "quarters": quarters, "max_gap": float(gap.max())}
+    assert stats["top1"] >= top1_floor, stats
+    assert min(quarters) >= top1_floor, stats
+    assert stats["max_gap"] <= logprob_ceiling, stats
+    return stats

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from synth import workloads as wl
-from tests.gpu_util import COS_HALF_PRECISION, FLOOR_SLACK, argmax_check, cosine, slot_parity, to_device
+from tests.gpu_util import COS_HALF_PRECISION, FLOOR_SLACK, argmax_check, distributional_gate, cosine, slot_parity, to_device
 
 pytestmark = pytest.mark.gpu
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_values.json")))
@@ -173,17 +173,27 @@ def test_gemma3_style_full_model(fwd):
 
 def test_gemma3_style_window_evicts(fwd):
     """One full 5:1 period (6 layers) at S = 1100 > W = 1024: positions >= 1024 lose
-    their oldest keys on the 5 local layers. The oracle runs all 1100 positions
-    (hidden slots only) and the window is checked to matter."""
+    their oldest keys on the 5 local layers. The oracle runs all 1100 positions; the
+    hidden slots take the cosine gates, the logits the window-edge distributional gate
+    ("pegainfer issue #878": top-64 log-probabilities, global and per-quarter top-1
+    floor, log-probability ceiling), and the window is checked to matter."""
     import torch
     cfg = wl.GEMMA3_STYLE.replace(n_layers=6, layer_kind=wl.GEMMA3_STYLE.layer_kind[:6], name="gemma3-6L")
     _say("gemma3-style 6 layers at 1 x 1100")
     model, host = _build(fwd, cfg, 1100)
     ids = wl.draw_ids(cfg, seq=1100)
-    out = model.prefill(ids, logits=False, hidden=True, argmax=False)
+    out = model.prefill(ids, logits=True, hidden=True, argmax=False)
     got = out["hidden"].cpu().numpy()
-    _say("  oracle, all 1100 positions, 6 layers (hidden slots only)")
-    ref = oracle.forward(cfg, host, ids, want_logits=False)
+    got_z = out["logits"].cpu().numpy()
+    del out
+    _say("  oracle, all 1100 positions, 6 layers and the head")
+    ref = oracle.forward(cfg, host, ids)
+    n, of = GOLD["window_edge_top1_floor"]["value"]
+    for name, sl in (("all 1100 positions", slice(None)), ("the 76 evicting positions", slice(1024, None))):
+        st = distributional_gate(got_z[:, sl], ref["logits"][:, sl], GOLD["window_edge_top_ids"]["value"],
+                                 n / of, GOLD["window_edge_logprob_ceiling"]["value"])
+        _say(f"  distributional gate, {name}: top-1 {st['top1']:.4f}, quarters "
+             f"{[round(q, 4) for q in st['quarters']]}, max |dlogprob| {st['max_gap']:.3e}")
     refb = {}
 
     def bf16_slot(s, tail=False):
