@@ -112,6 +112,50 @@ def decode_leg(fwd, model, cfg, ids, steps, stream):
             "note": "bytes = all packed weights + the cached keys and values read once per step"}
 
 
+def variant_leg(fwd, cfg0, ids, steps, stream):
+    """The Llama-3-8B shape with the family variants switched on (QK-norm, tanh-GELU
+    gating, llama3 frequency bands at original context 8192, factor 8): tokens/s of the
+    same prefill, and the QK-norm pass against HBM (it reads and writes every q and k
+    head once: T * (Hq + Hkv) * D * 2 B each way per layer)."""
+    import torch
+    from synth import workloads as wl
+    from tests.gpu_util import to_device
+    cfg = cfg0.replace(qk_norm=True, ffn_act="gelu_tanh", rope_scaling="llama3", rope_factor=8.0,
+                       rope_low_freq_factor=1.0, rope_high_freq_factor=4.0, rope_original_max_pos=8192,
+                       name="llama3-8b-shape-variants")
+    B, S = ids.shape
+    T = B * S
+    weights = {n: to_device(wl.draw_weight(cfg, n)) for n in wl.weight_shapes(cfg)}
+    model = fwd.Model(cfg, weights, max_tokens=T, stream=stream)
+    del weights
+    torch.cuda.empty_cache()
+    argmax = torch.empty((B, S), dtype=torch.int32, device="cuda")
+    model.prefill_into(ids, None, None, argmax)                       # warm-up
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps):
+        model.prefill_into(ids, None, None, argmax)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t) * 1000.0 / steps
+    model.set_timing(True)
+    model.prefill_into(ids, None, None, argmax)
+    torch.cuda.synchronize()
+    timing = model.timing()
+    model.set_timing(False)
+    model.close()
+    qk = timing["qk_norm"]
+    qk_bytes = 2 * T * (cfg.n_heads + cfg.n_kv_heads) * cfg.head_dim * 2
+    qk_us = qk["ms"] * 1000.0 / max(qk["launches"], 1)
+    log(f"variants: {ms:.2f} ms/step, QK-norm pass {qk_us:.1f} us per layer")
+    return {"config": "llama3-8b-shape prefill 8 x 2048 with QK-norm, tanh-GELU gating, llama3 rope scaling "
+                      "(factor 8, original context 8192); argmax only",
+            "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
+            "kernels_ms_per_step": {k: v["ms"] for k, v in timing.items() if v["launches"]},
+            "qk_norm_pass": {"us_per_layer": qk_us, "bytes_per_layer": qk_bytes, "bound": "hbm",
+                             "achieved_gbs": qk_bytes / (qk_us * 1e-6) / 1e9, "peak_gbs": PEAK_HBM_GBS,
+                             "frac": qk_bytes / (qk_us * 1e-6) / 1e9 / PEAK_HBM_GBS}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +166,8 @@ def main():
     ap.add_argument("--timing-steps", type=int, default=2, help="extra steps timed per kernel with HIP events")
     ap.add_argument("--decode-steps", type=int, default=16,
                     help="greedy decode steps timed on a cached session after the prefill (0: skip)")
+    ap.add_argument("--variant-leg", action="store_true",
+                    help="also time the same shape with QK-norm, tanh-GELU gating and llama3 rope scaling")
     args = ap.parse_args()
     if args.timing_steps < 1:
         ap.error("--timing-steps must be at least 1 (the roofline comes from those steps)")
@@ -170,6 +216,14 @@ def main():
     elapsed = time.perf_counter() - t
     ms_per_step = elapsed * 1000.0 / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step")
+    # the same prefill returning only the per-position argmax (no logits, no slots)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(args.steps):
+        model.prefill_into(ids, None, None, argmax)
+    torch.cuda.synchronize()
+    ms_argmax_only = (time.perf_counter() - t) * 1000.0 / args.steps
+    log(f"argmax-only outputs: {ms_argmax_only:.2f} ms/step")
     # per-kernel breakdown from separate steps with HIP events around every launch
     # (the events add gaps, so these steps are not part of the throughput figure)
     model.set_timing(True)
@@ -231,6 +285,10 @@ def main():
                        "tflops": total_flops / (ms_per_step * 1e-3) / 1e12,
                        "frac_of_bf16_peak": total_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "kernels": kernels,
+        "modes": {"all_outputs": {"ms_per_step": ms_per_step, "tokens_per_s": T * args.steps / elapsed,
+                                  "outputs": "fp32 logits, argmax" + ("" if args.no_hidden else ", hidden slots")},
+                  "argmax_only": {"ms_per_step": ms_argmax_only, "tokens_per_s": T / (ms_argmax_only * 1e-3),
+                                  "outputs": "argmax (logits kept in a 1024-row workspace)"}},
     }
     if args.decode_steps > 0:
         del logits, hidden
@@ -239,6 +297,9 @@ def main():
     model.close()
     del argmax
     torch.cuda.empty_cache()
+    if args.variant_leg:
+        result["variants"] = variant_leg(fwd, cfg, ids, max(args.steps, 1), stream)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(cfg, S)

@@ -58,6 +58,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
+// Every lane of an aligned group of N lanes (N = 4, 8, 16 or 32) gets the group's sum,
+// through DPP moves within rows of 16 lanes (and one shuffle across rows for 32).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group of 4, 8, 16 or 32 lanes");
+  v += dpp_mov<0xB1>(v);                          // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);                          // quad_perm [2, 3, 0, 1]: quad sums
+  if constexpr (N >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror: lane i <- 7 - i within 8 lanes
+  if constexpr (N >= 16) v += dpp_mov<0x140>(v);  // row_mirror: lane i <- 15 - i
+  if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+  return v;
+}
+
+// 8 bf16 values (16 bytes) widened to fp32, and packed back with rounding to nearest even.
+__device__ __forceinline__ void unpack8(const u32x4_t& u, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(u[i] << 16);
+    f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ u32x4_t pack8(const float (&f)[8]) {
+  u32x4_t u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  return u;
+}
+
 // exp2 on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // 1/x and 1/sqrt(x) on the hardware units (v_rcp_f32, v_rsq_f32).

@@ -164,30 +164,6 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(const float* __r
 
 
 // ------------------------------------------------------------------ bf16 kernel
-// Every lane of an aligned group of N lanes (N = 8, 16 or 32) gets the group's sum.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-  static_assert(N == 8 || N == 16 || N == 32, "group of 8, 16 or 32 lanes");
-  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]: quad sums
-  v += dpp_mov<0x141>(v);  // row_half_mirror: lane i <- 7 - i within 8 lanes
-  if constexpr (N >= 16) v += dpp_mov<0x140>(v);  // row_mirror: lane i <- 15 - i
-  if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
-  return v;
-}
-
-__device__ __forceinline__ void unpack8(const u32x4_t& u, float (&f)[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(u[i] << 16);
-    f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
-  }
-}
-
 __device__ __forceinline__ void store_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -259,6 +259,59 @@ __global__ void gains_kernel(const T* __restrict__ src, float* __restrict__ dst,
 // are scaled by gain / sqrt(mean of squares + eps), then each pair (k, k + D/2) turns
 // by the row's table entry. With a cache, the rotated k heads and the v heads are also
 // stored at the row's position. One wavefront per head, a lane per pair.
+// bf16: D / 16 lanes per head; a lane holds elements 8 j .. 8 j + 7 of both halves,
+// i.e. eight whole rotation pairs, with 16-byte loads and stores.
+template <int D>
+__global__ __launch_bounds__(256) void qk_norm_rope_bf16_kernel(QkNormArgs a, int rows) {
+  constexpr int LPH = D / 16, HPW = 64 / LPH, half = D / 2;
+  const int lane = threadIdx.x & 63, j = lane % LPH;
+  const int nh = a.Hq + a.Hkv, heads = nh + (a.vc ? a.Hkv : 0);
+  const int64_t gh = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * HPW + lane / LPH;
+  if (gh >= (int64_t)rows * heads) return;  // (whole groups of LPH lanes leave together)
+  const int row = (int)(gh / heads), h = (int)(gh - (int64_t)row * heads);
+  const int b = row / a.S, pos = a.pos0 + row % a.S;
+  bf16_t* x = (bf16_t*)a.qkv + (int64_t)row * a.ld + (int64_t)h * D + 8 * j;
+  const u32x4_t u0 = *reinterpret_cast<const u32x4_t*>(x), u1 = *reinterpret_cast<const u32x4_t*>(x + half);
+  if (h >= nh) {  // a value head: cache copy only
+    bf16_t* dst = (bf16_t*)a.vc + (((int64_t)b * a.Hkv + (h - nh)) * a.Smax + pos) * D + 8 * j;
+    *reinterpret_cast<u32x4_t*>(dst) = u0;
+    *reinterpret_cast<u32x4_t*>(dst + half) = u1;
+    return;
+  }
+  const bool is_k = h >= a.Hq;
+  const float* gain = (is_k ? a.gk : a.gq) + 8 * j;
+  const float4* cs4 = reinterpret_cast<const float4*>(a.cs + (int64_t)pos * half + 8 * j);  // 8 (cos, sin)
+  float p[8], q[8];
+  unpack8(u0, p);
+  unpack8(u1, q);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += p[e] * p[e] + q[e] * q[e];
+  ss = group_sum<LPH>(ss);
+  const float r = fast_rsqrt(ss / (float)D + a.eps);
+  float o0[8], o1[8];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    const float4 c = cs4[e2];  // pairs 2 e2 and 2 e2 + 1
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int e = 2 * e2 + t;
+      const float cx = t ? c.z : c.x, sy = t ? c.w : c.y;
+      const float u = p[e] * r * gain[e], v = q[e] * r * gain[e + half];
+      o0[e] = u * cx - v * sy;
+      o1[e] = u * sy + v * cx;
+    }
+  }
+  const u32x4_t w0 = pack8(o0), w1 = pack8(o1);
+  *reinterpret_cast<u32x4_t*>(x) = w0;
+  *reinterpret_cast<u32x4_t*>(x + half) = w1;
+  if (is_k && a.kc) {
+    bf16_t* kd = (bf16_t*)a.kc + (((int64_t)b * a.Hkv + (h - a.Hq)) * a.Smax + pos) * D + 8 * j;
+    *reinterpret_cast<u32x4_t*>(kd) = w0;
+    *reinterpret_cast<u32x4_t*>(kd + half) = w1;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkNormArgs a) {
   const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -376,6 +429,16 @@ hipError_t qk_norm_rope(DType dt, const QkNormArgs& a, int rows, hipStream_t s) 
   if (rows <= 0) return hipSuccess;
   if (a.D % 2 || a.D > 512 || (a.kc == nullptr) != (a.vc == nullptr)) return hipErrorInvalidValue;
   const int heads = a.Hq + a.Hkv + (a.vc ? a.Hkv : 0);
+  if (dt == DType::BF16 && (a.D == 64 || a.D == 128 || a.D == 256) && a.ld % 8 == 0) {
+    const int64_t per_block = 4LL * (64 / (a.D / 16));  // heads per workgroup
+    const dim3 grid((unsigned)(((int64_t)rows * heads + per_block - 1) / per_block));
+    switch (a.D) {
+      case 64: hipLaunchKernelGGL(qk_norm_rope_bf16_kernel<64>, grid, dim3(256), 0, s, a, rows); break;
+      case 128: hipLaunchKernelGGL(qk_norm_rope_bf16_kernel<128>, grid, dim3(256), 0, s, a, rows); break;
+      default: hipLaunchKernelGGL(qk_norm_rope_bf16_kernel<256>, grid, dim3(256), 0, s, a, rows);
+    }
+    return hipGetLastError();
+  }
   const dim3 grid(rows, (heads + 3) / 4);
   if (dt == DType::BF16) hipLaunchKernelGGL(qk_norm_rope_kernel<bf16_t>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(qk_norm_rope_kernel<float>, grid, dim3(256), 0, s, a);

@@ -30,7 +30,7 @@ GEMMA3 = wl.GEMMA3_STYLE.replace(n_heads=4, n_kv_heads=2, head_dim=256, sliding_
                                  layer_kind=("local", "global"), qk_norm=True, norm_gain_offset=1,
                                  ffn_act="gelu_tanh", rope_theta=1e6, rope_theta_local=1e4,
                                  name="gemma3-like-2L", **SMALL)
-LLAMA3_SCALED = wl.LLAMA3_8B.replace(n_heads=8, n_kv_heads=2, rope_scaling="llama3", rope_factor=8.0,
+LLAMA3_SCALED = wl.LLAMA3_8B.replace(n_heads=8, n_kv_heads=2, qk_norm=True, rope_scaling="llama3", rope_factor=8.0,
                                      rope_low_freq_factor=1.0, rope_high_freq_factor=4.0, rope_original_max_pos=64,
                                      name="llama3-scaled-2L", **SMALL)
 _rng = np.random.default_rng(11)
@@ -112,7 +112,7 @@ def test_f32_all_variants(fwd):
     _parity(fwd, cfg, np.asarray(wl.draw_ids(cfg)), logit_gate=LOGIT_MAX)
 
 
-@pytest.mark.parametrize("cfg", [QWEN3, GEMMA3], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [QWEN3, GEMMA3, LLAMA3_SCALED], ids=lambda c: c.name)
 def test_qk_norm_cached_decode(fwd, cfg):
     """Cached session with QK-norm: the normalising pass also fills the cache. Every
     step against the oracle's cacheless forward over the same sequence ([mg] Theorem 1:
