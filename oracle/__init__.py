@@ -27,6 +27,8 @@ from .forward import (  # noqa: F401
     gelu_tanh,
     gemm,
     greedy,
+    moe_ffn,
+    moe_route,
     rmsnorm,
     rope,
     rope_frequencies,

@@ -16,7 +16,8 @@ Sources (page title, then the passage):
   llama3 rope scaling, phi3 longrope) but gives no formula for them. Those functions
   below follow the families' published definitions, each restated where it is used:
   QK-norm, (1 + w) norm gains, the tanh-approximated GELU gate, a separate RoPE base
-  for local layers, the llama3 frequency bands and the longrope per-frequency factors.
+  for local layers, the llama3 frequency bands and the longrope per-frequency factors;
+  and the mixture-of-experts feed-forward of the hybrid dense/sparse family (qwen3moe).
 
 Every function takes float32 arrays, computes in float64 and returns float32.
 Where the pages leave a point open this file takes the plainest reading: rotate-half
@@ -275,6 +276,37 @@ def gated_ffn(g, u, act: str = "silu") -> np.ndarray:
     raise ValueError(f"ffn_act {act!r}")
 
 
+def moe_route(logits, top_k: int, norm_topk: bool):
+    """Expert choice of each token from router logits [..., E] (qwen3moe family axis of
+    [fp] Theorem statement; [fp] intro lists the MoE FFN; published definition):
+    probabilities p = softmax(logits) over all experts; the top_k experts by p (the
+    softmax is monotone, so by logit; lowest index first on ties); their weights p,
+    divided by their sum when norm_topk. Returns (idx int32 [..., k], w float64 [..., k])."""
+    z = _f64(logits)
+    m = z.max(axis=-1, keepdims=True)
+    e = np.exp(z - m)
+    p = e / e.sum(axis=-1, keepdims=True)
+    idx = np.argsort(-z, axis=-1, kind="stable")[..., :top_k].astype(np.int32)
+    w = np.take_along_axis(p, idx, axis=-1)
+    if norm_topk:
+        w = w / w.sum(axis=-1, keepdims=True)
+    return idx, w
+
+
+def moe_ffn(n, router, expert_gate, expert_up, expert_down, top_k: int, norm_topk: bool, act: str = "silu"):
+    """Mixture-of-experts feed-forward of rows n [..., H]: d = sum over the token's top_k
+    experts e of w_e * (act(n W_g,e^T) * (n W_u,e^T)) W_d,e^T, in expert-rank order.
+    expert_* are [E, F_e, H] / [E, H, F_e] row-major stacks (published qwen3moe form)."""
+    n2 = np.asarray(n).reshape(-1, np.shape(n)[-1])
+    idx, w = moe_route(gemm(n2, router), top_k, norm_topk)
+    out = np.zeros((n2.shape[0], np.shape(expert_down)[1]), dtype=np.float64)
+    for e in np.unique(idx):
+        rows, slot = np.nonzero(idx == e)
+        a = gated_ffn(gemm(n2[rows], expert_gate[e]), gemm(n2[rows], expert_up[e]), act)
+        out[rows] += w[rows, slot][:, None] * _f64(gemm(a, expert_down[e]))
+    return _f32(out).reshape(np.shape(n)[:-1] + (out.shape[-1],))
+
+
 # ---------------------------------------------------------------- head
 def softcap(z, cap: float) -> np.ndarray:
     """z <- cap * tanh(z / cap) when cap > 0 — [pi] Description (final-logit softcap)."""
@@ -327,6 +359,7 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
     goff = float(getattr(cfg, "norm_gain_offset", 0))
     act = getattr(cfg, "ffn_act", "silu")
     qk_norm = bool(getattr(cfg, "qk_norm", False))
+    ffn_kinds = cfg.ffn_kinds() if hasattr(cfg, "ffn_kinds") else ("dense",) * L
 
     E = weights["embed"]
     x = embed(E, ids, embed_scale(cfg.embed_scale_mode, H))            # [B, S, H]
@@ -355,10 +388,14 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
         if sandwich:
             u = rmsnorm(u, weights[p + "post_attn_norm"], eps, goff)
         x = _f32(_f64(x) + _f64(u))
-        # feed-forward sublayer
+        # feed-forward sublayer (dense, or mixture of experts on the layers the map names)
         n = rb(rmsnorm(x, weights[p + "ffn_norm"], eps, goff))
-        a = rb(gated_ffn(gemm(n, weights[p + "w_gate"]), gemm(n, weights[p + "w_up"]), act))
-        d = gemm(a, weights[p + "w_down"])
+        if ffn_kinds[l] == "moe":
+            d = moe_ffn(n, weights[p + "router"], weights[p + "expert_gate"], weights[p + "expert_up"],
+                        weights[p + "expert_down"], cfg.n_experts_per_tok, cfg.moe_norm_topk, act)
+        else:
+            a = rb(gated_ffn(gemm(n, weights[p + "w_gate"]), gemm(n, weights[p + "w_up"]), act))
+            d = gemm(a, weights[p + "w_down"])
         if sandwich:
             d = rmsnorm(d, weights[p + "post_ffn_norm"], eps, goff)
         x = _f32(_f64(x) + _f64(d))

@@ -58,6 +58,18 @@ class ModelConfig:
     rope_short_factor: Tuple[float, ...] = ()  # longrope, D / 2 values
     rope_long_factor: Tuple[float, ...] = ()   # longrope, D / 2 values
     gain_sigma: float = 0.0               # > 0: norm gains drawn as neutral + N(0, sigma^2)
+    # mixture-of-experts feed-forward (qwen3moe-style hybrid dense / sparse layers)
+    n_experts: int = 0                    # 0: dense feed-forward everywhere
+    n_experts_per_tok: int = 0            # top-k
+    moe_ffn: int = 0                      # width of each expert's gated FFN
+    moe_norm_topk: bool = True            # renormalise the top-k probabilities to sum 1
+    ffn_kind: Tuple[str, ...] = ()        # "dense" | "moe" per layer; empty = all "moe" when n_experts > 0
+    router_sigma: float = 0.0             # router weight spread (0: the matrix sigma)
+
+    def ffn_kinds(self) -> Tuple[str, ...]:
+        if self.n_experts <= 0:
+            return ("dense",) * self.n_layers
+        return self.ffn_kind if self.ffn_kind else ("moe",) * self.n_layers
 
     def kinds(self) -> Tuple[str, ...]:
         return self.layer_kind if self.layer_kind else ("global",) * self.n_layers
@@ -88,7 +100,8 @@ GEMM_SWEEP: List[Tuple[int, int, int]] = [
 
 
 def weight_shapes(cfg: ModelConfig) -> Dict[str, Tuple[Tuple[int, ...], str]]:
-    """name -> (shape, kind) with kind 'matrix' (N(0, 0.02^2)) or 'gain' (ones)."""
+    """name -> (shape, kind) with kind 'matrix' (N(0, 0.02^2)), 'router' (N(0, router_sigma^2))
+    or 'gain' (ones, or spread by gain_sigma)."""
     H, D, F = cfg.hidden, cfg.head_dim, cfg.ffn
     out = {"embed": ((cfg.vocab, H), "matrix"), "final_norm": ((H,), "gain")}
     for l in range(cfg.n_layers):
@@ -108,6 +121,14 @@ def weight_shapes(cfg: ModelConfig) -> Dict[str, Tuple[Tuple[int, ...], str]]:
         if cfg.qk_norm:
             out[p + "q_norm"] = ((D,), "gain")
             out[p + "k_norm"] = ((D,), "gain")
+        if cfg.ffn_kinds()[l] == "moe":  # the sparse layer replaces the dense FFN weights
+            for n in ("w_gate", "w_up", "w_down"):
+                del out[p + n]
+            E, Fe = cfg.n_experts, cfg.moe_ffn
+            out[p + "router"] = ((E, H), "router")
+            out[p + "expert_gate"] = ((E, Fe, H), "matrix")
+            out[p + "expert_up"] = ((E, Fe, H), "matrix")
+            out[p + "expert_down"] = ((E, H, Fe), "matrix")
     return out
 
 
@@ -122,6 +143,8 @@ def draw_weight(cfg: ModelConfig, name: str, seed: int = SEED_WEIGHTS) -> np.nda
         else:
             g = np.full(shape, neutral, dtype=np.float32)
         return g if cfg.dtype == "f32" else to_bf16_bits(g)
+    if kind == "router":
+        return normal(seed, name, shape, cfg.router_sigma or WEIGHT_SIGMA, cfg.dtype)
     return normal(seed, name, shape, WEIGHT_SIGMA, cfg.dtype)
 
 

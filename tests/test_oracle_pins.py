@@ -551,3 +551,75 @@ def test_gelu_tanh_closed_forms_and_gate():
     assert a[0] == pytest.approx(float(oracle.gelu_tanh(np.array([1.5]))[0]) * -2.0, rel=1e-6)
     b = oracle.gated_ffn(np.array([-2.0], np.float32), np.array([1.5], np.float32), "gelu_tanh")
     assert abs(a[0] - b[0]) > 0.1
+
+
+# ---------------------------------------------------------------- mixture of experts
+def test_moe_route_brute_force_and_ties():
+    z = np.array([[0.5, 2.0, 2.0, -1.0, 0.0], [3.0, 1.0, 1.0, 1.0, 3.0]], np.float32)
+    idx, w = oracle.moe_route(z, 3, False)
+    assert idx.tolist() == [[1, 2, 0], [0, 4, 1]]               # equal logits: lowest index first
+    z64 = z.astype(np.float64)
+    p = np.exp(z64 - z64.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    np.testing.assert_allclose(w, np.take_along_axis(p, idx.astype(np.int64), -1), rtol=1e-14)
+    _, wn = oracle.moe_route(z, 3, True)
+    np.testing.assert_allclose(wn.sum(-1), 1.0, rtol=1e-15)
+    np.testing.assert_allclose(wn, w / w.sum(-1, keepdims=True), rtol=1e-15)
+
+
+def _moe_weights(E=4, H=8, Fe=6, seed=5):
+    rng = np.random.default_rng(seed)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32) * 0.5
+    return f(E, H), f(E, Fe, H), f(E, Fe, H), f(E, H, Fe)
+
+
+def test_moe_identical_experts_reduce_to_the_dense_ffn():
+    r, g, u, d = _moe_weights()
+    g[:] = g[0]
+    u[:] = u[0]
+    d[:] = d[0]
+    n = np.random.default_rng(1).standard_normal((7, 8)).astype(np.float32)
+    dense = oracle.gemm(oracle.swiglu(oracle.gemm(n, g[0]), oracle.gemm(n, u[0])), d[0])
+    for k in (1, 2, 4):
+        np.testing.assert_allclose(oracle.moe_ffn(n, r, g, u, d, k, True), dense, rtol=1e-5, atol=1e-6)
+
+
+def test_moe_top1_normalised_is_the_winning_expert_alone():
+    r, g, u, d = _moe_weights()
+    n = np.random.default_rng(2).standard_normal((9, 8)).astype(np.float32)
+    got = oracle.moe_ffn(n, r, g, u, d, 1, True)
+    win = np.argmax(oracle.gemm(n, r), -1)
+    for t in range(9):
+        e = win[t]
+        ref = oracle.gemm(oracle.swiglu(oracle.gemm(n[t:t + 1], g[e]), oracle.gemm(n[t:t + 1], u[e])), d[e])
+        np.testing.assert_allclose(got[t], ref[0], rtol=1e-5, atol=1e-6)
+
+
+def test_moe_joint_expert_permutation_invariance():
+    r, g, u, d = _moe_weights(E=6)
+    n = np.random.default_rng(3).standard_normal((11, 8)).astype(np.float32)
+    base = oracle.moe_ffn(n, r, g, u, d, 2, False)
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    np.testing.assert_allclose(oracle.moe_ffn(n, r[perm], g[perm], u[perm], d[perm], 2, False), base,
+                               rtol=1e-5, atol=1e-6)
+    # permuting the experts alone (router unchanged) changes the result: the router matters
+    assert np.abs(oracle.moe_ffn(n, r, g[perm], u[perm], d[perm], 2, False) - base).max() > 1e-3
+
+
+def test_forward_moe_layer_with_dense_copies_equals_dense_forward():
+    dense = wl.TINY_F32
+    moe = dense.replace(n_experts=3, n_experts_per_tok=2, moe_ffn=dense.ffn, ffn_kind=("moe", "dense"),
+                        name="tiny-moe")
+    w = {n: np.asarray(a, np.float32) for n, a in wl.draw_all(dense).items()}
+    wm = dict(w)
+    for n in ("w_gate", "w_up", "w_down"):
+        del wm["layers.0." + n]
+    wm["layers.0.router"] = np.random.default_rng(4).standard_normal((3, dense.hidden)).astype(np.float32)
+    wm["layers.0.expert_gate"] = np.stack([w["layers.0.w_gate"]] * 3)
+    wm["layers.0.expert_up"] = np.stack([w["layers.0.w_up"]] * 3)
+    wm["layers.0.expert_down"] = np.stack([w["layers.0.w_down"]] * 3)
+    ids = wl.draw_ids(dense)
+    a, b = oracle.forward(dense, w, ids), oracle.forward(moe, wm, ids)
+    for s in range(dense.n_layers + 2):
+        np.testing.assert_allclose(b["hidden"][s], a["hidden"][s], rtol=1e-5, atol=1e-6)
+    assert set(wl.weight_shapes(moe)) == set(wm)                   # the recipe names the same tensors
