@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfwd.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["gemm.hip", "attention.hip", "rows.hip", "decode.hip", "fwd.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "rows.hip", "decode.hip", "moe.hip", "fwd.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", INCLUDE, "-I", CSRC,
          # keep the compiler from emitting packed-fp32 VALU forms

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -84,6 +85,21 @@ int check_config(const fwd_config* c) {
   if (c->ffn_act != FWD_FFN_SILU && c->ffn_act != FWD_FFN_GELU_TANH) return fail(FWD_E_CONFIG, "ffn_act");
   if (c->rope_theta_local != 0.0 && (!(c->rope_theta_local > 1.0) || !std::isfinite(c->rope_theta_local)))
     return fail(FWD_E_CONFIG, "rope_theta_local must be > 1, or 0 for rope_theta");
+  if (c->n_experts < 0 || (c->n_experts == 0 && c->ffn_kind))
+    for (int l = 0; c->ffn_kind && l < c->n_layers; ++l)
+      if (c->ffn_kind[l] != FWD_FFN_DENSE) return fail(FWD_E_CONFIG, "ffn_kind names MoE layers but n_experts is 0");
+  if (c->n_experts < 0) return fail(FWD_E_CONFIG, "n_experts must be >= 0");
+  if (c->n_experts > 0) {
+    if (c->dtype != FWD_DTYPE_BF16) return fail(FWD_E_CONFIG, "mixture of experts needs dtype bf16");
+    if (c->n_experts > fwdk::kMoeMaxExperts) return fail(FWD_E_CONFIG, "n_experts must be at most 256");
+    if (c->n_experts_per_tok < 1 || c->n_experts_per_tok > std::min(fwdk::kMoeMaxTopK, (int)c->n_experts))
+      return fail(FWD_E_CONFIG, "n_experts_per_tok must be in 1 .. min(8, n_experts)");
+    if (c->moe_ffn <= 0 || c->moe_ffn % 32) return fail(FWD_E_CONFIG, "moe_ffn must be a positive multiple of 32");
+    if (c->moe_norm_topk != 0 && c->moe_norm_topk != 1) return fail(FWD_E_CONFIG, "moe_norm_topk must be 0 or 1");
+    for (int l = 0; c->ffn_kind && l < c->n_layers; ++l)
+      if (c->ffn_kind[l] != FWD_FFN_DENSE && c->ffn_kind[l] != FWD_FFN_MOE)
+        return fail(FWD_E_CONFIG, "ffn_kind entries must be FWD_FFN_DENSE or FWD_FFN_MOE");
+  }
   if (c->rope_scaling != FWD_ROPE_NONE) {
     if (c->rope_scaling != FWD_ROPE_LLAMA3 && c->rope_scaling != FWD_ROPE_LONGROPE)
       return fail(FWD_E_CONFIG, "rope_scaling");
@@ -109,12 +125,17 @@ int check_config(const fwd_config* c) {
 // outputs) are kept K-tiled (16 x 32 tiles, rows padded to 16); f32 is row-major.
 struct Geometry {
   int64_t esize, H, Hq, Hkv, D, F, V, L, T, qkv_rows, logit_chunk, rope_tables;
+  int64_t E = 0, topk = 0, Fe = 0, moe_layers = 0;  // mixture of experts
+  int64_t moe_rows() const { return round_up(T * topk + 16 * E, 16); }  // permuted rows (16-aligned segments)
+  int64_t moe_tiles() const { return (T * topk + fwdk::kMoeTileRows - 1) / fwdk::kMoeTileRows + E; }
   bool tiled;
   int64_t rows(int64_t r) const { return tiled ? round_up(r, 16) : r; }  // allocated rows of an operand
   int64_t weight_bytes() const {
     const int64_t per_layer =
         (rows(qkv_rows) * H + rows(H) * Hq * D + rows(2 * F) * H + rows(H) * F) * esize + 4 * H * 4;
-    return rows(V) * H * esize + H * 4 + L * per_layer;
+    const int64_t moe_delta = moe_layers * ((rows(E) * H + E * (rows(2 * Fe) * H + rows(H) * Fe) -
+                                             (rows(2 * F) * H + rows(H) * F)) * esize);
+    return rows(V) * H * esize + H * 4 + L * per_layer + moe_delta;
   }
   // Workspace (bytes, each buffer rounded to 256) for up to T tokens.
   int64_t workspace_bytes(bool sandwich) const {
@@ -130,6 +151,11 @@ struct Geometry {
     w += r(logit_chunk * V * 4);                        // logits when the caller wants none
     w += rope_tables * r(T * (D / 2) * 8);              // RoPE cos/sin tables
     if (tiled) w += r(skinny_part_floats() * 4) + r(skinny_counters() * 4) + r(fwdk::skinny_groups((int)H) * 64 * 4);
+    if (E > 0) {
+      const int64_t A = T * topk, nch = fwdk::moe_chunks(A);
+      w += r(T * E * 4) + 3 * r(A * 4) + 2 * r(nch * E * 4) + 4 * r((E + 1) * 4);
+      w += r(moe_rows() * H * esize) + r(moe_rows() * Fe * esize) + r(moe_rows() * H * 4);
+    }
     return w;
   }
   // Split-K workspace of the few-row products (bf16, at most kSkinnyRows rows):
@@ -162,6 +188,12 @@ Geometry geometry(const fwd_config* c) {
   for (int l = 0; c->layer_kind && l < c->n_layers; ++l) any_local |= c->layer_kind[l] == FWD_LAYER_LOCAL;
   g.rope_tables = (any_local && c->rope_theta_local > 0.0 && c->rope_theta_local != c->rope_theta ? 2 : 1) *
                   (c->rope_scaling == FWD_ROPE_LONGROPE ? 2 : 1);
+  if (c->n_experts > 0) {
+    g.E = c->n_experts;
+    g.topk = c->n_experts_per_tok;
+    g.Fe = c->moe_ffn;
+    for (int l = 0; l < c->n_layers; ++l) g.moe_layers += !c->ffn_kind || c->ffn_kind[l] == FWD_FFN_MOE;
+  }
   return g;
 }
 
@@ -180,7 +212,9 @@ struct fwd_model {
   float* final_norm = nullptr;
   struct Layer {
     float *attn_norm, *ffn_norm, *post_attn, *post_ffn, *q_norm, *k_norm;
-    void *wqkv, *wo, *wgu, *wdown;
+    void *wqkv, *wo, *wgu, *wdown;  // MoE layers: wgu / wdown are the experts' stacks
+    void* router;                   // MoE layers: [E, H]
+    bool moe;
   };
   std::vector<Layer> layers;
 
@@ -199,6 +233,14 @@ struct fwd_model {
   float2* rope_tab[4] = {};  // [2 * local + long factors]: RoPE (cos, sin) tables of max_tokens rows
   std::vector<float> rope_short, rope_long;  // longrope factors (the config's arrays are borrowed)
   fwdk::SplitK sk{};  // workspace of the few-row products (bf16)
+  // mixture-of-experts workspace (models with MoE layers)
+  float* moe_logits = nullptr;  // [T, E]
+  int32_t* moe_idx = nullptr;   // [T, k]
+  float* moe_w = nullptr;       // [T, k]
+  fwdk::MoePlan plan{};
+  void* moe_x = nullptr;        // [moe_rows, H] bf16 K-tiled: token rows in expert order
+  void* moe_a = nullptr;        // [moe_rows, Fe] bf16 K-tiled: gated FFN activations
+  float* moe_y = nullptr;       // [moe_rows, H] fp32: expert outputs
   float* ssq = nullptr;  // [H / 64][kSkinnyRows] row sums of squares left by a few-row residual product
 
   // per-kernel-class event timing (fwd_set_timing)
@@ -413,7 +455,10 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
   const bool sandwich = cfg->norm_placement == FWD_NORM_SANDWICH;
   for (int l = 0; l < cfg->n_layers; ++l) {
     const fwd_layer_weights& L = w->layers[l];
-    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.ffn_norm || !L.w_gate || !L.w_up || !L.w_down ||
+    const bool moe = cfg->n_experts > 0 && (!cfg->ffn_kind || cfg->ffn_kind[l] == FWD_FFN_MOE);
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.ffn_norm ||
+        (!moe && (!L.w_gate || !L.w_up || !L.w_down)) ||
+        (moe && (!L.router || !L.expert_gate || !L.expert_up || !L.expert_down)) ||
         (sandwich && (!L.post_attn_norm || !L.post_ffn_norm)) || (cfg->qk_norm && (!L.q_norm || !L.k_norm)))
       return fail(FWD_E_WEIGHTS, "layer " + std::to_string(l) + " is missing a weight pointer");
   }
@@ -429,6 +474,7 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     m->rope_long.assign(cfg->rope_long_factor, cfg->rope_long_factor + cfg->head_dim / 2);
   }
   m->cfg.rope_short_factor = m->cfg.rope_long_factor = nullptr;
+  m->cfg.ffn_kind = nullptr;  // (read into each layer's flag at packing)
   m->dt = DType(cfg->dtype);
   m->g = geometry(cfg);
   m->stream = (hipStream_t)hip_stream;
@@ -451,7 +497,9 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     const size_t mv = append(identity_map((int)(g.Hkv * g.D), (int)((g.Hq + g.Hkv) * g.D)));
     const size_t mg = append(glu_row_map((int)g.F, C, 0));
     const size_t mu = append(glu_row_map((int)g.F, C, 1));
-    const size_t mid = append(identity_map((int)std::max(g.V, std::max(g.H, g.F)), 0));
+    const size_t mid = append(identity_map((int)std::max({g.V, g.H, g.F, g.E}), 0));
+    const size_t mge = append(glu_row_map((int)std::max<int64_t>(g.Fe, 1), C, 0));
+    const size_t mue = append(glu_row_map((int)std::max<int64_t>(g.Fe, 1), C, 1));
     int32_t* dmaps = nullptr;
     HIP_TRY(hipMalloc((void**)&dmaps, maps.size() * 4));
     struct Free {
@@ -511,14 +559,36 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
       if (int rc = put(L.wqkv, W.wq, mq, (int)(g.Hq * g.D), g.H)) return rc;
       if (int rc = put(L.wqkv, W.wk, mk, (int)(g.Hkv * g.D), g.H)) return rc;
       if (int rc = put(L.wqkv, W.wv, mv, (int)(g.Hkv * g.D), g.H)) return rc;
-      if (int rc = alloc_operand(&L.wgu, 2 * g.F, g.H)) return rc;
-      if (g.tiled) HIP_TRY(hipMemsetAsync(L.wgu, 0, g.rows(2 * g.F) * g.H * g.esize, s));
-      if (int rc = put(L.wgu, W.w_gate, mg, (int)g.F, g.H)) return rc;
-      if (int rc = put(L.wgu, W.w_up, mu, (int)g.F, g.H)) return rc;
+      L.moe = g.E > 0 && (!cfg->ffn_kind || cfg->ffn_kind[l] == FWD_FFN_MOE);
+      if (!L.moe) {
+        if (int rc = alloc_operand(&L.wgu, 2 * g.F, g.H)) return rc;
+        if (g.tiled) HIP_TRY(hipMemsetAsync(L.wgu, 0, g.rows(2 * g.F) * g.H * g.esize, s));
+        if (int rc = put(L.wgu, W.w_gate, mg, (int)g.F, g.H)) return rc;
+        if (int rc = put(L.wgu, W.w_up, mu, (int)g.F, g.H)) return rc;
+        if (int rc = alloc_operand(&L.wdown, g.H, g.F)) return rc;
+        if (int rc = place(L.wdown, g.H, W.w_down, mid, (int)g.H, g.F)) return rc;
+      } else {
+        // router [E, H]; per expert e: gate/up rows interleaved like the dense layer's
+        // at wgu + e * rows(2 Fe) * H, down at wdown + e * rows(H) * Fe (all K-tiled)
+        if (int rc = alloc_operand(&L.router, g.E, g.H)) return rc;
+        if (int rc = place(L.router, g.E, W.router, mid, (int)g.E, g.H)) return rc;
+        const int64_t gu_e = g.rows(2 * g.Fe) * g.H, d_e = g.rows(g.H) * g.Fe;
+        if (int rc = m->alloc(&L.wgu, g.E * gu_e * g.esize)) return rc;
+        if (int rc = m->alloc(&L.wdown, g.E * d_e * g.esize)) return rc;
+        HIP_TRY(hipMemsetAsync(L.wgu, 0, g.E * gu_e * g.esize, s));
+        HIP_TRY(hipMemsetAsync(L.wdown, 0, g.E * d_e * g.esize, s));
+        for (int64_t e = 0; e < g.E; ++e) {
+          char* gu = (char*)L.wgu + e * gu_e * g.esize;
+          const char* src_g = (const char*)W.expert_gate + e * g.Fe * g.H * g.esize;
+          const char* src_u = (const char*)W.expert_up + e * g.Fe * g.H * g.esize;
+          const char* src_d = (const char*)W.expert_down + e * g.H * g.Fe * g.esize;
+          if (int rc = put(gu, src_g, mge, (int)g.Fe, g.H)) return rc;
+          if (int rc = put(gu, src_u, mue, (int)g.Fe, g.H)) return rc;
+          if (int rc = put((char*)L.wdown + e * d_e * g.esize, src_d, mid, (int)g.H, g.Fe)) return rc;
+        }
+      }
       if (int rc = alloc_operand(&L.wo, g.H, g.Hq * g.D)) return rc;
       if (int rc = place(L.wo, g.H, W.wo, mid, (int)g.H, g.Hq * g.D)) return rc;
-      if (int rc = alloc_operand(&L.wdown, g.H, g.F)) return rc;
-      if (int rc = place(L.wdown, g.H, W.w_down, mid, (int)g.H, g.F)) return rc;
     }
     HIP_TRY(hipStreamSynchronize(s));  // the row maps are freed at scope end
 
@@ -540,6 +610,22 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     if (int rc = m->alloc((void**)&m->amax, T * 4)) return rc;
     if (int rc = m->alloc((void**)&m->flag, 256)) return rc;
     if (int rc = m->alloc((void**)&m->logits_ws, g.logit_chunk * g.V * 4)) return rc;
+    if (g.E > 0) {
+      const int64_t A = T * g.topk, nch = fwdk::moe_chunks(A);
+      if (int rc = m->alloc((void**)&m->moe_logits, T * g.E * 4)) return rc;
+      if (int rc = m->alloc((void**)&m->moe_idx, A * 4)) return rc;
+      if (int rc = m->alloc((void**)&m->moe_w, A * 4)) return rc;
+      if (int rc = m->alloc((void**)&m->plan.pos, A * 4)) return rc;
+      if (int rc = m->alloc((void**)&m->plan.chunk_count, nch * g.E * 4)) return rc;
+      if (int rc = m->alloc((void**)&m->plan.chunk_base, nch * g.E * 4)) return rc;
+      if (int rc = m->alloc((void**)&m->plan.total, g.E * 4)) return rc;
+      if (int rc = m->alloc((void**)&m->plan.seg_start, g.E * 4)) return rc;
+      if (int rc = m->alloc((void**)&m->plan.seg_count, g.E * 4)) return rc;
+      if (int rc = m->alloc((void**)&m->plan.mtile_start, (g.E + 1) * 4)) return rc;
+      if (int rc = m->alloc(&m->moe_x, g.moe_rows() * g.H * g.esize)) return rc;
+      if (int rc = m->alloc(&m->moe_a, g.moe_rows() * g.Fe * g.esize)) return rc;
+      if (int rc = m->alloc((void**)&m->moe_y, g.moe_rows() * g.H * 4)) return rc;
+    }
     if (g.tiled) {
       m->sk.part_floats = g.skinny_part_floats();
       m->sk.count_len = g.skinny_counters();
@@ -600,7 +686,7 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
   // Few rows, pre-norm, no hidden slots: each residual product also leaves its rows' sums
   // of squares, and the next product normalises its input itself (no norm launches
   // after the first).
-  const bool fuse = tl && M <= fwdk::kSkinnyRows && !sandwich && !hidden && L > 0;
+  const bool fuse = tl && M <= fwdk::kSkinnyRows && !sandwich && !hidden && L > 0 && g.moe_layers == 0;
   // RoPE tables of this call: per layer kind, and the longrope factor set its length selects
   float2* const* rope_tabs = sess ? sess->rope_tab : m->rope_tab;
   const int rope_set =
@@ -676,10 +762,40 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
     }
 
     // feed-forward sublayer
+    float* final32 = (last && hidden) ? hidden + (int64_t)(L + 1) * TH : nullptr;
+    if (w.moe) {
+      // mixture of experts on the normalised rows in m->n: route, permute by expert,
+      // grouped expert products, weighted combination (+ the residual for pre-norm)
+      const int E = (int)g.E, k = (int)g.topk, Fe = (int)g.Fe, A = M * k;
+      TIMED(m, FWD_KERNEL_MOE_ROUTE, fwdk::gemm_store(dt, m->n, w.router, m->moe_logits, E, M, E, H, 0.f, tl, s, sk));
+      TIMED(m, FWD_KERNEL_MOE_ROUTE, fwdk::moe_route(m->moe_logits, M, E, k, m->cfg.moe_norm_topk != 0, m->moe_idx,
+                                                     m->moe_w, s));
+      TIMED(m, FWD_KERNEL_MOE_ROUTE, fwdk::moe_plan(m->moe_idx, A, E, m->plan, s));
+      TIMED(m, FWD_KERNEL_MOE_ROUTE, fwdk::moe_gather(m->n, m->plan.pos, A, k, H, m->moe_x, s));
+      const int max_tiles = (A + fwdk::kMoeTileRows - 1) / fwdk::kMoeTileRows + E;
+      const fwdk::GroupArgs gu{m->plan.seg_start, m->plan.seg_count, m->plan.mtile_start, E, g.rows(2 * g.Fe) * H,
+                               max_tiles};
+      const fwdk::GroupArgs gd{m->plan.seg_start, m->plan.seg_count, m->plan.mtile_start, E, g.rows(g.H) * g.Fe,
+                               max_tiles};
+      TIMED(m, FWD_KERNEL_MOE_EXPERTS,
+            fwdk::gemm_grouped_swiglu(m->moe_x, w.wgu, m->moe_a, Fe, H, gu, m->cfg.ffn_act, s));
+      TIMED(m, FWD_KERNEL_MOE_EXPERTS, fwdk::gemm_grouped_store(m->moe_a, w.wdown, m->moe_y, H, Fe, gd, s));
+      if (!sandwich) {
+        TIMED(m, FWD_KERNEL_MOE_COMBINE,
+              fwdk::moe_combine(m->moe_y, m->plan.pos, m->moe_w, M, k, H, xmid, xout, s));
+        TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xout, next_norm, m->n, final32, M, H, eps, tl, s));
+      } else {
+        TIMED(m, FWD_KERNEL_MOE_COMBINE,
+              fwdk::moe_combine(m->moe_y, m->plan.pos, m->moe_w, M, k, H, nullptr, m->u, s));
+        TIMED(m, FWD_KERNEL_NORM,
+              fwdk::add_norm(dt, xmid, m->u, w.post_ffn, xout, next_norm, m->n, final32, M, H, eps, tl, s));
+      }
+      cur = xout;
+      continue;
+    }
     const fwdk::RowNormX nf = normx(xmid, w.ffn_norm);
     TIMED(m, FWD_KERNEL_GATE_UP,
           fwdk::gemm_swiglu(dt, m->n, w.wgu, m->a, M, F, H, tl, s, sk, fuse ? &nf : nullptr, m->cfg.ffn_act));
-    float* final32 = (last && hidden) ? hidden + (int64_t)(L + 1) * TH : nullptr;
     if (fuse) {
       TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, tl, s, sk, m->ssq));
     } else if (!sandwich) {
@@ -865,6 +981,18 @@ int fwd_rmsnorm(const float* x, const void* w, void* y, int32_t rows, int32_t hi
   if (!device_is_gfx950()) return fail(FWD_E_UNAVAILABLE, "no gfx950 device is available");
   HIP_TRY(fwdk::rmsnorm(DType(dtype), x, (const float*)w, y, nullptr, rows, hidden, eps, false,
                         (hipStream_t)hip_stream));
+  return FWD_OK;
+}
+
+int fwd_moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t norm_topk, int32_t* idx, float* w,
+                  void* hip_stream) {
+  if (T < 0 || E <= 0 || E > fwdk::kMoeMaxExperts || k < 1 || k > std::min(fwdk::kMoeMaxTopK, (int)E))
+    return fail(FWD_E_ARG, "need T >= 0, 1 <= E <= 256 and 1 <= k <= min(8, E)");
+  if (norm_topk != 0 && norm_topk != 1) return fail(FWD_E_ARG, "norm_topk must be 0 or 1");
+  if (T == 0) return FWD_OK;
+  if (!logits || !idx || !w) return fail(FWD_E_ARG, "NULL buffer");
+  if (!device_is_gfx950()) return fail(FWD_E_UNAVAILABLE, "no gfx950 device is available");
+  HIP_TRY(fwdk::moe_route(logits, T, E, k, norm_topk != 0, idx, w, (hipStream_t)hip_stream));
   return FWD_OK;
 }
 

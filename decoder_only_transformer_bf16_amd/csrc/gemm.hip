@@ -375,10 +375,14 @@ __device__ constexpr int need_frag(int n) {
   return n == 0 ? 0 : n == 1 ? TM : n <= TM ? n - 1 : n;
 }
 
-template <class C, class Epi, bool TILED>
+// GROUPED: one launch over the expert segments of a mixture-of-experts layer; the
+// workgroup's m-tile selects the expert (the last one whose first tile is at or
+// before it, so empty experts are skipped), whose X rows start at seg_start and whose
+// W is the e-th of a stack; output rows are the segment's rows.
+template <class C, class Epi, bool TILED, bool GROUPED = false>
 __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* __restrict__ X,
                                                                   const bf16_t* __restrict__ W, int M, int N, int K,
-                                                                  Epi epi) {
+                                                                  Epi epi, GroupArgs grp = GroupArgs{}) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::STAGES, NW = C::NW;
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN, KS = C::KS;
   constexpr int SLICE = (BM + BN) * BK;  // elements per stage
@@ -387,9 +391,26 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int nTM = (M + BM - 1) / BM, nTN = (N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, nTM, nTN, tm, tn);
+  const int nTN = (N + BN - 1) / BN;
+  int tm, tn, row0 = 0;
+  if constexpr (GROUPED) {
+    const int gm = blockIdx.x / nTN;
+    if (gm >= grp.mtile_start[grp.E]) return;  // past the last expert's tiles
+    int lo = 0, hi = grp.E;                     // mtile_start[lo] <= gm < mtile_start[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (grp.mtile_start[mid] <= gm) lo = mid;
+      else hi = mid;
+    }
+    tm = gm - grp.mtile_start[lo];
+    tn = blockIdx.x - gm * nTN;
+    row0 = grp.seg_start[lo];
+    M = grp.seg_count[lo];
+    X += (int64_t)row0 * K;  // (segments start on 16-row boundaries: whole K-tiled row blocks)
+    W += (int64_t)lo * grp.w_stride;
+  } else {
+    tile_coords(blockIdx.x, (M + BM - 1) / BM, nTN, tm, tn);
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   // (K-tiled operands are read in whole 16-row tiles: rows are padded to 16)
   const int mr = TILED ? (M + 15) / 16 * 16 : M, nr = TILED ? (N + 15) / 16 * 16 : N;
@@ -484,7 +505,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
     }
   }
 
-  write_tile<TM, TN>(epi, acc, m0 + wm * WTM, n0 + wn * WTN, M, N, lane);
+  write_tile<TM, TN>(epi, acc, row0 + m0 + wm * WTM, n0 + wn * WTN, row0 + M, N, lane);
 }
 
 template <class C, class Epi, bool TILED = false>
@@ -1045,6 +1066,32 @@ hipError_t launch_f32(const void* X, const void* W, int M, int N, int K, const E
 }
 
 }  // namespace
+
+namespace {
+template <class Epi>
+hipError_t launch_grouped(const void* X, const void* W, int N, int K, const Epi& epi, const GroupArgs& g,
+                          hipStream_t s) {
+  static_assert(CfgSmall::BM == kMoeTileRows, "the plan counts tiles of the grouped product's height");
+  if (g.max_tiles <= 0 || N <= 0) return hipSuccess;
+  if (K % 32 || g.E <= 0 || g.E > kMoeMaxExperts) return hipErrorInvalidValue;
+  const int grid = g.max_tiles * ((N + CfgSmall::BN - 1) / CfgSmall::BN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<CfgSmall, Epi, true, true>), dim3(grid), dim3(CfgSmall::NT), 0, s,
+                     (const bf16_t*)X, (const bf16_t*)W, 0, N, K, epi, g);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t gemm_grouped_swiglu(const void* X, const void* W, void* a, int F, int K, const GroupArgs& g, int act,
+                               hipStream_t s) {
+  if (act == 1) return launch_grouped(X, W, 2 * F, K, EpiSwiGLU<32, bf16_t, 1>{(bf16_t*)a, F, true}, g, s);
+  if (act != 0) return hipErrorInvalidValue;
+  return launch_grouped(X, W, 2 * F, K, EpiSwiGLU<32, bf16_t>{(bf16_t*)a, F, true}, g, s);
+}
+
+hipError_t gemm_grouped_store(const void* X, const void* W, float* Y, int N, int K, const GroupArgs& g,
+                              hipStream_t s) {
+  return launch_grouped(X, W, N, K, EpiStore<32>{Y, N, 0.f}, g, s);
+}
 
 int64_t skinny_part_floats(int M, int N, int K) {
   if (M <= 0 || N <= 0 || K < 32) return 0;

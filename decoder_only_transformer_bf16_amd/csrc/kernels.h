@@ -126,6 +126,45 @@ hipError_t pack_tiled(void* dst, const void* src, const int32_t* map, int rows, 
 // dst[i] = offset + float(src[i]) for a gain vector of dtype dt (offset 1: (1 + w) gains).
 hipError_t gains_to_f32(DType dt, const void* src, float* dst, int n, float offset, hipStream_t s);
 
+// ---- mixture of experts ----
+// Routing, permutation and combination of the MoE feed-forward (moe.hip); the expert
+// products are gemm_grouped_* below.
+constexpr int kMoeMaxExperts = 256, kMoeMaxTopK = 8;
+constexpr int kMoeTileRows = 128;  // rows per tile of the grouped products
+// idx[t, j], w[t, j] (j < k): the k largest logits of row t of logits [T, E] (lowest
+// index first on ties) and their softmax probabilities, renormalised when `norm`.
+hipError_t moe_route(const float* logits, int T, int E, int k, bool norm, int32_t* idx, float* w, hipStream_t s);
+// Device buffers of the permutation: chunk_count / chunk_base [moe_chunks(A) * E],
+// total / seg_start / seg_count [E], mtile_start [E + 1], pos [A].
+struct MoePlan {
+  int *chunk_count, *chunk_base, *total, *seg_start, *seg_count, *mtile_start;
+  int32_t* pos;
+};
+int64_t moe_chunks(int64_t A);
+// For the A = T * k assignments idx[]: pos[i] = the row of assignment i in the
+// expert-ordered matrix (expert segments 16-row aligned, token order inside), and per
+// expert seg_start / seg_count and mtile_start (prefix of ceil(count / kMoeTileRows)).
+hipError_t moe_plan(const int32_t* idx, int A, int E, const MoePlan& p, hipStream_t s);
+// xp row pos[i] = n row i / k (bf16 K-tiled, row width H).
+hipError_t moe_gather(const void* n, const int32_t* pos, int A, int k, int H, void* xp, hipStream_t s);
+// out[t] = (xin[t] if xin) + sum_j w[t, j] * y[pos[t * k + j]] (fp32 rows of H).
+hipError_t moe_combine(const float* y, const int32_t* pos, const float* w, int T, int k, int H, const float* xin,
+                       float* out, hipStream_t s);
+// Grouped products over the expert segments: X rows [seg_start[e], + seg_count[e]) times
+// expert e's W (W + e * w_stride elements, K-tiled), one launch for all experts.
+struct GroupArgs {
+  const int *seg_start, *seg_count, *mtile_start;
+  int E;
+  int64_t w_stride;
+  int max_tiles;  // upper bound of mtile_start[E] (sizes the grid)
+};
+// a[rows, F] = act(g) * u (K-tiled bf16, act as gemm_swiglu) with each expert's W packed
+// as interleaved gate/up chunks.
+hipError_t gemm_grouped_swiglu(const void* X, const void* W, void* a, int F, int K, const GroupArgs& g, int act,
+                               hipStream_t s);
+// Y[rows, N] fp32 (row stride N).
+hipError_t gemm_grouped_store(const void* X, const void* W, float* Y, int N, int K, const GroupArgs& g, hipStream_t s);
+
 // ---- QK-norm ----
 // In place on qkv [rows, ld] (as gemm_qkv_rope writes it without rotation): every q head
 // (gains gq [D]) and k head (gains gk [D]) is RMS-normalised over its D values, then

@@ -31,13 +31,14 @@ NORM = {"pre": 0, "sandwich": 1}
 LAYER = {"global": 0, "local": 1}
 FFN_ACT = {"silu": 0, "gelu_tanh": 1}
 ROPE_SCALING = {"none": 0, "llama3": 1, "longrope": 2}
+FFN_KIND = {"dense": 0, "moe": 1}
 
 EXPORTS = ("fwd_available", "fwd_create", "fwd_output_sizes", "fwd_prefill", "fwd_gemm", "fwd_attention",
            "fwd_rmsnorm", "fwd_set_timing", "fwd_get_timing", "fwd_destroy", "fwd_last_error",
            "fwd_session_create", "fwd_session_prefill", "fwd_session_decode", "fwd_session_length",
-           "fwd_session_destroy")
+           "fwd_session_destroy", "fwd_moe_route")
 KERNEL_CLASSES = ("embed", "norm", "qkv_rope", "attention", "o_proj", "gate_up", "down_proj", "lm_head", "argmax",
-                  "v_transpose", "qk_norm")
+                  "v_transpose", "qk_norm", "moe_route", "moe_experts", "moe_combine")
 
 c_i32, c_i64, c_f32, c_f64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -51,12 +52,15 @@ class FwdConfig(ctypes.Structure):
                 ("qk_norm", c_i32), ("norm_gain_offset", c_i32), ("ffn_act", c_i32), ("rope_theta_local", c_f64),
                 ("rope_scaling", c_i32), ("rope_factor", c_f32), ("rope_low_freq_factor", c_f32),
                 ("rope_high_freq_factor", c_f32), ("rope_original_max_pos", c_i32),
-                ("rope_short_factor", ctypes.POINTER(c_f32)), ("rope_long_factor", ctypes.POINTER(c_f32))]
+                ("rope_short_factor", ctypes.POINTER(c_f32)), ("rope_long_factor", ctypes.POINTER(c_f32)),
+                ("n_experts", c_i32), ("n_experts_per_tok", c_i32), ("moe_ffn", c_i32), ("moe_norm_topk", c_i32),
+                ("ffn_kind", ctypes.POINTER(c_i32))]
 
 
 class FwdLayerWeights(ctypes.Structure):
     _fields_ = [(n, c_vp) for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down",
-                                    "post_attn_norm", "post_ffn_norm", "q_norm", "k_norm")]
+                                    "post_attn_norm", "post_ffn_norm", "q_norm", "k_norm", "router",
+                                    "expert_gate", "expert_up", "expert_down")]
 
 
 class FwdWeights(ctypes.Structure):
@@ -101,6 +105,8 @@ def lib() -> ctypes.CDLL:
         L.fwd_attention.restype = c_i32
         L.fwd_rmsnorm.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_f32, c_i32, c_vp]
         L.fwd_rmsnorm.restype = c_i32
+        L.fwd_moe_route.argtypes = [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
+        L.fwd_moe_route.restype = c_i32
         L.fwd_set_timing.argtypes = [c_vp, c_i32]
         L.fwd_set_timing.restype = c_i32
         L.fwd_get_timing.argtypes = [c_vp, c_i32, ctypes.POINTER(c_f64), ctypes.POINTER(c_i64)]
@@ -153,6 +159,15 @@ def make_config(cfg, max_tokens: int):
     c.rope_low_freq_factor = float(getattr(cfg, "rope_low_freq_factor", 1.0))
     c.rope_high_freq_factor = float(getattr(cfg, "rope_high_freq_factor", 4.0))
     c.rope_original_max_pos = int(getattr(cfg, "rope_original_max_pos", 0))
+    if getattr(cfg, "n_experts", 0) > 0:
+        c.n_experts = int(cfg.n_experts)
+        c.n_experts_per_tok = int(cfg.n_experts_per_tok)
+        c.moe_ffn = int(cfg.moe_ffn)
+        c.moe_norm_topk = 1 if getattr(cfg, "moe_norm_topk", True) else 0
+        kinds_ffn = cfg.ffn_kinds() if hasattr(cfg, "ffn_kinds") else tuple(cfg.ffn_kind)
+        arr = (c_i32 * max(1, len(kinds_ffn)))(*[FFN_KIND[k] for k in kinds_ffn])
+        keep.append(arr)
+        c.ffn_kind = ctypes.cast(arr, ctypes.POINTER(c_i32))
     for field in ("rope_short_factor", "rope_long_factor"):
         vals = tuple(getattr(cfg, field, ()) or ())
         if vals:
@@ -184,7 +199,8 @@ class Model:
     """A model on the current GPU: fwd_create at construction, fwd_destroy on close()."""
 
     LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down",
-                    "post_attn_norm", "post_ffn_norm", "q_norm", "k_norm")
+                    "post_attn_norm", "post_ffn_norm", "q_norm", "k_norm", "router", "expert_gate", "expert_up",
+                    "expert_down")
 
     def __init__(self, cfg, weights: Mapping[str, "object"], max_tokens: int, stream=None):
         self.cfg = cfg
@@ -336,3 +352,14 @@ def rmsnorm(x, w, eps: float, dtype: str = "bf16", y=None, stream=None):
         y = torch.empty((rows, H), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device=x.device)
     _check(lib().fwd_rmsnorm(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows, H, eps, DTYPE[dtype], _stream(stream)))
     return y
+
+
+def moe_route(logits, k: int, norm_topk: bool = True, stream=None):
+    """fwd_moe_route: router logits fp32 [T, E] -> (idx int32 [T, k], w fp32 [T, k])."""
+    import torch
+    T, E = logits.shape
+    idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().fwd_moe_route(logits.data_ptr(), T, E, k, 1 if norm_topk else 0, idx.data_ptr(), w.data_ptr(),
+                               _stream(stream)))
+    return idx, w

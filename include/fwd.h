@@ -57,6 +57,8 @@ extern "C" {
 #define FWD_ROPE_NONE 0
 #define FWD_ROPE_LLAMA3 1   /* llama3 frequency bands                          */
 #define FWD_ROPE_LONGROPE 2 /* phi3 longrope per-frequency factors             */
+#define FWD_FFN_DENSE 0     /* the layer's feed-forward is the dense gated FFN */
+#define FWD_FFN_MOE 1       /* mixture of experts                              */
 
 /*
  * Model description ("pegainfer issue #878", Proposed Plan: one typed config,
@@ -101,6 +103,20 @@ extern "C" {
  *                       host arrays of head_dim / 2 positive floats (longrope), read
  *                       during fwd_create only
  *
+ * Mixture of experts (the qwen3moe hybrid dense/sparse axis of the same Theorem
+ * statement; the forward-parity intro lists the MoE FFN), bf16 only:
+ *  n_experts            E (0 = dense everywhere; at most 256)
+ *  n_experts_per_tok    k (1 .. min(8, E))
+ *  moe_ffn              F_e, width of each expert's gated FFN (multiple of 32)
+ *  moe_norm_topk        1: the k weights are renormalised to sum 1
+ *  ffn_kind             host array of n_layers FWD_FFN_DENSE / FWD_FFN_MOE values, read
+ *                       during fwd_create only; NULL = every layer MoE when n_experts > 0
+ * A MoE layer's feed-forward output for a token is sum_j w_j FFN_{e_j}(n): e_1..e_k
+ * are the experts with the k largest router logits n·W_routerᵀ (the softmax is
+ * monotone; lowest index first on ties) and w_j their softmax probabilities over all E
+ * experts, renormalised when moe_norm_topk. FFN_e is the gated FFN (ffn_act) with
+ * expert e's matrices.
+ *
  * Supported: bf16 needs head_dim in {64, 128, 256}; f32 needs head_dim <= 64;
  * hidden, Hq*D, Hkv*D and ffn multiples of 8 (bf16) or 4 (f32); bf16 additionally
  * needs hidden, Hq*D, Hkv*D and ffn multiples of 32 (its GEMM operands are stored in
@@ -129,6 +145,12 @@ typedef struct fwd_config {
   int32_t rope_original_max_pos;
   const float* rope_short_factor;
   const float* rope_long_factor;
+  /* mixture of experts (appended; zero = dense) */
+  int32_t n_experts;
+  int32_t n_experts_per_tok;
+  int32_t moe_ffn;
+  int32_t moe_norm_topk;
+  const int32_t* ffn_kind;
 } fwd_config;
 
 /*
@@ -138,6 +160,9 @@ typedef struct fwd_config {
  *  w_gate [F, H], w_up [F, H], w_down [H, F], *_norm [H].
  *  post_attn_norm / post_ffn_norm are read only for FWD_NORM_SANDWICH;
  *  q_norm / k_norm [D] only with qk_norm.
+ *  MoE layers read router [E, H], expert_gate and expert_up [E, F_e, H] and
+ *  expert_down [E, H, F_e] (each expert's matrix contiguous, row-major) instead of
+ *  w_gate / w_up / w_down.
  */
 typedef struct fwd_layer_weights {
   const void* attn_norm;
@@ -153,6 +178,10 @@ typedef struct fwd_layer_weights {
   const void* post_ffn_norm;
   const void* q_norm;
   const void* k_norm;
+  const void* router;
+  const void* expert_gate;
+  const void* expert_up;
+  const void* expert_down;
 } fwd_layer_weights;
 
 /* embed [V, H] (also the tied LM head), final_norm [H]: device pointers;
@@ -260,6 +289,17 @@ int fwd_rmsnorm(const float* x, const void* w, void* y, int32_t rows, int32_t hi
                 int32_t dtype, void* hip_stream);
 
 /*
+ * Mixture-of-experts routing alone (the decision inside a MoE layer; see fwd_config):
+ * for each of T rows of router logits [T, E] (device fp32), idx[t, j] (device int32
+ * [T, k]) = the experts with the k largest logits, largest first, lowest index first
+ * on ties; w[t, j] (device fp32 [T, k]) = their softmax probabilities over all E,
+ * divided by their sum when norm_topk. 1 <= k <= min(8, E), E <= 256.
+ * Errors: FWD_E_ARG, FWD_E_UNAVAILABLE, FWD_E_HIP.
+ */
+int fwd_moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t norm_topk, int32_t* idx, float* w,
+                  void* hip_stream);
+
+/*
  * Per-kernel timing of fwd_prefill with HIP events recorded on the model's stream
  * around every launch (off by default). Kernel classes:
  */
@@ -274,7 +314,10 @@ int fwd_rmsnorm(const float* x, const void* w, void* y, int32_t rows, int32_t hi
 #define FWD_KERNEL_ARGMAX 8        /* per-position argmax + non-finite check      */
 #define FWD_KERNEL_V_TRANSPOSE 9   /* values transposed to keys-contiguous order  */
 #define FWD_KERNEL_QK_NORM 10      /* QK-norm + RoPE pass (qk_norm models)        */
-#define FWD_KERNEL_CLASSES 11
+#define FWD_KERNEL_MOE_ROUTE 11    /* router product, top-k, permutation, gather  */
+#define FWD_KERNEL_MOE_EXPERTS 12  /* grouped expert products                     */
+#define FWD_KERNEL_MOE_COMBINE 13  /* weighted sum of the expert outputs          */
+#define FWD_KERNEL_CLASSES 14
 /* enable != 0 turns timing on and clears the accumulated totals; 0 turns it off. */
 int fwd_set_timing(fwd_model* m, int32_t enable);
 /* Accumulated milliseconds and launch count of one kernel class since the last

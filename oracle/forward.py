@@ -293,12 +293,16 @@ def moe_route(logits, top_k: int, norm_topk: bool):
     return idx, w
 
 
-def moe_ffn(n, router, expert_gate, expert_up, expert_down, top_k: int, norm_topk: bool, act: str = "silu"):
+def moe_ffn(n, router, expert_gate, expert_up, expert_down, top_k: int, norm_topk: bool, act: str = "silu",
+            logits_out=None):
     """Mixture-of-experts feed-forward of rows n [..., H]: d = sum over the token's top_k
     experts e of w_e * (act(n W_g,e^T) * (n W_u,e^T)) W_d,e^T, in expert-rank order.
     expert_* are [E, F_e, H] / [E, H, F_e] row-major stacks (published qwen3moe form)."""
     n2 = np.asarray(n).reshape(-1, np.shape(n)[-1])
-    idx, w = moe_route(gemm(n2, router), top_k, norm_topk)
+    z = gemm(n2, router)
+    if logits_out is not None:  # (test hook: the router logits that decided the routing)
+        logits_out.append(z)
+    idx, w = moe_route(z, top_k, norm_topk)
     out = np.zeros((n2.shape[0], np.shape(expert_down)[1]), dtype=np.float64)
     for e in np.unique(idx):
         rows, slot = np.nonzero(idx == e)
@@ -329,7 +333,8 @@ def argmax(z) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- whole forward
-def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = True, bf16_points: bool = False):
+def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = True, bf16_points: bool = False,
+            trace=None):
     """The prefill forward pass over a batch of prompts.
 
     cfg: an object with the geometry fields n_layers, hidden, n_heads, n_kv_heads,
@@ -345,6 +350,8 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
     input (normalised activations, rotated q / k, v, attention probabilities and
     output, SwiGLU output) to bf16, as a bf16 implementation does.
     Slots ([fp] Theorem 1): 0 = embedding, l+1 = after layer l, L+1 = final norm.
+    trace: optional dict; receives "moe_logits.<l>" = the router logits [B*S, E] of each
+    mixture-of-experts layer (to judge how decided the routing was).
     """
     ids = np.asarray(ids)
     B, S = ids.shape
@@ -391,8 +398,11 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
         # feed-forward sublayer (dense, or mixture of experts on the layers the map names)
         n = rb(rmsnorm(x, weights[p + "ffn_norm"], eps, goff))
         if ffn_kinds[l] == "moe":
+            zs = [] if trace is not None else None
             d = moe_ffn(n, weights[p + "router"], weights[p + "expert_gate"], weights[p + "expert_up"],
-                        weights[p + "expert_down"], cfg.n_experts_per_tok, cfg.moe_norm_topk, act)
+                        weights[p + "expert_down"], cfg.n_experts_per_tok, cfg.moe_norm_topk, act, zs)
+            if trace is not None:
+                trace[f"moe_logits.{l}"] = zs[0]
         else:
             a = rb(gated_ffn(gemm(n, weights[p + "w_gate"]), gemm(n, weights[p + "w_up"]), act))
             d = gemm(a, weights[p + "w_down"])
