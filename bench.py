@@ -156,6 +156,51 @@ def variant_leg(fwd, cfg0, ids, steps, stream):
                              "frac": qk_bytes / (qk_us * 1e-6) / 1e9 / PEAK_HBM_GBS}}
 
 
+def moe_leg(fwd, steps, stream):
+    """Mixture-of-experts layers at a 30B-A3B-style shape (hidden 2048, 32/4 heads x 128,
+    128 experts of width 768, top-8, vocab 151936), a 4-layer slice, prefill 8 x 2048:
+    per-kernel-class times and the grouped expert products against the bf16 peak
+    (algorithmic flops: 2 * T * k * H * 2 F_e for gate/up plus 2 * T * k * F_e * H for
+    down per layer)."""
+    import torch
+    from synth import workloads as wl
+    from tests.gpu_util import to_device
+    cfg = wl.ModelConfig("moe-30b-a3b-shape-4L", 4, 2048, 32, 4, 128, 6144, 151936, rope_theta=1e6, qk_norm=True,
+                         n_experts=128, n_experts_per_tok=8, moe_ffn=768, batch=8, seq=2048)
+    B, S = cfg.batch, cfg.seq
+    T = B * S
+    weights = {n: to_device(wl.draw_weight(cfg, n)) for n in wl.weight_shapes(cfg)}
+    model = fwd.Model(cfg, weights, max_tokens=T, stream=stream)
+    del weights
+    torch.cuda.empty_cache()
+    ids = wl.draw_ids(cfg)
+    argmax = torch.empty((B, S), dtype=torch.int32, device="cuda")
+    model.prefill_into(ids, None, None, argmax)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps):
+        model.prefill_into(ids, None, None, argmax)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t) * 1000.0 / steps
+    model.set_timing(True)
+    model.prefill_into(ids, None, None, argmax)
+    torch.cuda.synchronize()
+    timing = model.timing()
+    model.set_timing(False)
+    model.close()
+    k, H, Fe, L = cfg.n_experts_per_tok, cfg.hidden, cfg.moe_ffn, cfg.n_layers
+    expert_flops = L * (2 * T * k * H * 2 * Fe + 2 * T * k * Fe * H)
+    ex = timing["moe_experts"]["ms"]
+    log(f"moe: {ms:.2f} ms per 4-layer step, expert products {ex:.2f} ms")
+    return {"config": "4 layers of a MoE shape: hidden 2048, 32/4 heads x 128 (QK-norm), 128 experts x 768, top-8, "
+                      "vocab 151936; prefill 8 x 2048, argmax only",
+            "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "kernels_ms_per_step": {n: v["ms"] for n, v in timing.items() if v["launches"]},
+            "expert_products": {"bound": "mfma", "tflops": expert_flops / (ex * 1e-3) / 1e12,
+                                "frac": expert_flops / (ex * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                "algorithmic_tflop_per_step": expert_flops / 1e12}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +213,7 @@ def main():
                     help="greedy decode steps timed on a cached session after the prefill (0: skip)")
     ap.add_argument("--variant-leg", action="store_true",
                     help="also time the same shape with QK-norm, tanh-GELU gating and llama3 rope scaling")
+    ap.add_argument("--moe-leg", action="store_true", help="also time mixture-of-experts layers (4-layer slice)")
     args = ap.parse_args()
     if args.timing_steps < 1:
         ap.error("--timing-steps must be at least 1 (the roofline comes from those steps)")
@@ -299,6 +345,9 @@ def main():
     torch.cuda.empty_cache()
     if args.variant_leg:
         result["variants"] = variant_leg(fwd, cfg, ids, max(args.steps, 1), stream)
+        torch.cuda.empty_cache()
+    if args.moe_leg:
+        result["moe"] = moe_leg(fwd, max(args.steps, 1), stream)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the oracle on a bounded sample")

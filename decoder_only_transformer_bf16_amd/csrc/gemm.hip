@@ -375,6 +375,31 @@ __device__ constexpr int need_frag(int n) {
   return n == 0 ? 0 : n == 1 ? TM : n <= TM ? n - 1 : n;
 }
 
+// Grouped launches: m-tile gm belongs to the last expert whose first tile is at or
+// before it (so experts without rows are skipped). group_tile gives the tile's
+// coordinates within that expert, the expert's first row and its row count, or false
+// past the last expert's tiles.
+__device__ __forceinline__ int group_expert(const GroupArgs& g, int gm) {
+  int lo = 0, hi = g.E;  // mtile_start[lo] <= gm < mtile_start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.mtile_start[mid] <= gm) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+__device__ __forceinline__ bool group_tile(const GroupArgs& g, int block, int nTN, int& tm, int& tn, int& row0,
+                                           int& rows) {
+  const int gm = block / nTN;
+  if (gm >= g.mtile_start[g.E]) return false;
+  const int e = group_expert(g, gm);
+  tm = gm - g.mtile_start[e];
+  tn = block - gm * nTN;
+  row0 = g.seg_start[e];
+  rows = g.seg_count[e];
+  return true;
+}
+
 // GROUPED: one launch over the expert segments of a mixture-of-experts layer; the
 // workgroup's m-tile selects the expert (the last one whose first tile is at or
 // before it, so empty experts are skipped), whose X rows start at seg_start and whose
@@ -394,20 +419,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
   const int nTN = (N + BN - 1) / BN;
   int tm, tn, row0 = 0;
   if constexpr (GROUPED) {
-    const int gm = blockIdx.x / nTN;
-    if (gm >= grp.mtile_start[grp.E]) return;  // past the last expert's tiles
-    int lo = 0, hi = grp.E;                     // mtile_start[lo] <= gm < mtile_start[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (grp.mtile_start[mid] <= gm) lo = mid;
-      else hi = mid;
-    }
-    tm = gm - grp.mtile_start[lo];
-    tn = blockIdx.x - gm * nTN;
-    row0 = grp.seg_start[lo];
-    M = grp.seg_count[lo];
+    if (!group_tile(grp, blockIdx.x, nTN, tm, tn, row0, M)) return;
     X += (int64_t)row0 * K;  // (segments start on 16-row boundaries: whole K-tiled row blocks)
-    W += (int64_t)lo * grp.w_stride;
+    W += (int64_t)group_expert(grp, blockIdx.x / nTN) * grp.w_stride;
   } else {
     tile_coords(blockIdx.x, (M + BM - 1) / BM, nTN, tm, tn);
   }
@@ -549,9 +563,9 @@ struct PPCfg {
   static_assert((STAGES - 2) * LOADS < 64, "vmcnt range");
 };
 
-template <class C, class Epi, bool TILED>
+template <class C, class Epi, bool TILED, bool GROUPED = false>
 __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
-                                                        int M, int N, int K, Epi epi) {
+                                                        int M, int N, int K, Epi epi, GroupArgs grp = GroupArgs{}) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::STAGES, NW = C::NW;
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN, KS = C::KS;
   constexpr int SLICE = (BM + BN) * BK, LA = C::LOADS_A, LT = C::LOADS, FR = TM + TN;
@@ -561,9 +575,15 @@ __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = wave >> 2;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int nTM = (M + BM - 1) / BM, nTN = (N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, nTM, nTN, tm, tn);
+  const int nTN = (N + BN - 1) / BN;
+  int tm, tn, row0 = 0;
+  if constexpr (GROUPED) {
+    if (!group_tile(grp, blockIdx.x, nTN, tm, tn, row0, M)) return;
+    X += (int64_t)row0 * K;
+    W += (int64_t)group_expert(grp, blockIdx.x / nTN) * grp.w_stride;
+  } else {
+    tile_coords(blockIdx.x, (M + BM - 1) / BM, nTN, tm, tn);
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   // (K-tiled operands are read in whole 16-row tiles: rows are padded to 16)
   const int mr = TILED ? (M + 15) / 16 * 16 : M, nr = TILED ? (N + 15) / 16 * 16 : N;
@@ -695,7 +715,7 @@ __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict
   }
   if (group == 0) lds_barrier();  // matches group 1's extra barrier
 
-  write_tile<TM, TN>(epi, acc, m0 + wm * WTM, n0 + wn * WTN, M, N, lane);
+  write_tile<TM, TN>(epi, acc, row0 + m0 + wm * WTM, n0 + wn * WTN, row0 + M, N, lane);
 }
 
 // 8 wavefronts (two per SIMD) in ping-pong, 64 x 128 outputs each, four K slices of
@@ -1071,11 +1091,11 @@ namespace {
 template <class Epi>
 hipError_t launch_grouped(const void* X, const void* W, int N, int K, const Epi& epi, const GroupArgs& g,
                           hipStream_t s) {
-  static_assert(CfgSmall::BM == kMoeTileRows, "the plan counts tiles of the grouped product's height");
+  static_assert(CfgBig::BM == kMoeTileRows, "the plan counts tiles of the grouped product's height");
   if (g.max_tiles <= 0 || N <= 0) return hipSuccess;
   if (K % 32 || g.E <= 0 || g.E > kMoeMaxExperts) return hipErrorInvalidValue;
-  const int grid = g.max_tiles * ((N + CfgSmall::BN - 1) / CfgSmall::BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<CfgSmall, Epi, true, true>), dim3(grid), dim3(CfgSmall::NT), 0, s,
+  const int grid = g.max_tiles * ((N + CfgBig::BN - 1) / CfgBig::BN);
+  hipLaunchKernelGGL((gemm_pp_kernel<CfgBig, Epi, true, true>), dim3(grid), dim3(CfgBig::NT), 0, s,
                      (const bf16_t*)X, (const bf16_t*)W, 0, N, K, epi, g);
   return hipGetLastError();
 }

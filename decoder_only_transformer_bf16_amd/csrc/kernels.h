@@ -130,7 +130,7 @@ hipError_t gains_to_f32(DType dt, const void* src, float* dst, int n, float offs
 // Routing, permutation and combination of the MoE feed-forward (moe.hip); the expert
 // products are gemm_grouped_* below.
 constexpr int kMoeMaxExperts = 256, kMoeMaxTopK = 8;
-constexpr int kMoeTileRows = 128;  // rows per tile of the grouped products
+constexpr int kMoeTileRows = 256;  // rows per tile of the grouped products
 // idx[t, j], w[t, j] (j < k): the k largest logits of row t of logits [T, E] (lowest
 // index first on ties) and their softmax probabilities, renormalised when `norm`.
 hipError_t moe_route(const float* logits, int T, int E, int k, bool norm, int32_t* idx, float* w, hipStream_t s);
