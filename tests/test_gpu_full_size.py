@@ -87,12 +87,23 @@ def _whole_output_properties(out):
     assert torch.equal(picked, z.max(-1).values), "argmax is not a maximiser of its row"
 
 
-def test_llama3_8b_full_batch_sampled(fwd):
+@pytest.fixture(scope="module")
+def llama(fwd):
+    """The Llama-3-8B-shaped model, its host weights and the batch's ids, shared by the
+    tests below (results they hand on go in `state`)."""
     import torch
     cfg = wl.LLAMA3_8B
     _say("llama3-8b-shape: drawing and uploading 7.5e9 weights")
     model, host = _build(fwd, cfg, cfg.batch * cfg.seq)
     ids = wl.draw_ids(cfg)
+    yield {"cfg": cfg, "model": model, "host": host, "ids": ids, "state": {}}
+    model.close()
+    torch.cuda.empty_cache()
+
+
+def test_llama3_8b_full_batch_sampled(fwd, llama):
+    import torch
+    cfg, model, host, ids, st = llama["cfg"], llama["model"], llama["host"], llama["ids"], llama["state"]
     _say("prefill 8 x 2048 (the benchmark's launch)")
     out = model.prefill(ids, logits=True, hidden=True, argmax=True)
     torch.cuda.synchronize()
@@ -104,18 +115,19 @@ def test_llama3_8b_full_batch_sampled(fwd):
     # a row alone reproduces the same row of the batch, bit for bit
     again = model.prefill(ids[7:8], logits=True, hidden=False, argmax=True)
     assert torch.equal(again["logits"][0], out["logits"][7])
-    # cached session at full size: prefill the first 2046 tokens of every row, then
-    # decode tokens 2046 and 2047 (teacher-forced) over the 8-chunk cache; each step
-    # must give the cacheless prefill's logits at that position
-    # Both are bf16 computations that round at different points (the cached step keeps
-    # the probabilities in fp32), so between them the half-precision gate applies. Row
-    # 0 at position 2046 is also checked against the oracle (a 2047-token, 32-layer
-    # forward on the host). That deep, the oracle itself rounded to bf16 at the GPU's
-    # rounding points sits near the 0.999 gate, so there the gate is the floor-relative
-    # one of the hidden slots without the 0.999 minimum.
-    ref_z = out["logits"][:, 2046:].cpu().numpy()
+    st["cacheless_z"] = out["logits"][:, 2046:].cpu().numpy()   # positions 2046 and 2047
     del out, again
     torch.cuda.empty_cache()
+
+
+def test_llama3_8b_cached_decode(fwd, llama):
+    """Cached session at full size: prefill the first 2046 tokens of every row, then
+    decode tokens 2046 and 2047 (teacher-forced) over the 8-chunk cache. Both this and
+    the cacheless prefill are bf16 computations that round at different points (the
+    cached step keeps the probabilities in fp32), so between them the half-precision
+    gate applies, with argmax parity."""
+    model, ids, st = llama["model"], llama["ids"], llama["state"]
+    ref_z = st["cacheless_z"]
     _say("session: prefill 8 x 2046, decode positions 2046 and 2047")
     sess = fwd.Session(model, max_batch=8, max_seq=2048)
     sess.prefill(ids[:, :2046], logits=False, argmax=False)
@@ -131,19 +143,33 @@ def test_llama3_8b_full_batch_sampled(fwd):
         _say(f"  position {pos}: lowest row cosine cached vs cacheless {worst:.6f}, "
              f"max|d| {np.abs(z - ref_z[:, i]).max():.3e}, argmax pinned {pinned} near-tie {near}")
     sess.close()
+    st["cached_z"] = cached[0]
+
+
+def test_llama3_8b_position_2046_against_oracle(fwd, llama):
+    """Row 0 at position 2046, cached and cacheless, against the oracle (a 2047-token,
+    32-layer forward on the host)."""
+    cfg, host, ids, st = llama["cfg"], llama["host"], llama["ids"], llama["state"]
     _say("  oracle: row 0, positions 0..2046 (host forward, about a minute)")
     zo = oracle.forward(cfg, host, ids[:1, :2047], want_hidden=False)["logits"][:, -1]
-    c_cached, c_plain = cosine(cached[0][:1], zo), cosine(ref_z[:1, 0], zo)
+    c_cached, c_plain = cosine(st["cached_z"][:1], zo), cosine(st["cacheless_z"][:1, 0], zo)
     _say(f"  position 2046 vs oracle: cached {c_cached:.6f}, cacheless {c_plain:.6f}")
+    pinned, near, fails = argmax_check(np.argmax(st["cached_z"][:1], -1), zo, st["cached_z"][:1])
+    assert not fails, fails
+    st["oracle_z"], st["cos"] = zo, (c_cached, c_plain)
+
+
+def test_llama3_8b_position_2046_bf16_floor(fwd, llama):
+    """That deep, the oracle itself rounded to bf16 at the GPU's rounding points sits
+    near the 0.999 gate, so the gate here is the floor-relative one of the hidden slots
+    without the 0.999 minimum."""
+    cfg, host, ids, st = llama["cfg"], llama["host"], llama["ids"], llama["state"]
     _say("  oracle rounded at the bf16 points, same row and positions (about two minutes)")
     zb = oracle.forward(cfg, host, ids[:1, :2047], want_hidden=False, bf16_points=True)["logits"][:, -1]
-    floor = cosine(zb, zo)
+    floor = cosine(zb, st["oracle_z"])
     _say(f"  bf16-rounded oracle vs oracle at position 2046: {floor:.6f}")
-    for c in (c_cached, c_plain):
+    for c in st["cos"]:
         assert (1.0 - c) <= FLOOR_SLACK * (1.0 - floor) + 2e-6, (c, floor)
-    pinned, near, fails = argmax_check(np.argmax(cached[0][:1], -1), zo, cached[0][:1])
-    assert not fails, fails
-    model.close()
 
 
 def test_gemma3_style_full_model(fwd):
