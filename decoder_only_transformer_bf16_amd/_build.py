@@ -58,9 +58,11 @@ if __name__ == "__main__":
 
 def source_digest(files=("gemm.hip", "common.h", "kernels.h")) -> str:
     """sha256 over the GEMM kernel sources and the compile flags (ties stored counter
-    data to the kernel it measured)."""
+    data to the kernel it measured). Include paths enter relative to the repository
+    root, so a copy of the tree elsewhere has the same digest."""
     import hashlib
-    h = hashlib.sha256(" ".join(FLAGS).encode())
+    flags = [os.path.relpath(f, ROOT) if os.path.isabs(f) else f for f in FLAGS]
+    h = hashlib.sha256(" ".join(flags).encode())
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())

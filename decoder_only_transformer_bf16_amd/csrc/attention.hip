@@ -90,9 +90,17 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, float sca
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 31, lg = lane >> 5;
-  const int qb = gridDim.x - 1 - blockIdx.x;  // longest query blocks first
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (a.Hq / a.Hkv);
+  // One linear grid, decoded so that workgroups are dispatched longest query block
+  // first across all heads and batch rows (causal work grows with the block index),
+  // and so that the query heads of one KV head keep the same id modulo the number of
+  // (batch row, KV head) pairs, which sends them to the same XCD when that number is
+  // a multiple of 8.
+  const int G = a.Hq / a.Hkv, BG = a.B * a.Hkv;
+  const int per = a.Hq * a.B, nqb = gridDim.x / per;
+  const int id = blockIdx.x, qo = id / per, rem = id - qo * per;
+  const int hi = rem / BG, bg = rem - hi * BG;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv, h = g * G + hi;
+  const int qb = nqb - 1 - qo;
   const int S = a.S, W = a.window;
   const int q0 = qb * BQ;
   const int wq0 = q0 + wave * QW;
@@ -372,11 +380,11 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
   // SIMD without spilling (D = 64), and only when the grid stays full
   if constexpr (D == 64) {
     if (heads * ((a.S + 255) / 256) >= 512) {
-      hipLaunchKernelGGL((attn_bf16_kernel<D, 2, 3>), dim3((a.S + 255) / 256, a.Hq, a.B), blk, 0, s, a, sl);
+      hipLaunchKernelGGL((attn_bf16_kernel<D, 2, 3>), dim3((a.S + 255) / 256 * heads), blk, 0, s, a, sl);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 3>), dim3((a.S + 127) / 128, a.Hq, a.B), blk, 0, s, a, sl);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 3>), dim3((a.S + 127) / 128 * heads), blk, 0, s, a, sl);
   return hipGetLastError();
 }
 
