@@ -334,7 +334,7 @@ def main():
         "modes": {"all_outputs": {"ms_per_step": ms_per_step, "tokens_per_s": T * args.steps / elapsed,
                                   "outputs": "fp32 logits, argmax" + ("" if args.no_hidden else ", hidden slots")},
                   "argmax_only": {"ms_per_step": ms_argmax_only, "tokens_per_s": T / (ms_argmax_only * 1e-3),
-                                  "outputs": "argmax (logits kept in a 1024-row workspace)"}},
+                                  "outputs": "argmax only (folded into the LM-head epilogue; no logits or slots written)"}},
     }
     if args.decode_steps > 0:
         del logits, hidden

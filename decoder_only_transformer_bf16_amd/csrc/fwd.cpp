@@ -137,6 +137,10 @@ struct Geometry {
                                              (rows(2 * F) * H + rows(H) * F)) * esize);
     return rows(V) * H * esize + H * 4 + L * per_layer + moe_delta;
   }
+  // Logit chunk (few rows, fp32) or the fused head's argmax keys (8 bytes each).
+  int64_t logit_ws_bytes() const {
+    return std::max<int64_t>(logit_chunk * V * 4, fwdk::head_argmax_part_keys((int)T, (int)V) * 8);
+  }
   // Workspace (bytes, each buffer rounded to 256) for up to T tokens.
   int64_t workspace_bytes(bool sandwich) const {
     auto r = [](int64_t b) { return round_up(b, 256); };
@@ -148,7 +152,7 @@ struct Geometry {
     w += r(rows(T) * F * esize);                        // SwiGLU output
     if (sandwich) w += r(T * H * 4);                    // sublayer output before its norm
     w += r(T * 4) + r(T * 4) + 256;                     // ids, argmax, flag
-    w += r(logit_chunk * V * 4);                        // logits when the caller wants none
+    w += r(logit_ws_bytes());                           // logits when the caller wants none / argmax keys
     w += rope_tables * r(T * (D / 2) * 8);              // RoPE cos/sin tables
     if (tiled) w += r(skinny_part_floats() * 4) + r(skinny_counters() * 4) + r(fwdk::skinny_groups((int)H) * 64 * 4);
     if (E > 0) {
@@ -609,7 +613,7 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     if (int rc = m->alloc((void**)&m->ids, T * 4)) return rc;
     if (int rc = m->alloc((void**)&m->amax, T * 4)) return rc;
     if (int rc = m->alloc((void**)&m->flag, 256)) return rc;
-    if (int rc = m->alloc((void**)&m->logits_ws, g.logit_chunk * g.V * 4)) return rc;
+    if (int rc = m->alloc((void**)&m->logits_ws, g.logit_ws_bytes())) return rc;
     if (g.E > 0) {
       const int64_t A = T * g.topk, nch = fwdk::moe_chunks(A);
       if (int rc = m->alloc((void**)&m->moe_logits, T * g.E * 4)) return rc;
@@ -817,7 +821,14 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
   int32_t* am = o.argmax ? o.argmax : m->amax;
   const fwdk::RowNormX nh = normx(cur, m->final_norm);
   const fwdk::RowNormX* nhp = fuse ? &nh : nullptr;
-  if (o.logits) {
+  if (dt == fwdk::DType::BF16 && tl && M > fwdk::kSkinnyRows) {
+    // argmax folded into the head's epilogue; logits written only when requested
+    int nchunk = 0;
+    uint64_t* keys = (uint64_t*)m->logits_ws;
+    TIMED(m, FWD_KERNEL_LM_HEAD,
+          fwdk::gemm_head_keys(m->n, m->embed, o.logits, V, M, V, H, cap, keys, &nchunk, m->flag, s));
+    TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_keys(keys, nchunk, M, am, s));
+  } else if (o.logits) {
     TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, m->n, m->embed, o.logits, V, M, V, H, cap, tl, s, sk, nhp));
     TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(o.logits, V, M, V, am, m->flag, s));
   } else {

@@ -59,6 +59,88 @@ struct EpiStore {
   }
 };
 
+// Tied LM head with the per-position argmax folded in ("N7 · model/forward-parity",
+// Theorem 1: per-position argmax; "pegainfer issue #878", Acceptance Criteria: lowest
+// index on ties, non-finite logits fail the call). Logits (after the optional softcap)
+// are stored only when Y is set. Each lane keeps, per row, its best value and column;
+// it meets its columns in increasing order, so a strict comparison keeps the lowest
+// column among equal values. A running sum of v * 0 turns NaN as soon as any value is
+// infinite or NaN. write_tile then encodes each row's best as one 64-bit key that
+// orders by value first and by lower column second (the value's bits made monotone as
+// an unsigned integer, -0 counted as +0 since the two compare equal; the low word the
+// complement of the column), reduces the keys across lanes and stores one per (row,
+// column chunk) into part[row * nchunk + chunk]; argmax_partials_kernel reduces the
+// chunks.
+template <int C>
+struct EpiHead {
+  float* Y;  // optional [M, ldy] fp32 logits
+  int64_t ldy;
+  float cap;  // 0 = off
+  uint64_t* part;
+  int nchunk;
+  int* flag;  // set to 1 when a logit is not finite
+  static __device__ __forceinline__ uint64_t key(float v, int col) {
+    uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)col;
+  }
+  template <int R>
+  __device__ __forceinline__ void batch_best(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
+                                             bool ok0, bool ok1, float (&bv)[R], int (&bi)[R], float& chk) const {
+    const EpiStore<C> st{Y, ldy, cap};
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      if (row[q] < 0) continue;
+      const float a = st.apply(v0[q]), b = st.apply(v1[q]);
+      if (Y) {
+        float* y = Y + (int64_t)row[q] * ldy + c;
+        if (ok0) y[0] = a;
+        if (ok1) y[C] = b;
+      }
+      if (ok0) {
+        chk = fmaf(a, 0.f, chk);
+        if (a > bv[q]) bv[q] = a, bi[q] = c;
+      }
+      if (ok1) {
+        chk = fmaf(b, 0.f, chk);
+        if (b > bv[q]) bv[q] = b, bi[q] = c + C;
+      }
+    }
+  }
+};
+
+template <class E, class = void>
+struct kHasBest : std::false_type {};
+template <class E>
+struct kHasBest<E, std::void_t<decltype(&E::template batch_best<16>)>> : std::true_type {};
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// The 32 lanes of each half-wavefront hold keys of the same 16 rows (register q of
+// the 32x32 accumulator layout) for different columns. Four exchange steps halve the
+// rows each lane keeps (the lane keeps the half its bit selects and receives the
+// partner's keys of that half), a fifth combines the last pair, so lane l ends with
+// the maximum over all 32 lanes of row q = (l >> 1) & 15.
+__device__ __forceinline__ uint64_t reduce_rows16(uint64_t (&k)[16], int lane) {
+#pragma unroll
+  for (int n = 8; n >= 1; n >>= 1) {
+    // all ones where this lane keeps the upper half (lane bit 16, 8, 4, 2 for n = 8, 4, 2, 1);
+    // selected by masks rather than by index so that k stays in registers
+    const uint64_t m = (lane & (2 * n)) ? ~0ull : 0ull;
+#pragma unroll
+    for (int q = 0; q < n; ++q) {
+      const uint64_t lo = k[q], up = k[q + n];
+      const uint64_t send = (lo & m) | (up & ~m), keep = (up & m) | (lo & ~m);
+      k[q] = max_u64(keep, shfl_xor_u64(send, 2 * n));
+    }
+  }
+  return max_u64(k[0], shfl_xor_u64(k[0], 1));
+}
+
 template <int C>
 struct EpiResidual {
   const float* xin;
@@ -324,7 +406,13 @@ __device__ __forceinline__ void write_tile(const Epi& epi, const floatx16_t (&ac
                                            int N, int lane) {
   const int lr = lane & 31, lk = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    float bv[16], chk = 0.f;  // (argmax epilogues) per-row best value and column, finiteness check
+    int bi[16];
+    if constexpr (kHasBest<Epi>::value) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bv[r] = -INFINITY, bi[r] = 0x7FFFFFFF;
+    }
 #pragma unroll
     for (int jp = 0; jp < TN / 2; ++jp) {
       const int c = c0 + jp * 64 + lr;
@@ -338,8 +426,21 @@ __device__ __forceinline__ void write_tile(const Epi& epi, const floatx16_t (&ac
         v0[r] = acc[i][2 * jp][r];
         v1[r] = acc[i][2 * jp + 1][r];
       }
-      epi.batch(rows, c, v0, v1, ok0, ok1);
+      if constexpr (kHasBest<Epi>::value) epi.batch_best(rows, c, v0, v1, ok0, ok1, bv, bi, chk);
+      else epi.batch(rows, c, v0, v1, ok0, ok1);
     }
+    if constexpr (kHasBest<Epi>::value) {
+      // one key per (row, chunk of the wavefront's TN * 32 columns)
+      uint64_t keys[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) keys[r] = Epi::key(bv[r], bi[r]);
+      const uint64_t k = reduce_rows16(keys, lane);
+      const int q = (lane >> 1) & 15;
+      const int row = r0 + i * 32 + 8 * (q >> 2) + 4 * lk + (q & 3);
+      if ((lane & 1) == 0 && row < M && c0 < N) epi.part[(int64_t)row * epi.nchunk + c0 / (TN * 32)] = k;
+      if (chk != chk) *epi.flag = 1;
+    }
+  }
 }
 
 // Tile configuration: BM x BN output tile, BK-wide K slices, STAGES LDS buffers,
@@ -1085,6 +1186,20 @@ hipError_t launch_f32(const void* X, const void* W, int M, int N, int K, const E
   return hipGetLastError();
 }
 
+// out[row] = the column of the largest key among the row's nchunk partial keys (see
+// EpiHead). One wavefront per row, four rows per workgroup.
+__global__ __launch_bounds__(256) void argmax_partials_kernel(const uint64_t* __restrict__ part, int nchunk,
+                                                             int rows, int32_t* __restrict__ out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const uint64_t* p = part + (int64_t)row * nchunk;
+  uint64_t k = 0;
+  for (int j = lane; j < nchunk; j += 64) k = max_u64(k, p[j]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) k = max_u64(k, shfl_xor_u64(k, o));
+  if (lane == 0) out[row] = (int32_t)~(uint32_t)k;
+}
+
 }  // namespace
 
 namespace {
@@ -1125,6 +1240,31 @@ hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t 
   if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiStore<32>{Y, ldy, softcap}, tiled, s, sk, nx);
   if (tiled || nx) return hipErrorInvalidValue;
   return launch_f32(X, W, M, N, K, EpiStore<1>{Y, ldy, softcap}, s);
+}
+
+int64_t head_argmax_part_keys(int M, int N) {
+  if (M <= 0 || N <= 0) return 0;
+  return (int64_t)M * ((N + 63) / 64);  // the narrowest wavefront column span (64) bounds every config
+}
+
+hipError_t gemm_head_keys(const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K, float softcap,
+                         uint64_t* part, int* nchunk, int* flag, hipStream_t s) {
+  *nchunk = 0;
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % 32 || M <= kSkinnyRows || !part || !flag) return hipErrorInvalidValue;
+  EpiHead<32> epi{Y, ldy, softcap, part, 0, flag};
+  if ((int64_t)((M + 255) / 256) * ((N + 255) / 256) >= 256) {
+    *nchunk = epi.nchunk = (N + CfgBig::WTN - 1) / CfgBig::WTN;
+    return launch_pp<CfgBig, EpiHead<32>, true>(X, W, M, N, K, epi, s);
+  }
+  *nchunk = epi.nchunk = (N + CfgSmall::WTN - 1) / CfgSmall::WTN;
+  return launch_cfg<CfgSmall, EpiHead<32>, true>(X, W, M, N, K, epi, s);
+}
+
+hipError_t argmax_keys(const uint64_t* part, int nchunk, int M, int32_t* out, hipStream_t s) {
+  if (M <= 0 || nchunk <= 0) return hipSuccess;
+  hipLaunchKernelGGL(argmax_partials_kernel, dim3((M + 3) / 4), dim3(256), 0, s, part, nchunk, M, out);
+  return hipGetLastError();
 }
 
 hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xin, float* xout, int M, int N,

@@ -44,6 +44,16 @@ struct RowNormX {
 hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K,
                       float softcap, bool tiled, hipStream_t s, const SplitK* sk = nullptr,
                       const RowNormX* nx = nullptr);
+// Tied LM head with the per-position argmax fused (bf16 K-tiled operands, K a multiple
+// of 32, M > kSkinnyRows): logits as gemm_store when Y is set (Y may be null: argmax
+// only), plus per row the best (value, lowest column) key of each column chunk in
+// part[row * nchunk + chunk] (head_argmax_part_keys(M, N) keys bound the size);
+// *flag = 1 if any logit is not finite. argmax_keys then reduces the chunks: out[r] =
+// argmax over the N logits of row r, lowest index on ties.
+int64_t head_argmax_part_keys(int M, int N);
+hipError_t gemm_head_keys(const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K, float softcap,
+                         uint64_t* part, int* nchunk, int* flag, hipStream_t s);
+hipError_t argmax_keys(const uint64_t* part, int nchunk, int M, int32_t* out, hipStream_t s);
 // xout[M, N] = xin + X·Wᵀ (fp32 residual stream, row stride N; xin may equal xout).
 hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xin, float* xout, int M, int N,
                          int K, bool tiled, hipStream_t s, const SplitK* sk = nullptr, float* ssq_out = nullptr);
