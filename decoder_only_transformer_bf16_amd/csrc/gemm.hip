@@ -206,21 +206,58 @@ struct EpiSwiGLU {
   T* a;
   int F;
   bool tiled;  // a in the K-tiled layout (it is the next GEMM's X operand)
+  bool buf = false;  // the K-tiled output spans less than 2^31 bytes (32-bit buffer offsets)
+  static constexpr int kStagger = 2;
   __device__ __forceinline__ void pair(int row, int c, float g, float u, bool ok0, bool) const {
     if (!ok0) return;
     const int f = (c / (2 * C)) * C + (c % C);
-    float s;
+    Elem<T>::store(a + (tiled ? tiled_index(row, f, F) : (int64_t)row * F + f), act(g) * u);
+  }
+  static __device__ __forceinline__ float act(float g) {
     if constexpr (ACT == 0) {
-      s = g * fast_rcp(1.f + fast_exp2(-kLog2e * g));
+      return g * fast_rcp(1.f + fast_exp2(-kLog2e * g));
     } else {
       const float y = 0.7978845608028654f * (g + 0.044715f * g * g * g);
-      s = 0.5f * g * (2.f - 2.f * fast_rcp(1.f + fast_exp2(2.f * kLog2e * y)));
+      return 0.5f * g * (2.f - 2.f * fast_rcp(1.f + fast_exp2(2.f * kLog2e * y)));
     }
-    Elem<T>::store(a + (tiled ? tiled_index(row, f, F) : (int64_t)row * F + f), s * u);
   }
   template <int R>
   __device__ __forceinline__ void batch(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
                                         bool ok0, bool ok1) const {
+    if constexpr (std::is_same<T, bf16_t>::value && C == 32 && R % 2 == 0) {
+      if (tiled && buf) {
+        // Adjacent lanes hold adjacent outputs f, f + 1 of the same R rows. Each pair
+        // swaps half its results (even lanes give away rows R/2.., odd lanes rows
+        // ..R/2) so that every lane stores two neighbouring bf16 outputs with one
+        // 4-byte buffer store: the even lane rows q < R/2, the odd lane rows q + R/2.
+        // Rows past the end get an offset outside the buffer, which the hardware
+        // drops, so there is no branch per row. Selections between the two halves use
+        // bit masks, not indices, so that the arrays stay in registers. (F is a
+        // multiple of 32 for the K-tiled layout, so ok0 is the same for both lanes of
+        // a pair.)
+        if (!ok0) return;
+        const uint32_t m = (threadIdx.x & 1) ? ~0u : 0u;
+        const int f2 = ((c / (2 * C)) * C + (c % C)) & ~1;
+        const uint32_t colpart = (uint32_t)(f2 >> 5) * 1024u + (uint32_t)(f2 & 31) * 2u;
+        const uint32_t tilerow = (uint32_t)F * 32u;  // bytes per 16-row band of the K-tiled output
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a, 0x7FFFFFF0);
+        uint32_t s[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) s[q] = __float_as_uint(act(v0[q]) * v1[q]);
+#pragma unroll
+        for (int q = 0; q < R / 2; ++q) {
+          const uint32_t mine = s[q], other = s[q + R / 2];
+          const uint32_t send = (mine & m) | (other & ~m);
+          const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);  // partner
+          const float lo = __uint_as_float((recv & m) | (mine & ~m));
+          const float hi = __uint_as_float((other & m) | (recv & ~m));
+          const int r = (int)(((uint32_t)row[q] & ~m) | ((uint32_t)row[q + R / 2] & m));
+          const uint32_t off = r < 0 ? 0x80000000u : (uint32_t)(r >> 4) * tilerow + (uint32_t)(r & 15) * 64u + colpart;
+          __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(lo, hi), rs, (int)off, 0, 0);
+        }
+        return;
+      }
+    }
     batch_pairs(*this, row, c, v0, v1, ok0, ok1);
   }
 };
@@ -501,6 +538,24 @@ __device__ __forceinline__ bool group_tile(const GroupArgs& g, int block, int nT
   return true;
 }
 
+// Staggered start. Tiles of one launch take equal time, so without intervention all
+// CUs reach their epilogues together and the whole chip alternates between a phase of
+// matrix work and a phase of epilogue stores. Holding every other workgroup of the
+// first round back by a few microseconds puts neighbouring CUs out of phase for the
+// rest of the launch, so one CU's epilogue overlaps its neighbours' matrix work.
+// Measured on the Llama-shape gate/up product (28 rounds of 256 tiles): 2.93 -> 2.76
+// ms with two sleeps of 127 x 64 cycles; products whose epilogue gained nothing keep 0.
+template <class E, class = void>
+struct kStaggerOf : std::integral_constant<int, 0> {};
+template <class E>
+struct kStaggerOf<E, std::void_t<decltype(E::kStagger)>> : std::integral_constant<int, E::kStagger> {};
+__device__ __forceinline__ void stagger_first_round(int sleeps) {
+  // round-robin dispatch over 8 XCDs: ids x + 8 j land on XCD x, and bit 3 alternates
+  // between consecutive workgroups of one XCD
+  if (gridDim.x > 256 && blockIdx.x < 256 && (blockIdx.x & 8))
+    for (int i = 0; i < sleeps; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
 // GROUPED: one launch over the expert segments of a mixture-of-experts layer; the
 // workgroup's m-tile selects the expert (the last one whose first tile is at or
 // before it, so empty experts are skipped), whose X rows start at seg_start and whose
@@ -671,6 +726,7 @@ __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN, KS = C::KS;
   constexpr int SLICE = (BM + BN) * BK, LA = C::LOADS_A, LT = C::LOADS, FR = TM + TN;
   __shared__ __attribute__((aligned(1024))) bf16_t lds[ST * SLICE];
+  if constexpr (!GROUPED && kStaggerOf<Epi>::value > 0) stagger_first_round(kStaggerOf<Epi>::value);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1279,9 +1335,10 @@ hipError_t gemm_swiglu(DType dt, const void* X, const void* W, void* a, int M, i
                        hipStream_t s, const SplitK* sk, const RowNormX* nx, int act) {
   if (act != 0 && act != 1) return hipErrorInvalidValue;
   if (dt == DType::BF16) {
+    const bool fits = tiled && (int64_t)((M + 15) / 16 * 16) * F * 2 <= 0x7FFFFFF0LL;
     if (act == 1)
-      return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t, 1>{(bf16_t*)a, F, tiled}, tiled, s, sk, nx);
-    return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t>{(bf16_t*)a, F, tiled}, tiled, s, sk, nx);
+      return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t, 1>{(bf16_t*)a, F, tiled, fits}, tiled, s, sk, nx);
+    return launch_bf16(X, W, M, 2 * F, K, EpiSwiGLU<32, bf16_t>{(bf16_t*)a, F, tiled, fits}, tiled, s, sk, nx);
   }
   if (tiled || nx) return hipErrorInvalidValue;
   if (act == 1) return launch_f32(X, W, M, 2 * F, K, EpiSwiGLU<1, float, 1>{(float*)a, F, false}, s);
