@@ -207,7 +207,6 @@ struct EpiSwiGLU {
   int F;
   bool tiled;  // a in the K-tiled layout (it is the next GEMM's X operand)
   bool buf = false;  // the K-tiled output spans less than 2^31 bytes (32-bit buffer offsets)
-  static constexpr int kStagger = 2;
   __device__ __forceinline__ void pair(int row, int c, float g, float u, bool ok0, bool) const {
     if (!ok0) return;
     const int f = (c / (2 * C)) * C + (c % C);
@@ -538,24 +537,6 @@ __device__ __forceinline__ bool group_tile(const GroupArgs& g, int block, int nT
   return true;
 }
 
-// Staggered start. Tiles of one launch take equal time, so without intervention all
-// CUs reach their epilogues together and the whole chip alternates between a phase of
-// matrix work and a phase of epilogue stores. Holding every other workgroup of the
-// first round back by a few microseconds puts neighbouring CUs out of phase for the
-// rest of the launch, so one CU's epilogue overlaps its neighbours' matrix work.
-// Measured on the Llama-shape gate/up product (28 rounds of 256 tiles): 2.93 -> 2.76
-// ms with two sleeps of 127 x 64 cycles; products whose epilogue gained nothing keep 0.
-template <class E, class = void>
-struct kStaggerOf : std::integral_constant<int, 0> {};
-template <class E>
-struct kStaggerOf<E, std::void_t<decltype(E::kStagger)>> : std::integral_constant<int, E::kStagger> {};
-__device__ __forceinline__ void stagger_first_round(int sleeps) {
-  // round-robin dispatch over 8 XCDs: ids x + 8 j land on XCD x, and bit 3 alternates
-  // between consecutive workgroups of one XCD
-  if (gridDim.x > 256 && blockIdx.x < 256 && (blockIdx.x & 8))
-    for (int i = 0; i < sleeps; ++i) __builtin_amdgcn_s_sleep(127);
-}
-
 // GROUPED: one launch over the expert segments of a mixture-of-experts layer; the
 // workgroup's m-tile selects the expert (the last one whose first tile is at or
 // before it, so empty experts are skipped), whose X rows start at seg_start and whose
@@ -726,7 +707,6 @@ __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN, KS = C::KS;
   constexpr int SLICE = (BM + BN) * BK, LA = C::LOADS_A, LT = C::LOADS, FR = TM + TN;
   __shared__ __attribute__((aligned(1024))) bf16_t lds[ST * SLICE];
-  if constexpr (!GROUPED && kStaggerOf<Epi>::value > 0) stagger_first_round(kStaggerOf<Epi>::value);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
