@@ -109,6 +109,35 @@ struct EpiHead {
   }
 };
 
+// Epilogues with kInit = true take the residual into the accumulators before the K loop
+// (init_acc): the tile's residual loads then travel with the first operand loads, and
+// the epilogue only stores.
+template <class E, class = void>
+struct kInitAcc : std::false_type {};
+template <class E>
+struct kInitAcc<E, std::void_t<decltype(E::kInit)>> : std::true_type {};
+
+// xout = xin + X·Wᵀ for the tiled kernels: the accumulators start from xin (init_acc),
+// the epilogue stores them.
+template <int C>
+struct EpiResidualInit {
+  static constexpr bool kInit = true;
+  const float* xin;
+  float* xout;
+  int64_t ld;
+  template <int R>
+  __device__ __forceinline__ void batch(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
+                                        bool ok0, bool ok1) const {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      if (row[q] < 0) continue;
+      float* y = xout + (int64_t)row[q] * ld + c;
+      if (ok0) y[0] = v0[q];
+      if (ok1) y[C] = v1[q];
+    }
+  }
+};
+
 template <class E, class = void>
 struct kHasBest : std::false_type {};
 template <class E>
@@ -433,6 +462,22 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// acc[i][j] of a wavefront whose sub-tile starts at (r0, c0) := xin at the positions the
+// accumulator layout below gives its registers (zero outside M x N).
+template <int TM, int TN, class Epi>
+__device__ __forceinline__ void init_acc(const Epi& epi, floatx16_t (&acc)[TM][TN], int r0, int c0, int M, int N,
+                                         int lane) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), col = c0 + j * 32 + (lane & 31);
+        acc[i][j][r] = (row < M && col < N) ? epi.xin[(int64_t)row * epi.ld + col] : 0.f;
+      }
+}
+
 // Accumulator layout of v_mfma_f32_32x32x16: register r of lane l holds row
 // 8 (r / 4) + 4 (l / 32) + r % 4 and column l % 32 of the 32x32 sub-tile. Hands a
 // wavefront's TM x TN sub-tiles (origin r0, c0) to the epilogue, 16 rows of one
@@ -573,6 +618,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx16_t{};
+  if constexpr (kInitAcc<Epi>::value) init_acc<TM, TN>(epi, acc, row0 + m0 + wm * WTM, n0 + wn * WTN, row0 + M, N, lane);
 
   // Software pipeline over K slices; slice t lives in LDS buffer t % ST.
   // One barrier per slice, early in its last sub-step (whose fragments were read
@@ -751,6 +797,7 @@ __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx16_t{};
+  if constexpr (kInitAcc<Epi>::value) init_acc<TM, TN>(epi, acc, row0 + m0 + wm * WTM, n0 + wn * WTN, row0 + M, N, lane);
 
   constexpr int RS = C::RS;
   u32x4_t stage[RS > 0 ? RS : 1][LT];  // VGPR route: slices in flight in registers
@@ -1192,6 +1239,20 @@ hipError_t launch_skinny(const XOp& xop, const void* W, int M, int N, int K, con
 }
 
 // ------------------------------------------------------------------ dispatch
+// The tiled kernels only (256 x 256 ping-pong tiles for large problems, else 128 x 128).
+template <class Epi>
+hipError_t launch_dense(const void* X, const void* W, int M, int N, int K, const Epi& epi, bool tiled, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (tiled && K % 32) return hipErrorInvalidValue;
+  const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  if (tiled) {
+    if (big >= 256) return launch_pp<CfgBig, Epi, true>(X, W, M, N, K, epi, s);
+    return launch_cfg<CfgSmall, Epi, true>(X, W, M, N, K, epi, s);
+  }
+  if (big >= 256) return launch_pp<CfgBig, Epi, false>(X, W, M, N, K, epi, s);
+  return launch_cfg<CfgSmall, Epi, false>(X, W, M, N, K, epi, s);
+}
+
 // Both operands row-major, or both K-tiled (K a multiple of 32).
 template <class Epi>
 hipError_t launch_bf16(const void* X, const void* W, int M, int N, int K, const Epi& epi, bool tiled, hipStream_t s,
@@ -1204,13 +1265,7 @@ hipError_t launch_bf16(const void* X, const void* W, int M, int N, int K, const 
     if (nx) return launch_skinny(XNorm{nx->x, nx->w, nx->ssq, nx->groups, nx->eps}, W, M, N, K, epi, *sk, ssq_out, s);
     return launch_skinny(XTiled{(const bf16_t*)X}, W, M, N, K, epi, *sk, ssq_out, s);
   }
-  const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  if (tiled) {
-    if (big >= 256) return launch_pp<CfgBig, Epi, true>(X, W, M, N, K, epi, s);
-    return launch_cfg<CfgSmall, Epi, true>(X, W, M, N, K, epi, s);
-  }
-  if (big >= 256) return launch_pp<CfgBig, Epi, false>(X, W, M, N, K, epi, s);
-  return launch_cfg<CfgSmall, Epi, false>(X, W, M, N, K, epi, s);
+  return launch_dense(X, W, M, N, K, epi, tiled, s);
 }
 
 template <class Epi>
@@ -1305,8 +1360,11 @@ hipError_t argmax_keys(const uint64_t* part, int nchunk, int M, int32_t* out, hi
 
 hipError_t gemm_residual(DType dt, const void* X, const void* W, const float* xin, float* xout, int M, int N,
                          int K, bool tiled, hipStream_t s, const SplitK* sk, float* ssq_out) {
-  if (dt == DType::BF16)
-    return launch_bf16(X, W, M, N, K, EpiResidual<32>{xin, xout, N}, tiled, s, sk, nullptr, ssq_out);
+  if (dt == DType::BF16) {
+    if ((tiled && sk && M <= kSkinnyRows) || ssq_out)  // few rows: split-K kernel, residual added at the end
+      return launch_bf16(X, W, M, N, K, EpiResidual<32>{xin, xout, N}, tiled, s, sk, nullptr, ssq_out);
+    return launch_dense(X, W, M, N, K, EpiResidualInit<32>{xin, xout, N}, tiled, s);
+  }
   if (tiled || ssq_out) return hipErrorInvalidValue;
   return launch_f32(X, W, M, N, K, EpiResidual<1>{xin, xout, N}, s);
 }
