@@ -84,27 +84,42 @@ struct EpiHead {
     u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)col;
   }
+  // Rows rtile .. rtile + 31 (wave-uniform) hold every row of the batch. Logit stores are
+  // 4-byte buffer stores relative to that band; rows past M and columns past N get an
+  // out-of-range offset, which the hardware drops, and the comparisons use selects, so
+  // the batch has no per-element branches.
   template <int R>
   __device__ __forceinline__ void batch_best(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
-                                             bool ok0, bool ok1, float (&bv)[R], int (&bi)[R], float& chk) const {
+                                             bool ok0, bool ok1, float (&bv)[R], int (&bi)[R], float& chk,
+                                             int rtile) const {
+    if (cap > 0.f) best_rows<true>(row, c, v0, v1, ok0, ok1, bv, bi, chk, rtile);
+    else best_rows<false>(row, c, v0, v1, ok0, ok1, bv, bi, chk, rtile);
+  }
+  template <bool CAP, int R>
+  __device__ __forceinline__ void best_rows(const int (&row)[R], int c, const float (&v0)[R], const float (&v1)[R],
+                                            bool ok0, bool ok1, float (&bv)[R], int (&bi)[R], float& chk,
+                                            int rtile) const {
     const EpiStore<C> st{Y, ldy, cap};
+    // (without Y: a null range, never stored through)
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y ? Y + (int64_t)rtile * ldy : nullptr, Y ? (int64_t)32 * ldy * 4 : 0);
 #pragma unroll
     for (int q = 0; q < R; ++q) {
-      if (row[q] < 0) continue;
-      const float a = st.apply(v0[q]), b = st.apply(v1[q]);
+      const bool u0 = row[q] >= 0 && ok0, u1 = row[q] >= 0 && ok1;
+      const float a = CAP ? st.apply(v0[q]) : v0[q], b = CAP ? st.apply(v1[q]) : v1[q];
       if (Y) {
-        float* y = Y + (int64_t)row[q] * ldy + c;
-        if (ok0) y[0] = a;
-        if (ok1) y[C] = b;
+        const uint32_t off = ((uint32_t)(row[q] - rtile) * (uint32_t)ldy + (uint32_t)c) * 4u;  // (used if u0 / u1)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), ry, (int)(u0 ? off : 0x80000000u), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(b), ry, (int)(u1 ? off + 4u * C : 0x80000000u), 0, 0);
       }
-      if (ok0) {
-        chk = fmaf(a, 0.f, chk);
-        if (a > bv[q]) bv[q] = a, bi[q] = c;
-      }
-      if (ok1) {
-        chk = fmaf(b, 0.f, chk);
-        if (b > bv[q]) bv[q] = b, bi[q] = c + C;
-      }
+      chk = fmaf(u0 ? a : 0.f, 0.f, chk);
+      chk = fmaf(u1 ? b : 0.f, 0.f, chk);
+      const float a2 = u0 ? a : -INFINITY, b2 = u1 ? b : -INFINITY;
+      const bool ga = a2 > bv[q];
+      bv[q] = ga ? a2 : bv[q];
+      bi[q] = ga ? c : bi[q];
+      const bool gb = b2 > bv[q];
+      bv[q] = gb ? b2 : bv[q];
+      bi[q] = gb ? c + C : bi[q];
     }
   }
 };
@@ -507,7 +522,7 @@ __device__ __forceinline__ void write_tile(const Epi& epi, const floatx16_t (&ac
         v0[r] = acc[i][2 * jp][r];
         v1[r] = acc[i][2 * jp + 1][r];
       }
-      if constexpr (kHasBest<Epi>::value) epi.batch_best(rows, c, v0, v1, ok0, ok1, bv, bi, chk);
+      if constexpr (kHasBest<Epi>::value) epi.batch_best(rows, c, v0, v1, ok0, ok1, bv, bi, chk, r0 + i * 32);
       else epi.batch(rows, c, v0, v1, ok0, ok1);
     }
     if constexpr (kHasBest<Epi>::value) {
