@@ -1,11 +1,13 @@
 // Projections Y = X·Wᵀ ("N9 · metalgemm", Theorem 1: X [P, in], W [out, in],
 // both row-major, fp32 accumulation) with the fused epilogues of the forward pass:
-// plain fp32 store (+ final-logit softcap, "pegainfer issue #878"), residual add,
-// SwiGLU, and RoPE on the query/key heads ("N7 · model/forward-parity", intro).
+// plain fp32 store (+ final-logit softcap, "pegainfer issue #878"), the tied head with
+// the per-position argmax, residual add, SwiGLU, and RoPE on the query/key heads
+// ("N7 · model/forward-parity", intro and Theorem 1).
 //
-// bf16 path: CDNA4 MFMA v_mfma_f32_32x32x16_bf16, one 64-wide wavefront per
-// (BM/WM) x (BN/WN) sub-tile, K staged through LDS in 64-wide slices, double
-// buffered, with the next slice's global loads in flight during the MFMAs.
+// bf16 path: CDNA4 MFMA v_mfma_f32_32x32x16_bf16 on K-tiled operands staged through
+// LDS by buffer->LDS loads in 32-wide K slices: a two-group ping-pong kernel with
+// 256 x 256 tiles and four LDS stages for large problems, a 128 x 128 software-
+// pipelined kernel for small ones, and a split-K 16x16x32 kernel for few rows.
 // f32 path: an LDS-tiled VALU kernel (the fp32 configuration is tiny).
 #include <algorithm>
 #include <type_traits>
@@ -307,6 +309,32 @@ struct EpiSwiGLU {
 
 // KV: also store the rotated keys and the values in a KV cache (a separate
 // instantiation, so that the plain prefill keeps the lean epilogue).
+// bf16 stores of R rows of one column per lane into a row-major buffer (rs, `rowbytes`
+// per row), where lanes 2k and 2k + 1 hold neighbouring columns of the same rows (the
+// accumulator layouts of every kernel here): each pair swaps half its values by one DPP
+// move so that every lane stores two neighbouring outputs with one 4-byte store (the
+// even lane rows q < R/2, the odd lane rows q + R/2). `colbytes` is this lane's column
+// in bytes. Rows past the end (row < 0) get an out-of-range offset, which the hardware
+// drops; halves are selected by bit masks, not indices, so the arrays stay in registers.
+template <int R>
+__device__ __forceinline__ void store_pairs_rows(__amdgpu_buffer_rsrc_t rs, const int (&row)[R], uint32_t colbytes,
+                                                 const float (&v)[R], uint32_t rowbytes) {
+  static_assert(R % 2 == 0, "rows are split between the two lanes of a pair");
+  const uint32_t m = (threadIdx.x & 1) ? ~0u : 0u;
+  const uint32_t cb = colbytes & ~3u;
+#pragma unroll
+  for (int q = 0; q < R / 2; ++q) {
+    const uint32_t mine = __float_as_uint(v[q]), other = __float_as_uint(v[q + R / 2]);
+    const uint32_t send = (mine & m) | (other & ~m);
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    const float lo = __uint_as_float((recv & m) | (mine & ~m));
+    const float hi = __uint_as_float((other & m) | (recv & ~m));
+    const int r = (int)(((uint32_t)row[q] & ~m) | ((uint32_t)row[q + R / 2] & m));
+    const uint32_t off = r < 0 ? 0x80000000u : (uint32_t)r * rowbytes + cb;
+    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(lo, hi), rs, (int)off, 0, 0);
+  }
+}
+
 template <int C, typename T, bool KV, bool ROT = true>
 struct EpiRope {
   T* qkv;  // [M, (Hq + 2 Hkv) D]: rotated q, rotated k, plain v, natural dim order
@@ -314,6 +342,7 @@ struct EpiRope {
   int Hq, Hkv, D, S, pos0;  // row r is sequence r / S at position pos0 + r % S
   T *kc, *vc;               // with KV: the cache [B, Hkv, Smax, D]
   int Smax;
+  bool buf = false;  // bf16 qkv spans less than 2^31 bytes: pair-packed buffer stores (rotating path, no cache)
   __device__ __forceinline__ T* cache(T* base, int row, int head, int d) const {
     return base + (((int64_t)(row / S) * Hkv + head) * Smax + pos0 + row % S) * D + d;
   }
@@ -322,6 +351,35 @@ struct EpiRope {
                                         bool ok0, bool ok1) const {
     const int qsz = Hq * D, ksz = Hkv * D;
     if (!ok0) return;
+    if constexpr (std::is_same<T, bf16_t>::value && C == 32 && ROT && !KV && R % 2 == 0) {
+      if (buf) {  // (sections start at multiples of 32 columns: both lanes of a pair take the same path)
+        const uint32_t rowbytes = (uint32_t)(qsz + 2 * ksz) * 2u;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(qkv, 0x7FFFFFF0);
+        if (c >= qsz + ksz) {
+          store_pairs_rows(rs, row, (uint32_t)c * 2u, v0, rowbytes);
+          if (ok1) store_pairs_rows(rs, row, (uint32_t)(c + C) * 2u, v1, rowbytes);
+          return;
+        }
+        const int sec = c < qsz ? 0 : qsz;
+        const int cc = c - sec;
+        const int head = cc / D, pd = cc - head * D;
+        const int k = (pd / (2 * C)) * C + (pd % C);
+        float2 r[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q)  // all table loads first
+          r[q] = cs[(int64_t)((row[q] < 0 ? 0 : row[q]) % S + pos0) * (D / 2) + k];
+        float a[R], b[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+          a[q] = v0[q] * r[q].x - v1[q] * r[q].y;
+          b[q] = v0[q] * r[q].y + v1[q] * r[q].x;
+        }
+        const uint32_t col = (uint32_t)(sec + head * D + k) * 2u;
+        store_pairs_rows(rs, row, col, a, rowbytes);
+        store_pairs_rows(rs, row, col + (uint32_t)D, b, rowbytes);  // dim k + D/2: D/2 columns of 2 bytes
+        return;
+      }
+    }
     if (c >= qsz + ksz) {  // value columns: plain stores
       batch_pairs(*this, row, c, v0, v1, ok0, ok1);
       return;
@@ -1420,10 +1478,11 @@ hipError_t gemm_qkv_rope(DType dt, const void* X, const void* W, const RopeArgs&
                          EpiRope<32, bf16_t, true>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, (bf16_t*)r.kc,
                                                    (bf16_t*)r.vc, r.Smax},
                          tiled, s, sk, nx);
+    const bool fits = (int64_t)M * N * 2 <= 0x7FFFFFF0LL;
     return launch_bf16(
         X, W, M, N, K,
-        EpiRope<32, bf16_t, false>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, nullptr, nullptr, 0}, tiled,
-        s, sk, nx);
+        EpiRope<32, bf16_t, false>{(bf16_t*)r.qkv, r.cs, r.Hq, r.Hkv, r.D, r.S, r.pos0, nullptr, nullptr, 0, fits},
+        tiled, s, sk, nx);
   }
   if (tiled || nx) return hipErrorInvalidValue;
   if (r.kc)
