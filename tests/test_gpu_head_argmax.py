@@ -7,7 +7,9 @@ Gates ("N7 · model/forward-parity", Theorem 1: per-position argmax; "pegainfer 
 - the argmax-only call (no logits written) returns the same ids as the call that also
   writes logits, and those ids are the first maximum of the written logits;
 - the ids agree with the oracle wherever its top-1 margin pins them;
-- a single non-finite logit column raises FWD_E_NONFINITE.
+- a single non-finite logit column raises FWD_E_NONFINITE;
+- a vocabulary that ends inside a tile and a row count just past a tile boundary
+  (ragged edges of the head product and of its argmax chunks).
 """
 import sys
 
@@ -106,4 +108,27 @@ def test_single_nonfinite_column_fails(fwd):
     with pytest.raises(fwd.FwdError) as e:
         model.prefill(ids, logits=True, argmax=True)
     assert e.value.code == fwd.FWD_E_NONFINITE
+    model.close()
+
+
+@pytest.mark.parametrize("vocab,seq", [(1000, 257), (4097, 96), (40001, 257)])  # 128 x 128, 128 x 128, 256 x 256 tiles
+def test_ragged_vocab_and_rows(fwd, vocab, seq):
+    cfg = wl.SMOLLM2_135M.replace(n_layers=1, batch=1, seq=seq, vocab=vocab, name=f"smol-1L-v{vocab}-s{seq}")
+    _say(f"head argmax ragged edges: {cfg.name}")
+    host = wl.draw_all(cfg)
+    ids = wl.draw_ids(cfg)
+    model = fwd.Model(cfg, upload_weights(cfg, host), max_tokens=ids.size)
+    out = model.prefill(ids, logits=True, argmax=True)
+    z = out["logits"].cpu().numpy()
+    am = out["argmax"].cpu().numpy()
+    assert np.isfinite(z).all()
+    assert np.array_equal(am, np.argmax(z, -1))
+    only = model.prefill(ids, logits=False, argmax=True)["argmax"].cpu().numpy()
+    assert np.array_equal(only, am)
+    ref = oracle.forward(cfg, wl.HostWeights(host), ids, want_hidden=False)
+    err = float(np.max(np.abs(z - ref["logits"])) / np.max(np.abs(ref["logits"])))
+    assert err < 1e-2, err
+    pinned, near, fails = argmax_check(am, ref["logits"], z)
+    assert not fails, fails[:5]
+    _say(f"  err/scale {err:.2e}, pinned {pinned} near-tie {near}")
     model.close()
