@@ -123,6 +123,9 @@ int check_config(const fwd_config* c) {
 
 // bf16 GEMM operands (weights, normalised activations, attention and SwiGLU
 // outputs) are kept K-tiled (16 x 32 tiles, rows padded to 16); f32 is row-major.
+// (value, column) pairs the sliced argmax of a small batch may use (rows x slices <= 2 x 256)
+constexpr int64_t kArgPartPairs = 1024;
+
 struct Geometry {
   int64_t esize, H, Hq, Hkv, D, F, V, L, T, qkv_rows, logit_chunk, rope_tables;
   int64_t E = 0, topk = 0, Fe = 0, moe_layers = 0;  // mixture of experts
@@ -153,6 +156,7 @@ struct Geometry {
     if (sandwich) w += r(T * H * 4);                    // sublayer output before its norm
     w += r(T * 4) + r(T * 4) + 256;                     // ids, argmax, flag
     w += r(logit_ws_bytes());                           // logits when the caller wants none / argmax keys
+    w += r(kArgPartPairs * 8);                          // sliced argmax partials
     w += rope_tables * r(T * (D / 2) * 8);              // RoPE cos/sin tables
     if (tiled) w += r(skinny_part_floats() * 4) + r(skinny_counters() * 4) + r(fwdk::skinny_groups((int)H) * 64 * 4);
     if (E > 0) {
@@ -234,6 +238,7 @@ struct fwd_model {
   int32_t* amax = nullptr;
   int* flag = nullptr;
   float* logits_ws = nullptr;
+  float* argpart = nullptr;  // partial (value, column) pairs of the sliced argmax for few rows
   float2* rope_tab[4] = {};  // [2 * local + long factors]: RoPE (cos, sin) tables of max_tokens rows
   std::vector<float> rope_short, rope_long;  // longrope factors (the config's arrays are borrowed)
   fwdk::SplitK sk{};  // workspace of the few-row products (bf16)
@@ -614,6 +619,7 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     if (int rc = m->alloc((void**)&m->amax, T * 4)) return rc;
     if (int rc = m->alloc((void**)&m->flag, 256)) return rc;
     if (int rc = m->alloc((void**)&m->logits_ws, g.logit_ws_bytes())) return rc;
+    if (int rc = m->alloc((void**)&m->argpart, kArgPartPairs * 8)) return rc;
     if (g.E > 0) {
       const int64_t A = T * g.topk, nch = fwdk::moe_chunks(A);
       if (int rc = m->alloc((void**)&m->moe_logits, T * g.E * 4)) return rc;
@@ -830,7 +836,7 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
     TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_keys(keys, nchunk, M, am, s));
   } else if (o.logits) {
     TIMED(m, FWD_KERNEL_LM_HEAD, fwdk::gemm_store(dt, m->n, m->embed, o.logits, V, M, V, H, cap, tl, s, sk, nhp));
-    TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(o.logits, V, M, V, am, m->flag, s));
+    TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(o.logits, V, M, V, am, m->flag, s, m->argpart, kArgPartPairs));
   } else {
     const int64_t chunk = g.logit_chunk;
     for (int64_t r0 = 0; r0 < T; r0 += chunk) {
@@ -838,7 +844,8 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
       const char* nrow = (const char*)m->n + r0 * H * g.esize;  // (r0 is a multiple of 16: a tile row)
       TIMED(m, FWD_KERNEL_LM_HEAD,
             fwdk::gemm_store(dt, nrow, m->embed, m->logits_ws, V, rows, V, H, cap, tl, s, sk, nhp));  // (fused: one chunk)
-      TIMED(m, FWD_KERNEL_ARGMAX, fwdk::argmax_rows(m->logits_ws, V, rows, V, am + r0, m->flag, s));
+      TIMED(m, FWD_KERNEL_ARGMAX,
+            fwdk::argmax_rows(m->logits_ws, V, rows, V, am + r0, m->flag, s, m->argpart, kArgPartPairs));
     }
   }
   int flag = 0;

@@ -125,7 +125,12 @@ hipError_t add_norm(DType dt, const float* xin, const float* u, const float* wpo
 hipError_t embed(DType dt, const int32_t* ids, const void* E, float* x, int rows, int H, float scale, bool tiled,
                  hipStream_t s);
 // out[r] = argmax_v z[r, v] (lowest index on ties); *flag = 1 if any z is not finite.
-hipError_t argmax_rows(const float* z, int64_t ldz, int rows, int V, int32_t* out, int* flag, hipStream_t s);
+// With `part` (room for part_pairs (value, column) pairs: 2 * part_pairs floats), the
+// rows of a small batch are split into up to kArgmaxMaxSlices column slices whose
+// partial results a second launch merges.
+constexpr int kArgmaxMaxSlices = 64;
+hipError_t argmax_rows(const float* z, int64_t ldz, int rows, int V, int32_t* out, int* flag, hipStream_t s,
+                       float* part = nullptr, int64_t part_pairs = 0);
 
 // ---- packing ----
 // dst[map[r], :] = src[r, :] for r < rows; rows of `row_bytes` bytes (multiple of 4).

@@ -2,6 +2,8 @@
 // RMSNorm (plain, and the sandwich variant fused with the residual add), the
 // per-position argmax with the non-finite check, and weight packing copies.
 // One 64-lane wavefront per row, 16-byte vector accesses along the row.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -183,16 +185,22 @@ __device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
   }
 }
 
-__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ z, int64_t ldz, int V,
-                                                    int32_t* __restrict__ out, int* __restrict__ flag) {
+// Blocks (row, slice): columns [slice * span, min(V, slice * span + span)) of the row.
+// With one slice the block writes out[row]; otherwise its best (value, column) goes to
+// pv / pi[row * gridDim.y + slice] and argmax_merge_kernel picks among the slices (a
+// few rows, e.g. a decode step, would otherwise keep only a handful of workgroups busy).
+__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ z, int64_t ldz, int V, int span,
+                                                    int32_t* __restrict__ out, float* __restrict__ pv,
+                                                    int* __restrict__ pi, int* __restrict__ flag) {
   const int row = blockIdx.x, tid = threadIdx.x;
+  const int c0 = blockIdx.y * span, c1 = min(V, c0 + span);
   const float* zr = z + (int64_t)row * ldz;
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
   bool bad = false;
-  const bool vec = (V % 4 == 0) && ((ldz % 4) == 0);
+  const bool vec = (V % 4 == 0) && ((ldz % 4) == 0) && (span % 4 == 0);
   if (vec) {
-    for (int i = tid * 4; i < V; i += 1024) {
+    for (int i = c0 + tid * 4; i < c1; i += 1024) {
       const float4 v = *reinterpret_cast<const float4*>(zr + i);
       bad |= !(isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w));
       better(bv, bi, v.x, i);
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ z
       better(bv, bi, v.w, i + 3);
     }
   } else {
-    for (int i = tid; i < V; i += 256) {
+    for (int i = c0 + tid; i < c1; i += 256) {
       const float v = zr[i];
       bad |= !isfinite(v);
       better(bv, bi, v, i);
@@ -232,9 +240,26 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ z
       better(v, i, sv[w], si[w]);
       anybad |= sbad[w];
     }
-    if (out) out[row] = i;
+    if (gridDim.y == 1) {
+      if (out) out[row] = i;
+    } else {
+      pv[row * gridDim.y + blockIdx.y] = v;
+      pi[row * gridDim.y + blockIdx.y] = i;
+    }
     if (anybad) *flag = 1;
   }
+}
+
+// out[row] = the best of the row's `slices` partial (value, column) pairs (lowest column
+// among equal values, as `better` orders them).
+__global__ __launch_bounds__(64) void argmax_merge_kernel(const float* __restrict__ pv, const int* __restrict__ pi,
+                                                         int slices, int rows, int32_t* __restrict__ out) {
+  const int row = blockIdx.x * 64 + threadIdx.x;
+  if (row >= rows) return;
+  float v = pv[row * slices];
+  int i = pi[row * slices];
+  for (int j = 1; j < slices; ++j) better(v, i, pv[row * slices + j], pi[row * slices + j]);
+  out[row] = i;
 }
 
 // Packing copy: dst row map[r] <- src row r.
@@ -409,9 +434,25 @@ hipError_t embed(DType dt, const int32_t* ids, const void* E, float* x, int rows
   return hipGetLastError();
 }
 
-hipError_t argmax_rows(const float* z, int64_t ldz, int rows, int V, int32_t* out, int* flag, hipStream_t s) {
+hipError_t argmax_rows(const float* z, int64_t ldz, int rows, int V, int32_t* out, int* flag, hipStream_t s,
+                       float* part, int64_t part_pairs) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(256), 0, s, z, ldz, V, out, flag);
+  // split long rows of small batches so that at least ~256 workgroups run
+  int slices = 1;
+  if (part && out) {
+    const int want = std::min<int>(kArgmaxMaxSlices, (256 + rows - 1) / rows);
+    slices = std::max(1, std::min(want, (V + 4095) / 4096));
+    if ((int64_t)rows * slices > part_pairs) slices = 1;
+  }
+  const int span = ((V + slices - 1) / slices + 1023) & ~1023;  // a multiple of 1024 columns
+  slices = (V + span - 1) / span;
+  float* pv = slices > 1 ? part : nullptr;
+  int* pi = slices > 1 ? reinterpret_cast<int*>(part + (int64_t)rows * slices) : nullptr;
+  hipLaunchKernelGGL(argmax_kernel, dim3(rows, slices), dim3(256), 0, s, z, ldz, V, span, out, pv, pi, flag);
+  if (slices > 1) {
+    if (hipError_t e = hipGetLastError()) return e;
+    hipLaunchKernelGGL(argmax_merge_kernel, dim3((rows + 63) / 64), dim3(64), 0, s, pv, pi, slices, rows, out);
+  }
   return hipGetLastError();
 }
 
