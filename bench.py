@@ -201,6 +201,50 @@ def moe_leg(fwd, steps, stream):
                                 "algorithmic_tflop_per_step": expert_flops / 1e12}}
 
 
+def forward_flops(cfg, B, S):
+    """Algorithmic flops of one prefill: the projections, the head and the attention
+    contractions over the visible (causal, windowed) key pairs."""
+    return sum(kernel_flops(cfg, B, S).values())
+
+
+def configs_leg(fwd, steps, stream):
+    """The other forward configurations at their own shapes: the SmolLM2-shaped model
+    (30 layers, 1 x 512) and the Gemma3-style model (48 layers, 5 local : 1 global,
+    sandwich norms, softcap 30, 1 x 1024): ms per prefill (argmax only), tokens/s and
+    the fraction of the bf16 peak by algorithmic flops."""
+    import torch
+    from synth import workloads as wl
+    from tests.gpu_util import to_device
+    out = {}
+    for cfg in (wl.SMOLLM2_135M, wl.GEMMA3_STYLE):
+        B, S = cfg.batch, cfg.seq
+        ids = wl.draw_ids(cfg)
+        weights = {n: to_device(wl.draw_weight(cfg, n)) for n in wl.weight_shapes(cfg)}
+        model = fwd.Model(cfg, weights, max_tokens=B * S, stream=stream)
+        del weights
+        torch.cuda.empty_cache()
+        argmax = torch.empty((B, S), dtype=torch.int32, device="cuda")
+        for _ in range(2):
+            model.prefill_into(ids, None, None, argmax)                   # warm-up
+        torch.cuda.synchronize()
+        n = max(steps, 1) * (10 if S * B <= 512 else 2)
+        t = time.perf_counter()
+        for _ in range(n):
+            model.prefill_into(ids, None, None, argmax)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t) * 1000.0 / n
+        model.close()
+        del argmax
+        torch.cuda.empty_cache()
+        fl = forward_flops(cfg, B, S)
+        log(f"{cfg.name}: {ms:.3f} ms per prefill of {B} x {S}")
+        out[cfg.name] = {"batch": B, "seq": S, "ms_per_step": ms, "tokens_per_s": B * S / (ms * 1e-3),
+                         "algorithmic_tflop_per_step": fl / 1e12, "tflops": fl / (ms * 1e-3) / 1e12,
+                         "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "outputs": "argmax only"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,6 +258,8 @@ def main():
     ap.add_argument("--variant-leg", action="store_true",
                     help="also time the same shape with QK-norm, tanh-GELU gating and llama3 rope scaling")
     ap.add_argument("--moe-leg", action="store_true", help="also time mixture-of-experts layers (4-layer slice)")
+    ap.add_argument("--configs-leg", action="store_true",
+                    help="also time the SmolLM2-shaped (1 x 512) and Gemma3-style (1 x 1024) prefills")
     args = ap.parse_args()
     if args.timing_steps < 1:
         ap.error("--timing-steps must be at least 1 (the roofline comes from those steps)")
@@ -348,6 +394,9 @@ def main():
         torch.cuda.empty_cache()
     if args.moe_leg:
         result["moe"] = moe_leg(fwd, max(args.steps, 1), stream)
+        torch.cuda.empty_cache()
+    if args.configs_leg:
+        result["configs"] = configs_leg(fwd, max(args.steps, 1), stream)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the oracle on a bounded sample")

@@ -787,6 +787,11 @@ hipError_t launch_cfg(const void* X, const void* W, int M, int N, int K, const E
 }
 
 using CfgSmall = Cfg<128, 128, 32, 4, 2, 2>;
+// 64 x 128 tiles (4 wavefronts of 32 x 64) for problems that give the 128 x 128 kernel
+// fewer than 128 tiles, half the chip's CUs (a 512-token prefill of a 576-wide model:
+// 20 -> 40 tiles); at 240 tiles (a 1024-row, 3840-wide product) the 128 x 128 tiles
+// measured faster.
+using CfgNarrow = Cfg<64, 128, 32, 4, 2, 2, 1, 0>;
 
 
 // ------------------------------------------------------------------ ping-pong kernel
@@ -1318,12 +1323,15 @@ hipError_t launch_dense(const void* X, const void* W, int M, int N, int K, const
   if (M <= 0 || N <= 0) return hipSuccess;
   if (tiled && K % 32) return hipErrorInvalidValue;
   const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t small = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
   if (tiled) {
     if (big >= 256) return launch_pp<CfgBig, Epi, true>(X, W, M, N, K, epi, s);
-    return launch_cfg<CfgSmall, Epi, true>(X, W, M, N, K, epi, s);
+    if (small >= 128) return launch_cfg<CfgSmall, Epi, true>(X, W, M, N, K, epi, s);
+    return launch_cfg<CfgNarrow, Epi, true>(X, W, M, N, K, epi, s);
   }
   if (big >= 256) return launch_pp<CfgBig, Epi, false>(X, W, M, N, K, epi, s);
-  return launch_cfg<CfgSmall, Epi, false>(X, W, M, N, K, epi, s);
+  if (small >= 128) return launch_cfg<CfgSmall, Epi, false>(X, W, M, N, K, epi, s);
+  return launch_cfg<CfgNarrow, Epi, false>(X, W, M, N, K, epi, s);
 }
 
 // Both operands row-major, or both K-tiled (K a multiple of 32).
