@@ -106,13 +106,16 @@ __global__ __launch_bounds__(256) void add_norm_kernel(const float* __restrict__
   if (row >= rows) return;
   const int64_t off = (int64_t)row * H;
   if (H <= kMaxV * 256) {
-    float4 uv[kMaxV], xv[kMaxV];
+    // gains go out with the rows (post-norm gains) and before the second reduction
+    // (next-norm gains), so no load waits behind a reduction
+    float4 uv[kMaxV], xv[kMaxV], g[kMaxV];
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxV; ++j) {
       const int i = lane * 4 + j * 256;
       uv[j] = i < H ? Vec4<float>::load(u + off + i) : float4{0.f, 0.f, 0.f, 0.f};
       xv[j] = i < H ? Vec4<float>::load(xin + off + i) : float4{0.f, 0.f, 0.f, 0.f};
+      g[j] = i < H ? Vec4<float>::load(wpost + i) : float4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int j = 0; j < kMaxV; ++j) ss += sumsq4(uv[j]);
@@ -123,10 +126,15 @@ __global__ __launch_bounds__(256) void add_norm_kernel(const float* __restrict__
     for (int j = 0; j < kMaxV; ++j) {
       const int i = lane * 4 + j * 256;
       if (i >= H) continue;
-      const float4 n = mul4(uv[j], Vec4<float>::load(wpost + i), ru);
+      const float4 n = mul4(uv[j], g[j], ru);
       xv[j] = float4{xv[j].x + n.x, xv[j].y + n.y, xv[j].z + n.z, xv[j].w + n.w};
       Vec4<float>::store(xout + off + i, xv[j]);
       sx += sumsq4(xv[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxV; ++j) {
+      const int i = lane * 4 + j * 256;
+      g[j] = i < H ? Vec4<float>::load(wnext + i) : float4{0.f, 0.f, 0.f, 0.f};
     }
     sx = wave_sum(sx);
     const float rx = fast_rsqrt(sx / (float)H + eps);
@@ -134,7 +142,7 @@ __global__ __launch_bounds__(256) void add_norm_kernel(const float* __restrict__
     for (int j = 0; j < kMaxV; ++j) {
       const int i = lane * 4 + j * 256;
       if (i >= H) continue;
-      const float4 v = mul4(xv[j], Vec4<float>::load(wnext + i), rx);
+      const float4 v = mul4(xv[j], g[j], rx);
       Vec4<T>::store(y + (tiled ? tiled_index(row, i, H) : off + i), v);
       if (y32) Vec4<float>::store(y32 + off + i, v);
     }
