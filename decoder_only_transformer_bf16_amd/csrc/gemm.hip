@@ -788,9 +788,9 @@ hipError_t launch_cfg(const void* X, const void* W, int M, int N, int K, const E
 
 using CfgSmall = Cfg<128, 128, 32, 4, 2, 2>;
 // 64 x 128 tiles (4 wavefronts of 32 x 64) for problems that give the 128 x 128 kernel
-// fewer than 128 tiles, half the chip's CUs (a 512-token prefill of a 576-wide model:
-// 20 -> 40 tiles); at 240 tiles (a 1024-row, 3840-wide product) the 128 x 128 tiles
-// measured faster.
+// fewer tiles than the chip has CUs (a 512-token prefill of a 576-wide model: 20 -> 40
+// tiles; a 1024-row, 3840-wide product: 240 -> 480, K 15360 in 141-162 us instead of
+// 146-175 us interleaved).
 using CfgNarrow = Cfg<64, 128, 32, 4, 2, 2, 1, 0>;
 
 
@@ -1326,11 +1326,11 @@ hipError_t launch_dense(const void* X, const void* W, int M, int N, int K, const
   const int64_t small = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
   if (tiled) {
     if (big >= 256) return launch_pp<CfgBig, Epi, true>(X, W, M, N, K, epi, s);
-    if (small >= 128) return launch_cfg<CfgSmall, Epi, true>(X, W, M, N, K, epi, s);
+    if (small >= 256) return launch_cfg<CfgSmall, Epi, true>(X, W, M, N, K, epi, s);
     return launch_cfg<CfgNarrow, Epi, true>(X, W, M, N, K, epi, s);
   }
   if (big >= 256) return launch_pp<CfgBig, Epi, false>(X, W, M, N, K, epi, s);
-  if (small >= 128) return launch_cfg<CfgSmall, Epi, false>(X, W, M, N, K, epi, s);
+  if (small >= 256) return launch_cfg<CfgSmall, Epi, false>(X, W, M, N, K, epi, s);
   return launch_cfg<CfgNarrow, Epi, false>(X, W, M, N, K, epi, s);
 }
 
