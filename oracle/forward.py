@@ -45,9 +45,16 @@ def _f32(a) -> np.ndarray:
 def round_bf16(a) -> np.ndarray:
     """float32 -> nearest bf16 (ties to even) -> float32. Used only by the diagnostic
     mode of forward(), which rounds where a bf16 implementation must round, to tell a
-    precision deficit from a bug; the reference itself never rounds activations."""
-    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    precision deficit from a bug; the reference itself never rounds activations.
+
+    The IEEE conversion: finite values round to nearest, ties to the even neighbour
+    (overflowing to infinity past the largest bf16); infinities and zeros keep their
+    sign; a NaN stays a NaN (quietened, so that a payload held only in the dropped low
+    bits cannot turn into an infinity)."""
+    x = np.asarray(a, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
     r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    r = np.where(np.isnan(x), (u | 0x400000) >> 16 << 16, r)
     return r.astype(np.uint32).view(np.float32)
 
 
@@ -247,6 +254,16 @@ def _attention_rounded(q, k, v, window: int) -> np.ndarray:
     return out
 
 
+def _bf16_point(a, point: str, trace) -> np.ndarray:
+    """One rounding point of the bf16 diagnostic: round_bf16(a); with a trace dict the
+    rounded tensor is also kept as trace["bf16." + point] (a test hook, so that each
+    point can be checked as one rounding of the exact value of its inputs)."""
+    r = round_bf16(a)
+    if trace is not None:
+        trace["bf16." + point] = r
+    return r
+
+
 # ---------------------------------------------------------------- feed-forward
 def silu(z) -> np.ndarray:
     """silu(z) = z / (1 + e^-z), float64 in and out."""
@@ -351,7 +368,10 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
     output, SwiGLU output) to bf16, as a bf16 implementation does.
     Slots ([fp] Theorem 1): 0 = embedding, l+1 = after layer l, L+1 = final norm.
     trace: optional dict; receives "moe_logits.<l>" = the router logits [B*S, E] of each
-    mixture-of-experts layer (to judge how decided the routing was).
+    mixture-of-experts layer (to judge how decided the routing was), and with
+    bf16_points every rounded tensor as "bf16.<l>.<point>" (points n_attn, q_proj,
+    k_proj (QK-norm only), v, q, k, o, n_ffn, a) and "bf16.h", plus the residual after
+    each attention sublayer as "bf16.<l>.x_attn".
     """
     ids = np.asarray(ids)
     B, S = ids.shape
@@ -374,29 +394,33 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
     if want_hidden:
         hidden[0] = x
 
-    rb = round_bf16 if bf16_points else (lambda a: a)
+    def rb(a, point):  # a rounding point of the bf16 diagnostic (identity otherwise)
+        return _bf16_point(a, point, trace) if bf16_points else a
+
     for l in range(L):
         p = f"layers.{l}."
         window = cfg.sliding_window if kinds[l] == "local" else 0
         # attention sublayer
-        n = rb(rmsnorm(x, weights[p + "attn_norm"], eps, goff))
+        n = rb(rmsnorm(x, weights[p + "attn_norm"], eps, goff), f"{l}.n_attn")
         q = gemm(n, weights[p + "wq"]).reshape(B, S, Hq, D)
         k = gemm(n, weights[p + "wk"]).reshape(B, S, Hkv, D)
-        v = rb(gemm(n, weights[p + "wv"]).reshape(B, S, Hkv, D))
+        v = rb(gemm(n, weights[p + "wv"]).reshape(B, S, Hkv, D), f"{l}.v")
         if qk_norm:  # each head's q and k normalised over its D dims, before RoPE (qwen3 / gemma3)
-            q = rmsnorm(rb(q), weights[p + "q_norm"], eps, goff)
-            k = rmsnorm(rb(k), weights[p + "k_norm"], eps, goff)
+            q = rmsnorm(rb(q, f"{l}.q_proj"), weights[p + "q_norm"], eps, goff)
+            k = rmsnorm(rb(k, f"{l}.k_proj"), weights[p + "k_norm"], eps, goff)
         f, mult = rope_frequencies(cfg, kinds[l], S)
-        q = rb(np.stack([rotate(q[b], positions, f, mult) for b in range(B)]))
-        k = rb(np.stack([rotate(k[b], positions, f, mult) for b in range(B)]))
-        o = rb(_attention_rounded(q, k, v, window) if bf16_points else attention(q, k, v, window))
+        q = rb(np.stack([rotate(q[b], positions, f, mult) for b in range(B)]), f"{l}.q")
+        k = rb(np.stack([rotate(k[b], positions, f, mult) for b in range(B)]), f"{l}.k")
+        o = rb(_attention_rounded(q, k, v, window) if bf16_points else attention(q, k, v, window), f"{l}.o")
         o = o.reshape(B, S, Hq * D)
         u = gemm(o, weights[p + "wo"])
         if sandwich:
             u = rmsnorm(u, weights[p + "post_attn_norm"], eps, goff)
         x = _f32(_f64(x) + _f64(u))
+        if bf16_points and trace is not None:
+            trace[f"bf16.{l}.x_attn"] = x
         # feed-forward sublayer (dense, or mixture of experts on the layers the map names)
-        n = rb(rmsnorm(x, weights[p + "ffn_norm"], eps, goff))
+        n = rb(rmsnorm(x, weights[p + "ffn_norm"], eps, goff), f"{l}.n_ffn")
         if ffn_kinds[l] == "moe":
             zs = [] if trace is not None else None
             d = moe_ffn(n, weights[p + "router"], weights[p + "expert_gate"], weights[p + "expert_up"],
@@ -404,7 +428,7 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
             if trace is not None:
                 trace[f"moe_logits.{l}"] = zs[0]
         else:
-            a = rb(gated_ffn(gemm(n, weights[p + "w_gate"]), gemm(n, weights[p + "w_up"]), act))
+            a = rb(gated_ffn(gemm(n, weights[p + "w_gate"]), gemm(n, weights[p + "w_up"]), act), f"{l}.a")
             d = gemm(a, weights[p + "w_down"])
         if sandwich:
             d = rmsnorm(d, weights[p + "post_ffn_norm"], eps, goff)
@@ -417,7 +441,7 @@ def forward(cfg, weights, ids, want_logits: bool = True, want_hidden: bool = Tru
         hidden[L + 1] = h
     if not want_logits:                          # hidden slots only: the head is not needed
         return {"argmax": None, "hidden": hidden, "logits": None}
-    z = softcap(gemm(rb(h), E), cfg.final_logit_softcap)                # tied head
+    z = softcap(gemm(rb(h, "h"), E), cfg.final_logit_softcap)           # tied head
     return {"argmax": argmax(z), "hidden": hidden, "logits": z}
 
 

@@ -623,3 +623,274 @@ def test_forward_moe_layer_with_dense_copies_equals_dense_forward():
     for s in range(dense.n_layers + 2):
         np.testing.assert_allclose(b["hidden"][s], a["hidden"][s], rtol=1e-5, atol=1e-6)
     assert set(wl.weight_shapes(moe)) == set(wm)                   # the recipe names the same tensors
+
+
+# ---------------------------------------------------------------- bf16 diagnostic
+# The bf16-rounded forward sets the floor that deep bf16 configurations are gated
+# against, so its rounding function and every rounding point are pinned here: the
+# function against hand-worked round-to-nearest-even bit patterns, the points against
+# one rounding (by torch's own bf16 conversion, an independent implementation) of the
+# exact value of each point's rounded inputs.
+
+def _bits(x):
+    return np.asarray(x, np.float32).view(np.uint32)
+
+
+def _f(bits):
+    return np.asarray(bits, np.uint32).view(np.float32)
+
+
+# (input bits, expected bf16 bits << 16): worked by hand from the bf16 grid
+_RNE_CASES = [
+    (0x3F800000, 0x3F800000),  # 1.0 is a bf16 value: unchanged
+    (0x3F808000, 0x3F800000),  # 1 + 2^-8, halfway 1.0 / 1 + 2^-7: tie to the even 1.0 (down)
+    (0x3F818000, 0x3F820000),  # 1 + 3 * 2^-8, halfway: tie to the even 1 + 2^-6 (up)
+    (0x3F808001, 0x3F810000),  # just above halfway: up
+    (0x3F807FFF, 0x3F800000),  # just below halfway: down
+    (0x3FFF8000, 0x40000000),  # halfway 1.9921875 / 2.0: tie to even carries into the exponent
+    (0x3FFFC000, 0x40000000),  # above halfway under the exponent boundary: 2.0
+    (0xBF818000, 0xBF820000),  # negative tie: sign kept, magnitude to even
+    (0xBF808000, 0xBF800000),
+    (0x7F7F0000, 0x7F7F0000),  # the largest bf16 value stays
+    (0x7F7F7FFF, 0x7F7F0000),  # below halfway to the next binade: the largest bf16
+    (0x7F7FFFFF, 0x7F800000),  # the largest float32 overflows to infinity
+    (0xFF7FFFFF, 0xFF800000),
+    (0x7F800000, 0x7F800000),  # infinities pass through
+    (0xFF800000, 0xFF800000),
+    (0x00000000, 0x00000000),  # zeros keep their sign
+    (0x80000000, 0x80000000),
+    (0x00008000, 0x00000000),  # subnormal tie between 0 and the smallest bf16: even 0
+    (0x00018000, 0x00020000),  # subnormal tie between odd 1 and even 2 ulps: up
+]
+
+
+def test_round_bf16_hand_worked_bit_patterns():
+    got = _bits(oracle.round_bf16(_f([c[0] for c in _RNE_CASES])))
+    want = np.array([c[1] for c in _RNE_CASES], np.uint32)
+    bad = [(hex(c[0]), hex(int(g)), hex(c[1])) for c, g in zip(_RNE_CASES, got) if g != c[1]]
+    assert not bad, bad
+
+
+def test_round_bf16_nan_stays_nan_and_agrees_with_torch():
+    import torch
+    nan = _f([0x7FC00000, 0x7F800001, 0xFF800001, 0x7FBFFFFF])  # quiet, low-payload and signalling NaNs
+    assert np.all(np.isnan(oracle.round_bf16(nan)))
+    # random finite values over many binades (subnormals included): same bits as torch's conversion
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-140, 120, 200000))).astype(np.float32)
+    x = x[np.isfinite(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(_bits(oracle.round_bf16(x)), _bits(ref))
+    # idempotent, and the result always has zero low bits
+    r = oracle.round_bf16(x)
+    assert np.array_equal(_bits(oracle.round_bf16(r)), _bits(r))
+    assert not np.any(_bits(r) & 0xFFFF)
+
+
+def test_attention_rounded_equals_attention_when_probabilities_are_bf16_exact():
+    # two visible keys with scores 0 and ln 3 give p = (1/4, 3/4), both bf16 values:
+    # rounding the probabilities then changes nothing
+    D = 4
+    q = np.zeros((1, 2, 1, D), np.float32)
+    k = np.zeros((1, 2, 1, D), np.float32)
+    q[0, 1, 0, 0] = 1.0
+    k[0, 1, 0, 0] = np.float32(math.log(3.0) * math.sqrt(D))
+    v = rng.standard_normal((1, 2, 1, D)).astype(np.float32)
+    p = oracle.attention_probs(q, k)[0, 0, 1]
+    assert abs(p[0] - 0.25) < 1e-7 and abs(p[1] - 0.75) < 1e-7
+    a = oracle.attention(q, k, v)
+    b = oracle.forward_module._attention_rounded(q, k, v, 0)
+    # the rounded probabilities are within 1e-7 of 1/4 and 3/4, which round to exactly them
+    np.testing.assert_array_equal(b[0, 1, 0], (0.25 * v[0, 0, 0].astype(np.float64)
+                                               + 0.75 * v[0, 1, 0].astype(np.float64)).astype(np.float32))
+    np.testing.assert_allclose(a, b, rtol=0, atol=2e-7)
+
+
+def test_attention_rounded_rounds_probabilities_not_the_normaliser():
+    # three equal scores: p = 1/3 each; bf16(1/3) = 0x3EAB = 0.333984375, and the output is
+    # 0.333984375 * (v0 + v1 + v2) (the rounded weights are not renormalised to sum 1)
+    D = 2
+    q = np.zeros((1, 3, 1, D), np.float32)
+    k = np.zeros((1, 3, 1, D), np.float32)
+    v = np.array([1.0, 2.0, 4.0], np.float32).reshape(1, 3, 1, 1) * np.ones((1, 1, 1, D), np.float32)
+    o = oracle.forward_module._attention_rounded(q, k, v, 0)
+    assert o[0, 2, 0, 0] == np.float32(0.333984375 * 7.0)
+    assert o[0, 1, 0, 0] == np.float32(0.5 * 3.0)     # two keys: 1/2 is exact
+    assert o[0, 0, 0, 0] == np.float32(1.0)           # one key: weight 1
+
+
+def _rne_torch(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+_POINT_CFG = wl.TINY_F32.replace(n_layers=2, seq=11, batch=2)
+
+
+def _check_bf16_points(cfg, seed=7):
+    """Every rounding point of the diagnostic is one round-to-nearest-even of the exact
+    value of that point computed from the previous points' rounded tensors; the
+    unrounded tensors (residual, slots, logits) are not on the bf16 grid. Raises
+    AssertionError naming the first point that fails."""
+    w = wl.LazyWeights(cfg, seed=seed, cache=True)
+    ids = wl.draw_ids(cfg)
+    tr = {}
+    out = oracle.forward(cfg, w, ids, bf16_points=True, trace=tr)
+    B, S = ids.shape
+    H, Hq, Hkv, D = cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    eps = cfg.rms_eps
+    pos = np.arange(S)
+
+    def same(point, got, want):
+        assert np.array_equal(_bits(got), _bits(want)), f"point {point}: not one rounding of the exact value"
+        assert not np.any(_bits(got) & 0xFFFF), f"point {point}: not on the bf16 grid"
+
+    x = out["hidden"][0]
+    for l in range(cfg.n_layers):
+        p = f"layers.{l}."
+        g = lambda n: tr[f"bf16.{l}.{n}"]  # noqa: E731
+        same(f"{l}.n_attn", g("n_attn"), _rne_torch(oracle.rmsnorm(x, w[p + "attn_norm"], eps)))
+        n = g("n_attn")
+        same(f"{l}.v", g("v"), _rne_torch(oracle.gemm(n, w[p + "wv"]).reshape(B, S, Hkv, D)))
+        f, m = oracle.rope_frequencies(cfg, cfg.kinds()[l], S)
+        qp = oracle.gemm(n, w[p + "wq"]).reshape(B, S, Hq, D)
+        kp = oracle.gemm(n, w[p + "wk"]).reshape(B, S, Hkv, D)
+        same(f"{l}.q", g("q"), _rne_torch(np.stack([oracle.rotate(qp[b], pos, f, m) for b in range(B)])))
+        same(f"{l}.k", g("k"), _rne_torch(np.stack([oracle.rotate(kp[b], pos, f, m) for b in range(B)])))
+        # o: the exact probabilities of the rounded q, k, rounded once, times the rounded v
+        # (float64 sum, one float32 rounding), then rounded to bf16
+        window = cfg.sliding_window if cfg.kinds()[l] == "local" else 0
+        P = oracle.attention_probs(g("q"), g("k"), window)
+        o = np.empty((B, S, Hq, D), np.float32)
+        for b in range(B):
+            for h in range(Hq):
+                pr = _rne_torch(P[b, h].astype(np.float32)).astype(np.float64)
+                o[b, :, h, :] = (pr @ g("v")[b, :, h // (Hq // Hkv), :].astype(np.float64)).astype(np.float32)
+        same(f"{l}.o", g("o"), _rne_torch(o))
+        u = oracle.gemm(g("o").reshape(B, S, Hq * D), w[p + "wo"])
+        if cfg.norm_placement == "sandwich":  # the post-norm works on the fp32 product: no rounding point
+            u = oracle.rmsnorm(u, w[p + "post_attn_norm"], eps)
+        xa = (x.astype(np.float64) + u).astype(np.float32)
+        assert np.array_equal(_bits(g("x_attn")), _bits(xa)), f"{l}.x_attn"
+        assert np.any(_bits(xa) & 0xFFFF), f"{l}.x_attn should stay unrounded"
+        same(f"{l}.n_ffn", g("n_ffn"), _rne_torch(oracle.rmsnorm(xa, w[p + "ffn_norm"], eps)))
+        a = oracle.swiglu(oracle.gemm(g("n_ffn"), w[p + "w_gate"]), oracle.gemm(g("n_ffn"), w[p + "w_up"]))
+        same(f"{l}.a", g("a"), _rne_torch(a))
+        d = oracle.gemm(g("a"), w[p + "w_down"])
+        if cfg.norm_placement == "sandwich":
+            d = oracle.rmsnorm(d, w[p + "post_ffn_norm"], eps)
+        x = (xa.astype(np.float64) + d).astype(np.float32)
+        assert np.array_equal(_bits(out["hidden"][l + 1]), _bits(x)), f"slot {l + 1}"
+        assert np.any(_bits(x) & 0xFFFF), f"slot {l + 1} should stay unrounded"
+    hfin = out["hidden"][cfg.n_layers + 1]
+    assert np.any(_bits(hfin) & 0xFFFF), "the final-norm slot stays unrounded"
+    same("h", tr["bf16.h"], _rne_torch(hfin))
+    z = oracle.softcap(oracle.gemm(tr["bf16.h"], w["embed"]), cfg.final_logit_softcap)
+    assert np.array_equal(_bits(out["logits"]), _bits(z)), "logits from the rounded final norm"
+
+
+# the same points on the sandwich / window / softcap / scaled-embedding path
+_POINT_CFG_SANDWICH = _POINT_CFG.replace(norm_placement="sandwich", sliding_window=4,
+                                         layer_kind=("local", "global"), final_logit_softcap=2.0,
+                                         embed_scale_mode="bf16_sqrt_hidden")
+
+
+@pytest.mark.parametrize("cfg", [_POINT_CFG, _POINT_CFG_SANDWICH], ids=["pre", "sandwich"])
+def test_bf16_points_are_single_roundings_of_exact_values(cfg):
+    _check_bf16_points(cfg)
+
+
+def test_bf16_points_pin_fails_on_planted_rounding_mistakes(monkeypatch):
+    """Each planted mistake in the diagnostic (a dropped point, a truncating rounding,
+    unrounded probabilities, an extra rounding of the residual) fails the point pin."""
+    fm = oracle.forward_module
+    real_point, real_round, real_attn = fm._bf16_point, fm.round_bf16, fm._attention_rounded
+
+    def dropped(name):
+        def f(a, point, trace):
+            r = np.asarray(a, np.float32) if point.endswith(name) else real_round(a)
+            if trace is not None:
+                trace["bf16." + point] = r
+            return r
+        return f
+
+    def truncate(a):
+        u = np.asarray(a, np.float32).view(np.uint32)
+        return (u & 0xFFFF0000).view(np.float32)
+
+    plants = [(n, "_bf16_point", dropped(n)) for n in ("n_attn", ".v", ".q", ".k", ".o", "n_ffn", ".a", "h")]
+    plants += [("truncate", "round_bf16", truncate), ("exact p", "_attention_rounded",
+                                                     lambda q, k, v, window: oracle.attention(q, k, v, window))]
+    for label, attr, fn in plants:
+        monkeypatch.setattr(fm, attr, fn)
+        with pytest.raises(AssertionError):
+            _check_bf16_points(_POINT_CFG)
+        monkeypatch.setattr(fm, "_bf16_point", real_point)
+        monkeypatch.setattr(fm, "round_bf16", real_round)
+        monkeypatch.setattr(fm, "_attention_rounded", real_attn)
+    # an extra rounding of the residual stream
+    real_f32 = fm._f32
+    monkeypatch.setattr(fm, "_f32", lambda a: real_round(real_f32(a)))
+    with pytest.raises(AssertionError):
+        _check_bf16_points(_POINT_CFG)
+    monkeypatch.setattr(fm, "_f32", real_f32)
+    _check_bf16_points(_POINT_CFG)  # and the real diagnostic passes again
+
+
+# ---------------------------------------------------------------- longrope / llama3 closed forms
+def _longrope_cfg(s, L0=64):
+    D = wl.TINY_F32.head_dim
+    return wl.TINY_F32.replace(rope_scaling="longrope", rope_factor=float(s), rope_original_max_pos=L0,
+                               rope_short_factor=(1.0,) * (D // 2), rope_long_factor=(2.0,) * (D // 2))
+
+
+@pytest.mark.parametrize("L0", [64, 4096])
+def test_longrope_multiplier_special_cases(L0):
+    # sqrt(1 + ln s / ln L0): s = L0 gives sqrt 2, s = L0^2 gives sqrt 3, no extension gives 1
+    _, m = oracle.rope_frequencies(_longrope_cfg(L0, L0), "global", 8)
+    assert m == pytest.approx(math.sqrt(2.0), rel=1e-14)
+    _, m = oracle.rope_frequencies(_longrope_cfg(L0 * L0, L0), "global", 8)
+    assert m == pytest.approx(math.sqrt(3.0), rel=1e-14)
+    for s in (1.0, 0.5):
+        _, m = oracle.rope_frequencies(_longrope_cfg(s, L0), "global", 8)
+        assert m == 1.0
+    # the multiplier grows with the extension and does not depend on the sequence length
+    _, a = oracle.rope_frequencies(_longrope_cfg(8.0, L0), "global", 8)
+    _, b = oracle.rope_frequencies(_longrope_cfg(8.0, L0), "global", L0 + 5)
+    _, c = oracle.rope_frequencies(_longrope_cfg(16.0, L0), "global", 8)
+    assert a == b and 1.0 < a < c
+
+
+def test_longrope_multiplier_pin_fails_on_planted_mistakes(monkeypatch):
+    # a multiplier with the logarithms swapped or a missing square root fails the special cases
+    real = oracle.forward_module.rope_frequencies
+
+    def planted(variant):
+        def f(cfg, kind, seq_len):
+            inv, m = real(cfg, kind, seq_len)
+            s, L0 = cfg.rope_factor, cfg.rope_original_max_pos
+            if s <= 1.0:
+                return inv, m
+            if variant == "swapped":
+                return inv, math.sqrt(1.0 + math.log(L0) / math.log(s))
+            return inv, 1.0 + math.log(s) / math.log(L0)
+        return f
+
+    for variant in ("swapped", "no_sqrt"):
+        monkeypatch.setattr(oracle, "rope_frequencies", planted(variant))
+        with pytest.raises(AssertionError):
+            test_longrope_multiplier_special_cases(64)
+        monkeypatch.setattr(oracle, "rope_frequencies", real)
+
+
+def test_llama3_band_interior_hand_worked():
+    # place the original context so that a chosen pair sits a quarter and a half of the
+    # way through the blended band: L0 / wavelength = lo + t (hi - lo) gives
+    # f' = (1 - t) f / s + t f, i.e. f (0.75 / s + 0.25) and f (0.5 / s + 0.5)
+    D, s, lo, hi = 128, 8.0, 1.0, 4.0
+    plain = 500000.0 ** (-2.0 * np.arange(D // 2) / D)
+    k = 40
+    wavelen = 2 * math.pi / plain[k]
+    for t, factor in ((0.25, 0.75 / s + 0.25), (0.5, 0.5 / s + 0.5), (0.75, 0.25 / s + 0.75)):
+        L0 = wavelen * (lo + t * (hi - lo))
+        f, _ = oracle.rope_frequencies(_llama3_cfg(rope_original_max_pos=L0, rope_factor=s), "global", 16)
+        assert f[k] == pytest.approx(plain[k] * factor, rel=1e-12)
