@@ -72,10 +72,13 @@ def cpu_baseline(cfg, S):
     t_layer = max(times[1] - times[0], 1e-9)
     per_row = times[0] + cfg.n_layers * t_layer
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    nproc, model = cpu_info()
     return {
         "value": S / per_row,
         "unit": "tokens/s",
         "cores": threads,
+        "nproc": nproc,
+        "cpu_model": model,
         "kind": "oracle",
         "sample": (f"1 row x {S} tokens: embedding+final norm+LM head ({times[0]:.1f} s) and one decoder layer "
                    f"({t_layer:.1f} s) timed, scaled to {cfg.n_layers} layers; float64 numpy oracle"),
@@ -119,13 +122,12 @@ def variant_leg(fwd, cfg0, ids, steps, stream):
     head once: T * (Hq + Hkv) * D * 2 B each way per layer)."""
     import torch
     from synth import workloads as wl
-    from tests.gpu_util import to_device
     cfg = cfg0.replace(qk_norm=True, ffn_act="gelu_tanh", rope_scaling="llama3", rope_factor=8.0,
                        rope_low_freq_factor=1.0, rope_high_freq_factor=4.0, rope_original_max_pos=8192,
                        name="llama3-8b-shape-variants")
     B, S = ids.shape
     T = B * S
-    weights = {n: to_device(wl.draw_weight(cfg, n)) for n in wl.weight_shapes(cfg)}
+    weights = {n: fwd.to_device(wl.draw_weight(cfg, n)) for n in wl.weight_shapes(cfg)}
     model = fwd.Model(cfg, weights, max_tokens=T, stream=stream)
     del weights
     torch.cuda.empty_cache()
@@ -164,12 +166,11 @@ def moe_leg(fwd, steps, stream):
     down per layer)."""
     import torch
     from synth import workloads as wl
-    from tests.gpu_util import to_device
     cfg = wl.ModelConfig("moe-30b-a3b-shape-4L", 4, 2048, 32, 4, 128, 6144, 151936, rope_theta=1e6, qk_norm=True,
                          n_experts=128, n_experts_per_tok=8, moe_ffn=768, batch=8, seq=2048)
     B, S = cfg.batch, cfg.seq
     T = B * S
-    weights = {n: to_device(wl.draw_weight(cfg, n)) for n in wl.weight_shapes(cfg)}
+    weights = {n: fwd.to_device(wl.draw_weight(cfg, n)) for n in wl.weight_shapes(cfg)}
     model = fwd.Model(cfg, weights, max_tokens=T, stream=stream)
     del weights
     torch.cuda.empty_cache()
@@ -201,6 +202,109 @@ def moe_leg(fwd, steps, stream):
                                 "algorithmic_tflop_per_step": expert_flops / 1e12}}
 
 
+def gemm_sweep_leg(fwd, stream, calls):
+    """The standalone projection Y = X·Wᵀ over the [P, in, out] sweep (bf16 N(0, 1)
+    operands, fp32 output): per shape, the median of `calls` fwd_gemm launches, each
+    bracketed by HIP events on the stream the call runs on; TFLOP/s by algorithmic flops
+    2 P in out, against the bf16 peak, and the achieved HBM rate by algorithmic bytes
+    2 (P in + out in) + 4 P out."""
+    import torch
+    from synth import workloads as wl
+    out = []
+    for P, K, N in wl.GEMM_SWEEP:
+        Xh, Wh = wl.draw_gemm(P, K, N)
+        X, W = fwd.to_device(Xh), fwd.to_device(Wh)
+        del Xh, Wh
+        Y = torch.empty((P, N), dtype=torch.float32, device="cuda")
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                fwd.gemm(X, W, Y, stream=stream)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+            for a, b in ev:
+                a.record(stream)
+                fwd.gemm(X, W, Y, stream=stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)
+        med = ms[len(ms) // 2]
+        flops, nbytes = 2.0 * P * K * N, 2.0 * (P * K + N * K) + 4.0 * P * N
+        tf = flops / (med * 1e-3) / 1e12
+        out.append({"shape_P_in_out": [P, K, N], "calls": calls, "median_us": med * 1e3, "min_us": ms[0] * 1e3,
+                    "tflops": tf, "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS,
+                    "achieved_gbs": nbytes / (med * 1e-3) / 1e9})
+        log(f"gemm [{P},{K},{N}]: {med * 1e3:.1f} us median of {calls}, {tf:.1f} TFLOP/s "
+            f"({tf / PEAK_BF16_TFLOPS:.3f} of peak)")
+        del X, W, Y
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_info():
+    """(logical CPUs, CPU model name) of this host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
+def cpu_oracle_other_workloads():
+    """The oracle on the other workloads, each bounded to seconds: the tiny fp32 model
+    and the SmolLM2-shaped model in full, the Gemma3-style model as embedding + final
+    norm + head and one layer scaled to 48 layers (as the Llama sample), and the GEMM
+    sweep (the two large shapes on 256 rows of X, scaled to P rows: every output row is
+    an independent product)."""
+    import numpy as np
+
+    import oracle
+    from synth import bf16_bits_to_f32
+    from synth import workloads as wl
+    res = {}
+    for cfg in (wl.TINY_F32, wl.SMOLLM2_135M):
+        w = wl.LazyWeights(cfg, cache=True)
+        for name in wl.weight_shapes(cfg):
+            w[name]
+        ids = wl.draw_ids(cfg)
+        t = time.perf_counter()
+        oracle.forward(cfg, w, ids, want_hidden=False)
+        dt = time.perf_counter() - t
+        res[cfg.name] = {"tokens_per_s": ids.size / dt, "seconds": dt, "sample": f"full prefill {ids.shape}"}
+        del w
+    cfg = wl.GEMMA3_STYLE
+    ids = wl.draw_ids(cfg)
+    times = {}
+    for n in (0, 1):
+        c = cfg.replace(n_layers=n, layer_kind=cfg.layer_kind[:n])
+        w = wl.LazyWeights(c, cache=True)
+        for name in wl.weight_shapes(c):
+            w[name]
+        t = time.perf_counter()
+        oracle.forward(c, w, ids, want_hidden=False)
+        times[n] = time.perf_counter() - t
+        del w
+    per = times[0] + cfg.n_layers * max(times[1] - times[0], 1e-9)
+    res[cfg.name] = {"tokens_per_s": ids.size / per, "seconds_extrapolated": per,
+                     "sample": f"1 x {ids.shape[1]} tokens: head ({times[0]:.1f} s) + one layer, scaled to 48 layers"}
+    sweep = []
+    for P, K, N in wl.GEMM_SWEEP:
+        Xh, Wh = wl.draw_gemm(P, K, N)
+        rows = min(P, 256)
+        X, W = bf16_bits_to_f32(Xh[:rows]), bf16_bits_to_f32(Wh)
+        t = time.perf_counter()
+        oracle.gemm(X, W)
+        dt = (time.perf_counter() - t) * P / rows
+        sweep.append({"shape_P_in_out": [P, K, N], "seconds": dt, "gflops": 2.0 * P * K * N / dt / 1e9,
+                      "sample": f"{rows} of {P} rows" + (", scaled" if rows < P else "")})
+        del X, W, Xh, Wh
+    res["gemm_sweep"] = sweep
+    return res
+
+
 def forward_flops(cfg, B, S):
     """Algorithmic flops of one prefill: the projections, the head and the attention
     contractions over the visible (causal, windowed) key pairs."""
@@ -214,12 +318,11 @@ def configs_leg(fwd, steps, stream):
     the fraction of the bf16 peak by algorithmic flops."""
     import torch
     from synth import workloads as wl
-    from tests.gpu_util import to_device
     out = {}
     for cfg in (wl.SMOLLM2_135M, wl.GEMMA3_STYLE):
         B, S = cfg.batch, cfg.seq
         ids = wl.draw_ids(cfg)
-        weights = {n: to_device(wl.draw_weight(cfg, n)) for n in wl.weight_shapes(cfg)}
+        weights = {n: fwd.to_device(wl.draw_weight(cfg, n)) for n in wl.weight_shapes(cfg)}
         model = fwd.Model(cfg, weights, max_tokens=B * S, stream=stream)
         del weights
         torch.cuda.empty_cache()
@@ -260,6 +363,8 @@ def main():
     ap.add_argument("--moe-leg", action="store_true", help="also time mixture-of-experts layers (4-layer slice)")
     ap.add_argument("--configs-leg", action="store_true",
                     help="also time the SmolLM2-shaped (1 x 512) and Gemma3-style (1 x 1024) prefills")
+    ap.add_argument("--gemm-calls", type=int, default=20,
+                    help="fwd_gemm calls timed per shape of the standalone GEMM sweep (0: skip the sweep)")
     args = ap.parse_args()
     if args.timing_steps < 1:
         ap.error("--timing-steps must be at least 1 (the roofline comes from those steps)")
@@ -273,7 +378,6 @@ def main():
 
     from decoder_only_transformer_bf16_amd import fwd
     from synth import workloads as wl
-    from tests.gpu_util import to_device
 
     cfg = wl.LLAMA3_8B
     B, S = cfg.batch, cfg.seq
@@ -285,7 +389,7 @@ def main():
     t0 = time.time()
     weights = {}
     for name in wl.weight_shapes(cfg):
-        weights[name] = to_device(wl.draw_weight(cfg, name))
+        weights[name] = fwd.to_device(wl.draw_weight(cfg, name))
     stream = torch.cuda.Stream()
     model = fwd.Model(cfg, weights, max_tokens=T, stream=stream)
     del weights
@@ -398,9 +502,14 @@ def main():
     if args.configs_leg:
         result["configs"] = configs_leg(fwd, max(args.steps, 1), stream)
         torch.cuda.empty_cache()
+    if args.gemm_calls > 0:
+        result["gemm_sweep"] = gemm_sweep_leg(fwd, stream, max(args.gemm_calls, 20))
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(cfg, S)
+        log("cpu oracle on the other workloads (bounded samples)")
+        result["cpu_baseline"]["other_workloads"] = cpu_oracle_other_workloads()
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

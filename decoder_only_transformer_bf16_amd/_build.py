@@ -52,9 +52,6 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-if __name__ == "__main__":
-    print(build(verbose=True))
-
 
 def source_digest(files=("gemm.hip", "common.h", "kernels.h")) -> str:
     """sha256 over the GEMM kernel sources and the compile flags (ties stored counter
@@ -67,3 +64,7 @@ def source_digest(files=("gemm.hip", "common.h", "kernels.h")) -> str:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -184,6 +184,15 @@ def output_sizes(cfg, B: int, S: int, max_tokens: Optional[int] = None) -> Dict[
     return {f: getattr(s, f) for f, _ in FwdSizes._fields_}
 
 
+def to_device(arr: np.ndarray):
+    """Host array in storage form -> device tensor on the current GPU: float32 stays
+    float32, uint16 (bf16 bit patterns) becomes bfloat16 (bits unchanged)."""
+    import torch
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 

@@ -7,10 +7,8 @@ import numpy as np
 
 def to_device(arr: np.ndarray):
     """float32 array -> float32 tensor; uint16 (bf16 bits) -> bfloat16 tensor; on cuda."""
-    import torch
-    if arr.dtype == np.uint16:
-        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
-    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+    from decoder_only_transformer_bf16_amd import fwd
+    return fwd.to_device(arr)
 
 
 def upload_weights(cfg, host: dict) -> dict:
@@ -36,29 +34,73 @@ def err_over_scale(got, ref) -> float:
     return float(np.max(np.abs(np.asarray(got, np.float64) - ref)) / np.max(np.abs(ref)))
 
 
-def argmax_check(got_ids, ref_logits, got_logits):
-    """Argmax parity under the near-tie reading: where the oracle's top-1 margin exceeds
-    twice the row's max logit error the id must match exactly; otherwise the GPU id must
-    lie within 2 * error of the oracle's max. Returns (n_pinned, n_near_tie, failures)."""
-    ref = np.asarray(ref_logits, np.float64).reshape(-1, ref_logits.shape[-1])
-    got = np.asarray(got_logits, np.float64).reshape(ref.shape)
+# Allowed logit error of the fp32 path: ~100x the fp32 rounding of these dot products
+# (observed 1e-6 and below), far inside the pages' 0.05 fp32 logit gate.
+F32_LOGIT_BAND = 1e-4
+
+
+def oracle_band(ref_logits, ref_bf16_logits=None, slack: float = None):
+    """Per-position allowed logit error, fixed by the oracle alone (never by the GPU's
+    result): for a bf16 computation, `slack` times the largest deviation over the
+    vocabulary of the oracle rounded at the GPU's bf16 points from the exact oracle at
+    that position; for the fp32 path (ref_bf16_logits None), F32_LOGIT_BAND."""
+    r = np.asarray(ref_logits, np.float64)
+    r = r.reshape(-1, r.shape[-1])
+    if ref_bf16_logits is None:
+        return np.full(r.shape[0], F32_LOGIT_BAND)
+    b = np.asarray(ref_bf16_logits, np.float64).reshape(r.shape)
+    return (FLOOR_SLACK if slack is None else slack) * np.max(np.abs(b - r), axis=-1)
+
+
+def argmax_check(got_ids, ref_logits, band):
+    """Argmax parity under the near-tie reading ("N7 · model/forward-parity", Theorem 1:
+    the argmax the oracle pins). band[t] is the allowed logit error at position t (from
+    oracle_band, or a scalar). Where the oracle's top-1 margin exceeds 2 band[t] the GPU
+    id must equal the oracle's; otherwise (a near tie) it must lie within 2 band[t] of
+    the oracle's maximum. Returns (n_pinned, n_near_tie, failures)."""
+    ref = np.asarray(ref_logits, np.float64)
+    ref = ref.reshape(-1, ref.shape[-1])
     ids = np.asarray(got_ids).ravel()
+    band = np.asarray(band, np.float64)
+    band = np.full(ref.shape[0], float(band)) if band.ndim == 0 else band.reshape(-1)
+    if band.shape != (ref.shape[0],):  # one value per position (a logits array is not a band)
+        raise ValueError(f"band of {band.size} values for {ref.shape[0]} positions")
+    assert ids.shape == (ref.shape[0],)
     pinned = near = 0
     fails = []
     for t in range(ref.shape[0]):
-        eps = float(np.max(np.abs(got[t] - ref[t])))
         top2 = np.partition(ref[t], -2)[-2:]
         margin = float(top2[1] - top2[0])
         best = int(np.argmax(ref[t]))
-        if margin > 2 * eps:
+        if margin > 2 * band[t]:
             pinned += 1
             if ids[t] != best:
-                fails.append((t, int(ids[t]), best, margin, eps))
+                fails.append((t, int(ids[t]), best, margin, float(band[t])))
         else:
             near += 1
-            if ref[t, ids[t]] < ref[t, best] - 2 * eps:
-                fails.append((t, int(ids[t]), best, margin, eps))
+            if ref[t, ids[t]] < ref[t, best] - 2 * band[t]:
+                fails.append((t, int(ids[t]), best, margin, float(band[t])))
     return pinned, near, fails
+
+
+def band_for(cfg, host, ids, ref_logits):
+    """oracle_band of a forward over `ids`: for bf16 configurations the oracle is run
+    again, rounded at the bf16 points (host: name -> float32 weights)."""
+    if cfg.dtype != "bf16":
+        return oracle_band(ref_logits)
+    import oracle
+    refb = oracle.forward(cfg, host, ids, want_hidden=False, bf16_points=True)
+    return oracle_band(ref_logits, refb["logits"])
+
+
+def logit_band_check(got_logits, ref_logits, band):
+    """The GPU's logits within the oracle-side allowance: the largest |d logit| over the
+    compared positions must not exceed the largest band over them (a per-position match
+    of the rounding noise is not expected). Returns (max |d|, max band)."""
+    ref = np.asarray(ref_logits, np.float64)
+    ref = ref.reshape(-1, ref.shape[-1])
+    d = float(np.max(np.abs(np.asarray(got_logits, np.float64).reshape(ref.shape) - ref)))
+    return d, float(np.max(band))
 
 
 COS_PRIMARY = 0.9999        # "N7 · model/forward-parity", Theorem 1 proof (f32 forward vs f32 reference)

@@ -7,7 +7,7 @@ import os
 import numpy as np
 import pytest
 
-from tests.gpu_util import argmax_check, distributional_gate
+from tests.gpu_util import F32_LOGIT_BAND, argmax_check, distributional_gate, logit_band_check, oracle_band
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_values.json")))
 FLOOR = GOLD["window_edge_top1_floor"]["value"][0] / GOLD["window_edge_top1_floor"]["value"][1]
@@ -54,8 +54,28 @@ def test_distributional_gate_catches_a_large_logprob_gap_and_nonfinite():
 
 def test_argmax_check_pins_clear_winners_and_tolerates_near_ties():
     ref = np.array([[0.0, 5.0, 1.0], [2.0, 2.0 + 1e-4, 0.0]])
-    got = ref + np.array([[0.0, 0.0, 0.0], [1e-3, -1e-3, 0.0]])
-    pinned, near, fails = argmax_check(np.argmax(got, -1), ref, got)
+    pinned, near, fails = argmax_check(np.array([1, 0]), ref, 1e-3)   # row 1: a near tie, either id
     assert (pinned, near, fails) == (1, 1, [])
-    pinned, near, fails = argmax_check(np.array([2, 0]), ref, got)  # row 0 pinned to 1, not 2
+    pinned, near, fails = argmax_check(np.array([2, 0]), ref, 1e-3)   # row 0 pinned to 1, not 2
     assert fails and fails[0][0] == 0
+    pinned, near, fails = argmax_check(np.array([1, 2]), ref, 1e-3)   # near tie, but id 2 is far below
+    assert fails and fails[0][0] == 1
+    # per-position allowance: a wide band turns row 0 into a near tie too
+    pinned, near, fails = argmax_check(np.array([1, 0]), ref, np.array([3.0, 1e-3]))
+    assert (pinned, near) == (0, 2)
+
+
+def test_argmax_check_band_comes_from_the_oracle_only():
+    ref = np.random.default_rng(2).standard_normal((5, 50))
+    with pytest.raises(ValueError):                                    # a logits array is not a band
+        argmax_check(np.argmax(ref, -1), ref, ref + 0.1)
+
+
+def test_oracle_band_is_slack_times_the_bf16_rounded_deviation():
+    ref = np.zeros((2, 4))
+    rb = np.array([[0.0, 0.2, -0.1, 0.0], [0.05, 0.0, 0.0, -0.3]])
+    np.testing.assert_allclose(oracle_band(ref, rb), [0.25, 0.375])
+    np.testing.assert_allclose(oracle_band(ref, rb, slack=2.0), [0.4, 0.6])
+    np.testing.assert_allclose(oracle_band(ref), [F32_LOGIT_BAND] * 2)
+    d, b = logit_band_check(ref + 0.2, ref, oracle_band(ref, rb))
+    assert (d, b) == (pytest.approx(0.2), pytest.approx(0.375))

@@ -2,8 +2,10 @@
 
 Gates ("N7 · model/forward-parity", Theorem 1): hidden-state cosine >= 0.9999 at
 every slot; per-position argmax exact where the oracle pins it (near ties: the GPU
-id must lie within twice the row's logit error of the oracle's max); final logits
-max|d| <= 0.05 on the fp32 configuration. Determinism: a second run is bitwise
+id must lie within twice the oracle-side logit allowance of the oracle's max, the
+allowance being 1.25x the deviation of the oracle rounded at the bf16 points, or 1e-4
+on the fp32 path); final logits max|d| <= 0.05 on the fp32 configuration and within
+that allowance on bf16 ones. Determinism: a second run is bitwise
 identical ("pegainfer issue #878", Acceptance Criteria: to_bits replay).
 """
 import json
@@ -15,7 +17,7 @@ import pytest
 
 import oracle
 from synth import workloads as wl
-from tests.gpu_util import argmax_check, cosine, upload_weights
+from tests.gpu_util import argmax_check, band_for, cosine, logit_band_check, upload_weights
 
 pytestmark = pytest.mark.gpu
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_values.json")))
@@ -44,6 +46,7 @@ def run_pair(fwd, cfg, ids, max_tokens=None, host=None):
     out = model.prefill(ids, logits=True, hidden=True, argmax=True)
     got = {k: v.cpu().numpy() for k, v in out.items()}
     ref = oracle.forward(cfg, wl.HostWeights(host), ids)
+    ref["band"] = band_for(cfg, wl.HostWeights(host), ids, ref["logits"])  # oracle-side logit allowance
     return model, got, ref
 
 
@@ -55,10 +58,12 @@ def check_parity(cfg, got, ref, logit_gate=None):
     dz = float(np.max(np.abs(got["logits"] - ref["logits"])))
     if logit_gate is not None:
         assert dz <= logit_gate, dz
-    pinned, near, fails = argmax_check(got["argmax"], ref["logits"], got["logits"])
+    pinned, near, fails = argmax_check(got["argmax"], ref["logits"], ref["band"])
     assert not fails, fails[:5]
+    d, b = logit_band_check(got["logits"], ref["logits"], ref["band"])
+    assert d <= b, f"max|dlogit| {d} over the oracle-side allowance {b}"
     assert np.array_equal(got["argmax"], np.argmax(got["logits"], -1)), "argmax must follow the GPU's own logits"
-    _say(f"  {cfg.name}: max|dlogit| {dz:.3e}, argmax pinned {pinned} near-tie {near}")
+    _say(f"  {cfg.name}: max|dlogit| {dz:.3e} (allowance {b:.3e}), argmax pinned {pinned} near-tie {near}")
     return pinned, near
 
 
