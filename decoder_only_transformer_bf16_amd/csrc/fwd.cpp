@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -154,6 +155,7 @@ struct Geometry {
     w += r(rows(T) * Hq * D * esize);                   // attention output
     w += r(rows(T) * F * esize);                        // SwiGLU output
     if (sandwich) w += r(T * H * 4);                    // sublayer output before its norm
+    if (sandwich && tiled) w += r(dense_split_floats() * 4);  // split-K partials of its products
     w += r(T * 4) + r(T * 4) + 256;                     // ids, argmax, flag
     w += r(logit_ws_bytes());                           // logits when the caller wants none / argmax keys
     w += r(kArgPartPairs * 8);                          // sliced argmax partials
@@ -176,6 +178,18 @@ struct Geometry {
     return f;
   }
   int64_t skinny_counters() const { return fwdk::skinny_groups((int)std::max({qkv_rows, H, 2 * F, V})); }
+  // Split-K partials of the sandwich products (O and down, whose outputs are stored
+  // before their norm): the largest need over every row count up to T. It depends on
+  // the rows only through their 128-row tile count, so the last row count of each
+  // tile count bounds it.
+  int64_t dense_split_floats() const {
+    int64_t f = 0;
+    for (int64_t c = 1; c <= (T + 127) / 128; ++c) {
+      const int M = (int)std::min(128 * c, T);
+      f = std::max({f, fwdk::dense_split_floats(M, (int)H, (int)(Hq * D)), fwdk::dense_split_floats(M, (int)H, (int)F)});
+    }
+    return f;
+  }
 };
 
 Geometry geometry(const fwd_config* c) {
@@ -242,6 +256,7 @@ struct fwd_model {
   float2* rope_tab[4] = {};  // [2 * local + long factors]: RoPE (cos, sin) tables of max_tokens rows
   std::vector<float> rope_short, rope_long;  // longrope factors (the config's arrays are borrowed)
   fwdk::SplitK sk{};  // workspace of the few-row products (bf16)
+  fwdk::DenseSplit ds{};  // split-K partials of the sandwich products (bf16)
   // mixture-of-experts workspace (models with MoE layers)
   float* moe_logits = nullptr;  // [T, E]
   int32_t* moe_idx = nullptr;   // [T, k]
@@ -615,6 +630,10 @@ int fwd_create(const fwd_config* cfg, const fwd_weights* w, void* hip_stream, fw
     if (int rc = m->alloc(&m->a, g.rows(T) * g.F * g.esize)) return rc;
     if (sandwich)
       if (int rc = m->alloc((void**)&m->u, T * g.H * 4)) return rc;
+    if (sandwich && g.tiled) {
+      m->ds.part_floats = g.dense_split_floats();
+      if (int rc = m->alloc((void**)&m->ds.part, m->ds.part_floats * 4)) return rc;
+    }
     if (int rc = m->alloc((void**)&m->ids, T * 4)) return rc;
     if (int rc = m->alloc((void**)&m->amax, T * 4)) return rc;
     if (int rc = m->alloc((void**)&m->flag, 256)) return rc;
@@ -767,7 +786,7 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
       TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_residual(dt, m->o, w.wo, xin, xmid, M, H, Hq * D, tl, s, sk));
       TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, tl, s));
     } else {
-      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_store(dt, m->o, w.wo, m->u, H, M, H, Hq * D, 0.f, tl, s, sk));
+      TIMED(m, FWD_KERNEL_O_PROJ, fwdk::gemm_store(dt, m->o, w.wo, m->u, H, M, H, Hq * D, 0.f, tl, s, sk, nullptr, &m->ds));
       TIMED(m, FWD_KERNEL_NORM, fwdk::add_norm(dt, xin, m->u, w.post_attn, xmid, w.ffn_norm, m->n, nullptr, M, H, eps, tl, s));
     }
 
@@ -812,7 +831,7 @@ int forward(fwd_model* m, fwd_session* sess, const int32_t* ids_host, int32_t B,
       TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_residual(dt, m->a, w.wdown, xmid, xout, M, H, F, tl, s, sk));
       TIMED(m, FWD_KERNEL_NORM, fwdk::rmsnorm(dt, xout, next_norm, m->n, final32, M, H, eps, tl, s));
     } else {
-      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_store(dt, m->a, w.wdown, m->u, H, M, H, F, 0.f, tl, s, sk));
+      TIMED(m, FWD_KERNEL_DOWN_PROJ, fwdk::gemm_store(dt, m->a, w.wdown, m->u, H, M, H, F, 0.f, tl, s, sk, nullptr, &m->ds));
       TIMED(m, FWD_KERNEL_NORM, fwdk::add_norm(dt, xmid, m->u, w.post_ffn, xout, next_norm, m->n, final32, M, H, eps, tl, s));
     }
     cur = xout;
@@ -950,15 +969,72 @@ int32_t fwd_session_length(const fwd_session* se) { return se ? se->len : -1; }
 
 void fwd_session_destroy(fwd_session* se) { delete se; }
 
-int fwd_gemm(const void* X, const void* W, float* Y, int32_t P, int32_t in, int32_t out, int32_t dtype,
-             void* hip_stream) {
+}  // extern "C"
+
+namespace {
+// fwd_gemm's split partials come from a memory pool of the library's own on each device,
+// allocated and freed in stream order (so calls on concurrent streams never share them),
+// with a release threshold that keeps the freed memory in the pool between calls
+// instead of returning it to the driver at every synchronisation.
+hipError_t split_pool(hipMemPool_t* out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static hipMemPool_t pools[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!pools[dev]) {
+    hipMemPoolProps props{};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t p = nullptr;
+    if ((e = hipMemPoolCreate(&p, &props)) != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;
+    if ((e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) return e;
+    pools[dev] = p;
+  }
+  *out = pools[dev];
+  return hipSuccess;
+}
+
+// Argument checks of fwd_gemm: FWD_OK to go on, `done` set when there is nothing to
+// compute.
+int gemm_args(const void* X, const void* W, const float* Y, int32_t P, int32_t in, int32_t out, int32_t dtype,
+              bool* done) {
+  *done = false;
   if (dtype != FWD_DTYPE_BF16 && dtype != FWD_DTYPE_F32) return fail(FWD_E_ARG, "dtype");
   if (P < 0 || in <= 0 || out < 0) return fail(FWD_E_ARG, "sizes must be P >= 0, in > 0, out >= 0");
   if (in % (dtype == FWD_DTYPE_BF16 ? 8 : 4)) return fail(FWD_E_ARG, "in must be a multiple of 8 (bf16) / 4 (f32)");
-  if ((int64_t)P * out == 0) return FWD_OK;
+  if ((int64_t)P * out == 0) {
+    *done = true;
+    return FWD_OK;
+  }
   if (!X || !W || !Y) return fail(FWD_E_ARG, "NULL buffer");
   if (!device_is_gfx950()) return fail(FWD_E_UNAVAILABLE, "no gfx950 device is available");
-  HIP_TRY(fwdk::gemm_store(DType(dtype), X, W, Y, out, P, out, in, 0.f, false, (hipStream_t)hip_stream));
+  return FWD_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int fwd_gemm(const void* X, const void* W, float* Y, int32_t P, int32_t in, int32_t out, int32_t dtype,
+             void* hip_stream) {
+  bool done = false;
+  if (int rc = gemm_args(X, W, Y, P, in, out, dtype, &done)) return rc;
+  if (done) return FWD_OK;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  fwdk::DenseSplit ds{nullptr, dtype == FWD_DTYPE_BF16 ? fwdk::dense_split_floats(P, out, in) : 0};
+  if (ds.part_floats > 0) {  // split partials, stream-ordered: concurrent calls on other streams do not share them
+    hipMemPool_t pool = nullptr;
+    HIP_TRY(split_pool(&pool));
+    HIP_TRY(hipMallocFromPoolAsync((void**)&ds.part, (size_t)ds.part_floats * 4, pool, s));
+  }
+  const hipError_t e = fwdk::gemm_store(DType(dtype), X, W, Y, out, P, out, in, 0.f, false, s, nullptr, nullptr, &ds);
+  if (ds.part) HIP_TRY(hipFreeAsync(ds.part, s));
+  HIP_TRY(e);
   return FWD_OK;
 }
 

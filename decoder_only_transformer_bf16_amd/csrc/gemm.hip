@@ -4,10 +4,11 @@
 // the per-position argmax, residual add, SwiGLU, and RoPE on the query/key heads
 // ("N7 · model/forward-parity", intro and Theorem 1).
 //
-// bf16 path: CDNA4 MFMA v_mfma_f32_32x32x16_bf16 on K-tiled operands staged through
-// LDS by buffer->LDS loads in 32-wide K slices: a two-group ping-pong kernel with
-// 256 x 256 tiles and four LDS stages for large problems, a 128 x 128 software-
-// pipelined kernel for small ones, and a split-K 16x16x32 kernel for few rows.
+// bf16 path: CDNA4 MFMA v_mfma_f32_32x32x16_bf16 on operands staged through LDS by
+// buffer->LDS loads: a two-group ping-pong kernel with 256 x 256 tiles for large
+// problems (K-tiled operands: 32-wide K slices in four LDS stages; row-major ones:
+// 64-wide slices in two), a 128 x 128 software-pipelined kernel for small ones (with an
+// optional split of K over workgroups), and a split-K 16x16x32 kernel for few rows.
 // f32 path: an LDS-tiled VALU kernel (the fp32 configuration is tiny).
 #include <algorithm>
 #include <type_traits>
@@ -655,14 +656,13 @@ __device__ __forceinline__ bool group_tile(const GroupArgs& g, int block, int nT
   return true;
 }
 
-// GROUPED: one launch over the expert segments of a mixture-of-experts layer; the
-// workgroup's m-tile selects the expert (the last one whose first tile is at or
-// before it, so empty experts are skipped), whose X rows start at seg_start and whose
-// W is the e-th of a stack; output rows are the segment's rows.
-template <class C, class Epi, bool TILED, bool GROUPED = false>
+// SPLIT: workgroup b takes tile b % tiles and K slices [kps (b / tiles), + kps) of it;
+// the epilogue (a plain store) writes that split's fp32 partial tile to
+// epi.Y + (b / tiles) M ldy, and a second launch adds the splits in order.
+template <class C, class Epi, bool TILED, bool SPLIT = false>
 __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* __restrict__ X,
                                                                   const bf16_t* __restrict__ W, int M, int N, int K,
-                                                                  Epi epi, GroupArgs grp = GroupArgs{}) {
+                                                                  Epi epi, int kps = 0) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::STAGES, NW = C::NW;
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN, KS = C::KS;
   constexpr int SLICE = (BM + BN) * BK;  // elements per stage
@@ -671,15 +671,17 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int nTN = (N + BN - 1) / BN;
-  int tm, tn, row0 = 0;
-  if constexpr (GROUPED) {
-    if (!group_tile(grp, blockIdx.x, nTN, tm, tn, row0, M)) return;
-    X += (int64_t)row0 * K;  // (segments start on 16-row boundaries: whole K-tiled row blocks)
-    W += (int64_t)group_expert(grp, blockIdx.x / nTN) * grp.w_stride;
-  } else {
-    tile_coords(blockIdx.x, (M + BM - 1) / BM, nTN, tm, tn);
+  const int nTM = (M + BM - 1) / BM, nTN = (N + BN - 1) / BN;
+  int pid = blockIdx.x, kt0 = 0, nk = (K + BK - 1) / BK;
+  if constexpr (SPLIT) {
+    const int sp = pid / (nTM * nTN);
+    pid -= sp * nTM * nTN;
+    kt0 = sp * kps;
+    nk = min(nk - kt0, kps);
+    epi.Y += (int64_t)sp * M * epi.ldy;
   }
+  int tm, tn;
+  tile_coords(pid, nTM, nTN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   // (K-tiled operands are read in whole 16-row tiles: rows are padded to 16)
   const int mr = TILED ? (M + 15) / 16 * 16 : M, nr = TILED ? (N + 15) / 16 * 16 : N;
@@ -691,7 +693,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx16_t{};
-  if constexpr (kInitAcc<Epi>::value) init_acc<TM, TN>(epi, acc, row0 + m0 + wm * WTM, n0 + wn * WTN, row0 + M, N, lane);
+  if constexpr (kInitAcc<Epi>::value) init_acc<TM, TN>(epi, acc, m0 + wm * WTM, n0 + wn * WTN, M, N, lane);
 
   // Software pipeline over K slices; slice t lives in LDS buffer t % ST.
   // One barrier per slice, early in its last sub-step (whose fragments were read
@@ -714,7 +716,6 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
   static_assert(ST > 2 || LPRE == LT, "two stages: every refill load precedes the barrier");
   constexpr int WAIT_STEADY = ST == 2 ? 0 : (ST - 3) * LT + LPRE;  // loads allowed in flight at a barrier
   static_assert(WAIT_STEADY < 64, "vmcnt range");
-  const int nk = (K + BK - 1) / BK;
   auto issue_load = [&](int p, bf16_t* buf, int k0) {  // load p of this wave's share of one slice
     if (p < LA) load_block<BK, TILED>(ra, buf, K, k0, wave + p * NW, lane);
     else load_block<BK, TILED>(rb, buf + BM * BK, K, k0, wave + (p - LA) * NW, lane);
@@ -723,7 +724,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
   for (int q = 0; q < ST - 1; ++q)
     if (q < nk)
 #pragma unroll
-      for (int p = 0; p < LT; ++p) issue_load(p, lds + q * SLICE, q * BK);
+      for (int p = 0; p < LT; ++p) issue_load(p, lds + q * SLICE, (kt0 + q) * BK);
   const int lr = lane & 31, lk = lane >> 5;
   const int arow = wm * WTM + lr, brow = BM + wn * WTN + lr;  // tile rows this lane reads (+32 i / +32 j)
   bf16x8_t fa[2][TM], fb[2][TN];
@@ -768,14 +769,14 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_bf16_kernel(const bf16_t* 
         if (refill) {
 #pragma unroll
           for (int p = 0; p < LT; ++p)
-            if ((p * LS) / LT == g) issue_load(p, fill, (kt + ST - 1) * BK);
+            if ((p * LS) / LT == g) issue_load(p, fill, (kt0 + kt + ST - 1) * BK);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
-  write_tile<TM, TN>(epi, acc, row0 + m0 + wm * WTM, n0 + wn * WTN, row0 + M, N, lane);
+  write_tile<TM, TN>(epi, acc, m0 + wm * WTM, n0 + wn * WTN, M, N, lane);
 }
 
 template <class C, class Epi, bool TILED = false>
@@ -988,6 +989,225 @@ template <class C, class Epi, bool TILED = false>
 hipError_t launch_pp(const void* X, const void* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   const int grid = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
   hipLaunchKernelGGL((gemm_pp_kernel<C, Epi, TILED>), dim3(grid), dim3(C::NT), 0, s, (const bf16_t*)X,
+                     (const bf16_t*)W, M, N, K, epi);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ ping-pong, 64-wide slices
+// The same two-group alternation for row-major operands (the standalone product), with
+// 64-wide K slices in two LDS stages of 64 KiB: each row then contributes one full
+// 128-byte cache line per slice (eight rows per 1 KiB load), where a 32-wide slice
+// reads half lines and costs the texture address unit twice the cycles per load. Group
+// 0 issues every buffer->LDS load of slice s + 1 at the start of its memory(s) phase,
+// into the buffer both groups finished reading by the barrier ending step 2s - 1, and
+// waits for them before the barrier ending step 2s + 1, which group 0's memory(s + 1)
+// needs; group 1 only reads fragments. Interleaved in one process on operands uniform in
+// [-1, 1): 7.5% faster than the 32-wide kernel on [4096, 4096, 14336], 1% on
+// [8192, 4096, 128256], bitwise equal (every accumulator takes the same MFMAs in the
+// same K order). On K-tiled operands inside the forward (weights N(0, 0.02)) it was
+// 5.8% slower per prefill (223.6 vs 211.2 ms interleaved, the down product 53.5 vs
+// 47.2 ms): two steps of prefetch do not cover the memory latency there, where the
+// 32-wide kernel keeps three slices in flight. K-tiled operands stay supported (two
+// 32-wide sub-slices per slice, each laid out as in the 32-wide kernels).
+template <int BM_, int BN_, int WM_, int WN_>
+struct PP64Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = 64, STAGES = 2, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = NW * 64;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32, KS = BK / 16;
+  static constexpr int BLK_A = BM * BK / 512, BLK = (BM + BN) * BK / 512;  // 1 KiB blocks per slice
+  static constexpr int LOADS = BLK / (NW / 2);                              // per group-0 wavefront
+  static_assert(NW == 8, "two groups of four wavefronts");
+  static_assert(LOADS * (NW / 2) == BLK && BM % 16 == 0 && BN % 16 == 0, "load split");
+  static_assert(STAGES * (BM + BN) * BK * 2 <= 160 * 1024, "LDS budget");
+  static_assert(TN % 2 == 0, "pair epilogues need an even number of 32-column sub-tiles");
+  static_assert(LOADS < 64, "vmcnt range");
+};
+
+// LDS element offset of 8-element chunk c (0..7) of row r in a 64-wide slice region of R rows.
+template <int R, bool TILED>
+__device__ __forceinline__ int lds_off64(int r, int c) {
+  if constexpr (TILED) return (c >> 2) * (R * 32) + r * 32 + (swz<32>(r, c & 3) << 3);
+  else return lds_off<64>(r, c);
+}
+
+// 1 KiB block `blk` of a 64-wide slice (k0) of an R-row operand tile into its region.
+// K-tiled: block (sub, rb) = (blk / (R / 16), blk % (R / 16)) is the 16 x 32 tile
+// (rb, k0 / 32 + sub). Row-major: rows 8 blk .. 8 blk + 7, 128 bytes each.
+template <int R, bool TILED>
+__device__ __forceinline__ void load_block64(__amdgpu_buffer_rsrc_t rs, bf16_t* region, int K, int k0, int blk,
+                                             int lane) {
+  if constexpr (TILED) {
+    const int sub = blk / (R / 16), rb = blk - sub * (R / 16);
+    const int row = lane >> 2, ch = swz<32>(row, lane & 3);
+    // (past the last K tile, when K is an odd number of 32-wide tiles: zeros)
+    const uint32_t off = k0 / 32 + sub < K / 32
+                             ? (uint32_t)((rb * (K / 32) + k0 / 32 + sub) * 512 + row * 32 + ch * 8) * 2u
+                             : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(region + blk * 512), 16, off, 0, 0, 0);
+  } else {
+    load_block<64, false>(rs, region, K, k0, blk, lane);
+  }
+}
+
+template <class C, class Epi, bool TILED, bool GROUPED = false>
+__global__ __launch_bounds__(C::NT) void gemm_pp64_kernel(const bf16_t* __restrict__ X,
+                                                          const bf16_t* __restrict__ W, int M, int N, int K, Epi epi,
+                                                          GroupArgs grp = GroupArgs{}) {
+  constexpr int BM = C::BM, BN = C::BN, BK = 64;
+  constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN, KS = C::KS;
+  constexpr int SLICE = (BM + BN) * BK, FR = TM + TN, LT = C::LOADS;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[2 * SLICE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int nTN = (N + BN - 1) / BN;
+  int tm, tn, row0 = 0;
+  if constexpr (GROUPED) {
+    if (!group_tile(grp, blockIdx.x, nTN, tm, tn, row0, M)) return;
+    X += (int64_t)row0 * K;
+    W += (int64_t)group_expert(grp, blockIdx.x / nTN) * grp.w_stride;
+  } else {
+    tile_coords(blockIdx.x, (M + BM - 1) / BM, nTN, tm, tn);
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int mr = TILED ? (M + 15) / 16 * 16 : M, nr = TILED ? (N + 15) / 16 * 16 : N;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(X + (int64_t)m0 * K, (int64_t)min(BM, mr - m0) * K * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + (int64_t)n0 * K, (int64_t)min(BN, nr - n0) * K * 2);
+  const int nk = (K + BK - 1) / BK;
+  // group 0 only: wave w (0..3) takes blocks w, w + 4, ... of the slice (A blocks first)
+  auto issue_slice = [&](bf16_t* buf, int k0) {
+#pragma unroll
+    for (int p = 0; p < LT; ++p) {
+      const int blk = wave + p * (C::NW / 2);
+      if (blk < C::BLK_A) load_block64<BM, TILED>(ra, buf, K, k0, blk, lane);
+      else load_block64<BN, TILED>(rb, buf + BM * BK, K, k0, blk - C::BLK_A, lane);
+    }
+  };
+  const int lr = lane & 31, lk = lane >> 5;
+  const int arow = wm * WTM + lr, brow = wn * WTN + lr;
+  bf16x8_t fa[KS][TM], fb[KS][TN];
+  auto read_slice = [&](const bf16_t* base) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int n = 0; n < FR; ++n) {
+        const int f = need_frag<TM>(n);
+        if (f < TM)
+          fa[kk][f] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(base + lds_off64<BM, TILED>(arow + f * 32, kk * 2 + lk)));
+        else
+          fb[kk][f - TM] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
+              base + BM * BK + lds_off64<BN, TILED>(brow + (f - TM) * 32, kk * 2 + lk)));
+      }
+    }
+  };
+
+  floatx16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx16_t{};
+  if constexpr (kInitAcc<Epi>::value) init_acc<TM, TN>(epi, acc, row0 + m0 + wm * WTM, n0 + wn * WTN, row0 + M, N, lane);
+
+  if (group == 0) {
+    issue_slice(lds, 0);
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+  if (group == 1) lds_barrier();  // group 1 runs one step behind
+
+  for (int s = 0; s < nk; ++s) {
+    // memory(s): fragments of slice s; group 0 also starts slice s + 1
+    read_slice(lds + (s & 1) * SLICE);
+    if (group == 0 && s + 1 < nk) issue_slice(lds + ((s + 1) & 1) * SLICE, (s + 1) * BK);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)  // compute(s)
+#pragma unroll
+      for (int x = 0; x < TM * TN; ++x) {
+        const int i = x % TM, j = x / TM;
+        acc[i][j] = mfma_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    if (group == 0) wait_vmcnt<0>();  // this barrier ends an odd step: slice s + 1 has landed
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (group == 0) lds_barrier();  // matches group 1's extra barrier
+
+  write_tile<TM, TN>(epi, acc, row0 + m0 + wm * WTM, n0 + wn * WTN, row0 + M, N, lane);
+}
+
+using Cfg64 = PP64Cfg<256, 256, 4, 2>;
+
+// ------------------------------------------------------------------ split K
+// Products with few output tiles and a long K (the Gemma-style sandwich down product,
+// small standalone products) leave most CUs idle on the tiled kernels. There the K
+// slices are cut into nsplit ranges: workgroup b computes tile b % tiles over range b / tiles and
+// stores its fp32 partial tile into part[split][M][N]; splitk_sum_kernel then adds the
+// partials of every output in split order and applies the softcap, so the result does
+// not depend on timing and repeats bit for bit.
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ part, int nsplit, int M, int N,
+                                                         float* __restrict__ Y, int64_t ldy, float cap) {
+  const EpiStore<32> st{nullptr, 0, cap};
+  const int64_t MN = (int64_t)M * N;
+  if ((N & 3) == 0 && (ldy & 3) == 0) {  // four outputs of a row per thread, 16-byte accesses
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < MN / 4; q += (int64_t)gridDim.x * blockDim.x) {
+      const int64_t e = 4 * q, r = e / N, c = e - r * N;
+      float4 acc = *reinterpret_cast<const float4*>(part + e);
+      for (int sp = 1; sp < nsplit; ++sp) {
+        const float4 v = *reinterpret_cast<const float4*>(part + sp * MN + e);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+      *reinterpret_cast<float4*>(Y + r * ldy + c) = float4{st.apply(acc.x), st.apply(acc.y), st.apply(acc.z),
+                                                           st.apply(acc.w)};
+    }
+    return;
+  }
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < MN; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / N, c = e - r * N;
+    float acc = part[e];
+    for (int sp = 1; sp < nsplit; ++sp) acc += part[sp * MN + e];
+    Y[r * ldy + c] = st.apply(acc);
+  }
+}
+
+// nsplit ranges of kps 32-wide K slices each (nsplit = 1: no split).
+struct DenseSplitPlan {
+  int nsplit, kps;
+};
+DenseSplitPlan split_ranges(int K, int ns) {
+  const int nk = (K + 31) / 32;
+  ns = std::max(1, std::min(ns, nk));
+  const int kps = (nk + ns - 1) / ns;
+  return {(nk + kps - 1) / kps, kps};
+}
+
+template <class C, bool TILED>
+hipError_t launch_split(const void* X, const void* W, int M, int N, int K, float* Y, int64_t ldy, float cap,
+                        float* part, const DenseSplitPlan& p, hipStream_t s) {
+  static_assert(C::BK == 32, "split ranges count 32-wide slices");
+  const int tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<C, EpiStore<32>, TILED, true>), dim3(tiles * p.nsplit), dim3(C::NT), 0, s,
+                     (const bf16_t*)X, (const bf16_t*)W, M, N, K, EpiStore<32>{part, N, 0.f}, p.kps);
+  const int64_t work = ((N & 3) == 0 && (ldy & 3) == 0) ? (int64_t)M * N / 4 : (int64_t)M * N;
+  const int blocks = (int)std::min<int64_t>((work + 255) / 256, 4096);
+  hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, (const float*)part, p.nsplit, M, N, Y, ldy,
+                     cap);
+  return hipGetLastError();
+}
+
+template <class C, class Epi, bool TILED = false>
+hipError_t launch_pp64(const void* X, const void* W, int M, int N, int K, const Epi& epi, hipStream_t s) {
+  const int grid = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL((gemm_pp64_kernel<C, Epi, TILED>), dim3(grid), dim3(C::NT), 0, s, (const bf16_t*)X,
                      (const bf16_t*)W, M, N, K, epi);
   return hipGetLastError();
 }
@@ -1329,7 +1549,7 @@ hipError_t launch_dense(const void* X, const void* W, int M, int N, int K, const
     if (small >= 256) return launch_cfg<CfgSmall, Epi, true>(X, W, M, N, K, epi, s);
     return launch_cfg<CfgNarrow, Epi, true>(X, W, M, N, K, epi, s);
   }
-  if (big >= 256) return launch_pp<CfgBig, Epi, false>(X, W, M, N, K, epi, s);
+  if (big >= 256) return launch_pp64<Cfg64, Epi, false>(X, W, M, N, K, epi, s);
   if (small >= 256) return launch_cfg<CfgSmall, Epi, false>(X, W, M, N, K, epi, s);
   return launch_cfg<CfgNarrow, Epi, false>(X, W, M, N, K, epi, s);
 }
@@ -1407,8 +1627,44 @@ int64_t skinny_part_floats(int M, int N, int K) {
 }
 int64_t skinny_groups(int N) { return N > 0 ? (N + 63) / 64 : 0; }
 
+namespace {
+// Which products to split, from interleaved timings: a long K (>= 8192) with fewer than
+// 256 tiles of 128 x 128, on 128 x 128 tiles, the split count aiming at two workgroups
+// per CU with at least 128 slices per range (a 1024 x 3840 product over K 15360, K-tiled:
+// 2 ranges 133 us, 3 ranges 145 us, 4 ranges 149 us, against 165-174 us unsplit on
+// 64 x 128 tiles). A split did not pay below that: the same product over K 4096 took
+// 46 us unsplit and 50-80 us in 2-8 ranges; 256 x 1536 over K 1536 gained 1.5 us from 3
+// ranges on 64 x 128 tiles, less than the standalone product's stream-ordered
+// allocation of the partials costs (about 15 us per call).
+constexpr int kCUs = 256;
+DenseSplitPlan dense_split_plan(int M, int N, int K) {
+  const DenseSplitPlan none{1, 0};
+  if (M <= 0 || N <= 0 || K <= 0) return none;
+  const int64_t small = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  const int nk = (K + 31) / 32;
+  if (small >= 256 || nk < 256) return none;
+  const int ns = (int)std::min<int64_t>(std::max<int64_t>((2 * kCUs + small / 2) / small, 2), nk / 128);
+  return split_ranges(K, ns);
+}
+}  // namespace
+
+int64_t dense_split_floats(int M, int N, int K) {
+  const DenseSplitPlan p = dense_split_plan(M, N, K);
+  return p.nsplit > 1 ? (int64_t)p.nsplit * M * N : 0;
+}
+
 hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K,
-                      float softcap, bool tiled, hipStream_t s, const SplitK* sk, const RowNormX* nx) {
+                      float softcap, bool tiled, hipStream_t s, const SplitK* sk, const RowNormX* nx,
+                      const DenseSplit* ds) {
+  if (dt == DType::BF16 && ds && !nx && !(tiled && sk && M <= kSkinnyRows) && M > 0 && N > 0) {
+    const DenseSplitPlan p = dense_split_plan(M, N, K);
+    if (p.nsplit > 1) {
+      if (tiled && K % 32) return hipErrorInvalidValue;
+      if ((int64_t)p.nsplit * M * N > ds->part_floats || !ds->part) return hipErrorInvalidValue;
+      return tiled ? launch_split<CfgSmall, true>(X, W, M, N, K, Y, ldy, softcap, ds->part, p, s)
+                   : launch_split<CfgSmall, false>(X, W, M, N, K, Y, ldy, softcap, ds->part, p, s);
+    }
+  }
   if (dt == DType::BF16) return launch_bf16(X, W, M, N, K, EpiStore<32>{Y, ldy, softcap}, tiled, s, sk, nx);
   if (tiled || nx) return hipErrorInvalidValue;
   return launch_f32(X, W, M, N, K, EpiStore<1>{Y, ldy, softcap}, s);

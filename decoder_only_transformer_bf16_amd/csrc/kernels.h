@@ -41,9 +41,17 @@ struct RowNormX {
   int groups;        // ceil(K / 64)
   float eps;
 };
+// Products with few output tiles and a long K are cut into K ranges whose fp32 partial
+// tiles a second launch adds in range order (deterministic) when `ds` holds room for
+// dense_split_floats(M, N, K) partials (bf16 only; 0 floats: the product is not split).
+struct DenseSplit {
+  float* part;
+  int64_t part_floats;
+};
+int64_t dense_split_floats(int M, int N, int K);
 hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K,
                       float softcap, bool tiled, hipStream_t s, const SplitK* sk = nullptr,
-                      const RowNormX* nx = nullptr);
+                      const RowNormX* nx = nullptr, const DenseSplit* ds = nullptr);
 // Tied LM head with the per-position argmax fused (bf16 K-tiled operands, K a multiple
 // of 32, M > kSkinnyRows): logits as gemm_store when Y is set (Y may be null: argmax
 // only), plus per row the best (value, lowest column) key of each column chunk in

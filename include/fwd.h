@@ -258,6 +258,11 @@ int fwd_prefill(fwd_model* m, const int32_t* ids_host, int32_t B, int32_t S, con
  * Theorem 1: Weight.MatMul). X device [P, in], W device [out, in], both of
  * `dtype` (FWD_DTYPE_BF16 or FWD_DTYPE_F32); Y device fp32 [P, out]. fp32
  * accumulation. `in` must be a multiple of 8 (bf16) or 4 (f32).
+ * bf16 products with few output tiles and a long `in` are cut into ranges of `in`
+ * whose fp32 partial products are added in range order (deterministic: a call
+ * repeats bit for bit); their partials live in device memory the call allocates
+ * and frees in stream order on hip_stream, from a memory pool of its own that keeps
+ * the memory for later calls.
  * Errors: FWD_E_ARG, FWD_E_UNAVAILABLE, FWD_E_HIP.
  */
 int fwd_gemm(const void* X, const void* W, float* Y, int32_t P, int32_t in, int32_t out,
