@@ -1000,8 +1000,8 @@ hipError_t split_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
-// Argument checks of fwd_gemm: FWD_OK to go on, `done` set when there is nothing to
-// compute.
+// Argument checks shared by fwd_gemm and fwd_gemm_noalloc: FWD_OK to go on, `done`
+// set when there is nothing to compute.
 int gemm_args(const void* X, const void* W, const float* Y, int32_t P, int32_t in, int32_t out, int32_t dtype,
               bool* done) {
   *done = false;
@@ -1035,6 +1035,26 @@ int fwd_gemm(const void* X, const void* W, float* Y, int32_t P, int32_t in, int3
   const hipError_t e = fwdk::gemm_store(DType(dtype), X, W, Y, out, P, out, in, 0.f, false, s, nullptr, nullptr, &ds);
   if (ds.part) HIP_TRY(hipFreeAsync(ds.part, s));
   HIP_TRY(e);
+  return FWD_OK;
+}
+
+int fwd_gemm_noalloc(const void* X, const void* W, float* Y, int32_t P, int32_t in, int32_t out, int32_t dtype,
+                     void* hip_stream) {
+  bool done = false;
+  if (int rc = gemm_args(X, W, Y, P, in, out, dtype, &done)) return rc;
+  if (done) return FWD_OK;
+  const int64_t need = dtype == FWD_DTYPE_BF16 ? fwdk::dense_split_floats(P, out, in) : 0;
+  if (need > fwdk::kStaticSplitFloats)
+    return fail(FWD_E_TOO_LARGE, "this product's split partials need " + std::to_string(need * 4) +
+                                     " bytes; the static scratch holds " +
+                                     std::to_string(fwdk::kStaticSplitFloats * 4));
+  fwdk::DenseSplit ds{nullptr, 0};
+  if (need > 0) {
+    HIP_TRY(fwdk::static_split_scratch(&ds.part));
+    ds.part_floats = fwdk::kStaticSplitFloats;
+  }
+  HIP_TRY(fwdk::gemm_store(DType(dtype), X, W, Y, out, P, out, in, 0.f, false, (hipStream_t)hip_stream, nullptr,
+                           nullptr, &ds));
   return FWD_OK;
 }
 

@@ -11,6 +11,7 @@
 // optional split of K over workgroups), and a split-K 16x16x32 kernel for few rows.
 // f32 path: an LDS-tiled VALU kernel (the fp32 configuration is tiny).
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1647,6 +1648,29 @@ DenseSplitPlan dense_split_plan(int M, int N, int K) {
   return split_ranges(K, ns);
 }
 }  // namespace
+
+// The static split-K scratch. In host code `scratch` names a host-side stand-in, not
+// device memory: kernels get the address hipGetSymbolAddress returns for each device.
+static __device__ __align__(256) float scratch[kStaticSplitFloats];
+
+hipError_t static_split_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 int64_t dense_split_floats(int M, int N, int K) {
   const DenseSplitPlan p = dense_split_plan(M, N, K);

@@ -49,6 +49,12 @@ struct DenseSplit {
   int64_t part_floats;
 };
 int64_t dense_split_floats(int M, int N, int K);
+// For callers that cannot allocate: a static device array of kStaticSplitFloats floats
+// that serves as the split-K partial buffer. static_split_scratch gives its address on
+// the current device (looked up once per device). Calls that use it concurrently on one
+// device race.
+constexpr int64_t kStaticSplitFloats = (int64_t)4 << 20;  // 16 MiB
+hipError_t static_split_scratch(float** ptr);
 hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t ldy, int M, int N, int K,
                       float softcap, bool tiled, hipStream_t s, const SplitK* sk = nullptr,
                       const RowNormX* nx = nullptr, const DenseSplit* ds = nullptr);

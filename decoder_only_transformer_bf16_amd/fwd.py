@@ -33,7 +33,8 @@ FFN_ACT = {"silu": 0, "gelu_tanh": 1}
 ROPE_SCALING = {"none": 0, "llama3": 1, "longrope": 2}
 FFN_KIND = {"dense": 0, "moe": 1}
 
-EXPORTS = ("fwd_available", "fwd_create", "fwd_output_sizes", "fwd_prefill", "fwd_gemm", "fwd_attention",
+EXPORTS = ("fwd_available", "fwd_create", "fwd_output_sizes", "fwd_prefill", "fwd_gemm", "fwd_gemm_noalloc",
+           "fwd_attention",
            "fwd_rmsnorm", "fwd_set_timing", "fwd_get_timing", "fwd_destroy", "fwd_last_error",
            "fwd_session_create", "fwd_session_prefill", "fwd_session_decode", "fwd_session_length",
            "fwd_session_destroy", "fwd_moe_route")
@@ -101,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.fwd_prefill.restype = c_i32
         L.fwd_gemm.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp]
         L.fwd_gemm.restype = c_i32
+        L.fwd_gemm_noalloc.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp]
+        L.fwd_gemm_noalloc.restype = c_i32
         L.fwd_attention.argtypes = [c_vp, c_vp, c_vp, c_vp] + [c_i32] * 7 + [c_vp]
         L.fwd_attention.restype = c_i32
         L.fwd_rmsnorm.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_f32, c_i32, c_vp]
@@ -328,15 +331,17 @@ class Session:
         return res
 
 
-def gemm(X, W, Y=None, stream=None):
-    """Y = X·Wᵀ (fwd_gemm). X [P, in], W [out, in] torch tensors (bf16 or f32) on the GPU."""
+def gemm(X, W, Y=None, stream=None, noalloc: bool = False):
+    """Y = X·Wᵀ (fwd_gemm; fwd_gemm_noalloc with noalloc=True, which needs Y given to
+    allocate nothing). X [P, in], W [out, in] torch tensors (bf16 or f32) on the GPU."""
     import torch
     P, K = X.shape
     N = W.shape[0]
     dt = "bf16" if X.dtype == torch.bfloat16 else "f32"
     if Y is None:
         Y = torch.empty((P, N), dtype=torch.float32, device=X.device)
-    _check(lib().fwd_gemm(X.data_ptr(), W.data_ptr(), Y.data_ptr(), P, K, N, DTYPE[dt], _stream(stream)))
+    call = lib().fwd_gemm_noalloc if noalloc else lib().fwd_gemm
+    _check(call(X.data_ptr(), W.data_ptr(), Y.data_ptr(), P, K, N, DTYPE[dt], _stream(stream)))
     return Y
 
 

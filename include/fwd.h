@@ -269,6 +269,21 @@ int fwd_gemm(const void* X, const void* W, float* Y, int32_t P, int32_t in, int3
              int32_t dtype, void* hip_stream);
 
 /*
+ * fwd_gemm for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same arguments,
+ * the same kernels and the same result bit for bit, with no allocation of any kind.
+ * The split partials of products that fwd_gemm cuts into ranges of `in` live in a
+ * static device array of 16 MiB that every GPU the library runs on holds until the
+ * process ends; a product whose partials need more returns FWD_E_TOO_LARGE and
+ * computes nothing. The array is shared by every call on a GPU and keeps the last
+ * call's partials (each call writes every partial it reads): calls that overlap on one
+ * GPU race.
+ * Errors: FWD_E_ARG, FWD_E_TOO_LARGE, FWD_E_UNAVAILABLE, FWD_E_HIP.
+ */
+int fwd_gemm_noalloc(const void* X, const void* W, float* Y, int32_t P, int32_t in, int32_t out,
+                     int32_t dtype, void* hip_stream);
+
+/*
  * Causal grouped-query attention alone, the operation inside each layer
  * ("N7 · model/forward-parity", introduction; "N9 · metalgemm", Theorem 1 op
  * chain): o[b,i,h,:] = sum_j softmax_j(q[b,i,h,:]·k[b,j,g,:] / sqrt(D)) v[b,j,g,:]
