@@ -11,10 +11,12 @@
 // the softmax statistics are per lane except for one cross-lane max. The
 // probabilities then feed Oᵀ += Vᵀ·Pᵀ straight from registers as the MFMA B operand;
 // values are kept transposed (keys contiguous) so the A operand is a 16-byte LDS
-// read. K and Vᵀ blocks stream global -> LDS by buffer loads through a 3-deep ring
-// (two blocks in flight), and the score MFMAs of block j + 1 are issued before the
-// softmax of block j so the two overlap. Registers are held to two wavefronts per
-// SIMD, so one wavefront's softmax also overlaps the other's MFMAs.
+// read. K and Vᵀ blocks stream global -> LDS by buffer loads through a 3-deep ring.
+// Each step of the block loop issues the next block's score MFMAs in one basic block
+// with this block's exponentials, then the value MFMAs (for D = 64 all the step's MFMA
+// fragments are read from LDS first). The normaliser sums the bf16 probabilities the
+// value product uses. With two or three wavefronts per SIMD, one wavefront's vector
+// work overlaps another's MFMAs.
 //
 // f32 path (D <= 64): one wavefront per query row on the vector ALUs.
 #include "common.h"
@@ -53,40 +55,69 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// One 1 KiB piece (64 lanes x 16 bytes) of a K or Vᵀ block, global -> LDS directly.
-// Pieces 0 .. D/16-1 are K, D/16 .. D/8-1 are Vᵀ. Keys past the sequence read as zero
-// (out of the buffer's range); the partial 8-key chunk at the end of Vᵀ rows reads the
-// row padding, whose weight is exactly zero.
+// One K + Vᵀ block, global -> LDS by buffer loads into `kl` (1 KiB pieces of 64 lanes x
+// 16 bytes; pieces 0 .. D/16 - 1 are K, the rest Vᵀ; this wavefront takes pieces
+// wave + 4 p, so p < LPW / 2 are K pieces). loff[p] is the lane's byte offset relative
+// to the block's first key. The buffer resources start at the block: K keys past S
+// fall outside the K range and read as zero; Vᵀ chunks (8 keys) at or past S are given
+// an offset outside the range in the last block, and the partial chunk before S reads
+// the zero padding of the Vᵀ rows. (A device function, not a lambda: a lambda in a
+// kernel is also compiled for the host, where the resource type does not exist.)
 template <int D>
-__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int64_t ldk, int ldvt,
-                                           bf16_t* klds, bf16_t* vlds, int j0, int S, int piece, int lane) {
-  constexpr int CH = D / 8, RPB = 64 / CH;  // K: chunks per row, rows per piece
-  if (piece < D / 16) {
-    const int R = piece * RPB + lane / CH;
-    const int c = kswz<D>(R, lane % CH);
-    const int key = j0 + key_of_row(R);
-    const uint32_t off = key < S ? (uint32_t)(key * ldk + c * 8) * 2u : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(klds + piece * 512), 16, off, 0, 0, 0);
-  } else {
-    const int vp = piece - D / 16;
-    const int d = vp * 16 + lane / 4;
-    const int c = vswz(d, lane & 3);
-    const int key = j0 + c * 8;
-    const uint32_t off = key < S ? (uint32_t)(d * ldvt + key) * 2u : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vlds + vp * 512), 16, off, 0, 0, 0);
+__device__ __forceinline__ void load_block(const bf16_t* kbase, const bf16_t* vbase, int64_t ldk, int ldvt, int S,
+                                           int j0, bf16_t* kl, const uint32_t* loff, int wave, int lane) {
+  constexpr int LPW = D / 32, KSZ = KB * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)j0 * ldk, (int64_t)(S - j0) * ldk * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + j0, ((int64_t)D * ldvt - j0) * 2);
+  const bool tail = j0 + KB > S;
+#pragma unroll
+  for (int p = 0; p < LPW; ++p) {
+    const int piece = wave + 4 * p;
+    if (p < LPW / 2) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kl + piece * 512), 16, loff[p], 0, 0, 0);
+    } else {
+      const int vp = piece - D / 16;
+      uint32_t off = loff[p];
+      if (tail) {
+        const int d = vp * 16 + lane / 4;
+        if (j0 + vswz(d, lane & 3) * 8 >= S) off = 0x80000000u;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(kl + KSZ + vp * 512), 16, off, 0, 0, 0);
+    }
   }
 }
 
+// Cross-half maximum: lanes l and l ^ 32 (the two halves of one query's keys) swap
+// values by one v_permlane32_swap, no LDS round trip.
+__device__ __forceinline__ float max_halves(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+
+// Wavefronts per SIMD the registers are held to, and whether a block's MFMA fragments
+// are read from LDS ahead of its softmax. D = 128: three (three 48 KiB workgroups per
+// CU), fragments read just before their MFMAs; in the Llama-shape forward this is 8%
+// faster than two wavefronts reading ahead. D = 64: two, reading ahead (11% faster).
+template <int D>
+constexpr int attn_waves_per_simd() { return D == 128 ? 3 : 2; }
+template <int D, int QT>
+constexpr bool attn_read_ahead() { return QT == 1 && D == 64; }
+
 template <int D, int QT, int ST>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
+__global__ __launch_bounds__(256, (attn_waves_per_simd<D>())) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
   constexpr int QW = 32 * QT;      // queries per wavefront
   constexpr int BQ = 4 * QW;       // queries per workgroup
   constexpr int DS = D / 16;       // k-steps of the score contraction
   constexpr int DT = D / 32;       // 32-row d tiles of the output
-  constexpr int PIECES = D / 8;    // 1 KiB loads per K+Vᵀ block
-  constexpr int LPW = PIECES / 4;  // ... per wavefront
-  constexpr int KSZ = KB * D, VSZ = D * KB;
-  __shared__ __attribute__((aligned(1024))) bf16_t lds[ST * (KSZ + VSZ)];
+  constexpr int LPW = D / 32;      // 1 KiB pieces per wavefront per block: D / 8 over 4 wavefronts
+  constexpr int KSZ = KB * D, VSZ = D * KB, SLOT = KSZ + VSZ;
+  // The loop is unrolled so that both the ring slot of a block (its index since the
+  // first block, modulo ST) and the score buffer it uses (modulo 2) are constants:
+  // LDS reads then take immediate offsets, and no scores are copied between buffers.
+  constexpr int UNROLL = ST % 2 ? 2 * ST : ST;
+  constexpr bool READ_AHEAD = attn_read_ahead<D, QT>();
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[ST * SLOT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 31, lg = lane >> 5;
@@ -109,8 +140,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, float sca
   const bf16_t* qbase = (const bf16_t*)a.q + (int64_t)b * S * a.ldq + h * D;
   const bf16_t* kbase = (const bf16_t*)a.k + (int64_t)b * S * a.ldk + g * D;
   const bf16_t* vbase = (const bf16_t*)a.vt + (int64_t)(b * a.Hkv + g) * D * a.ldvt;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (int64_t)S * a.ldk * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (int64_t)D * a.ldvt * 2);
 
   // Qᵀ fragments (MFMA B operand): lane owns query wq0 + 32 qt + ln, dims 16 ds + 8 lg .. + 7
   bf16x8_t qf[QT][DS];
@@ -126,6 +155,23 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, float sca
   }
   wait_vmcnt<0>();
 
+  // Block loads: 1 KiB pieces (64 lanes x 16 bytes) global -> LDS by buffer loads.
+  // Pieces 0 .. D/16 - 1 are the K block, the rest its Vᵀ block; this wavefront takes
+  // pieces wave + 4 p, so that p < LPW / 2 are K pieces. Byte offsets relative to the
+  // block's first key are the same for every block.
+  uint32_t loff[LPW];
+#pragma unroll
+  for (int p = 0; p < LPW; ++p) {
+    const int piece = wave + 4 * p;
+    if (p < LPW / 2) {
+      constexpr int CH = D / 8, RPB = 64 / CH;  // chunks per K row, rows per piece
+      const int R = piece * RPB + lane / CH;
+      loff[p] = (uint32_t)(key_of_row(R) * a.ldk + kswz<D>(R, lane % CH) * 8) * 2u;
+    } else {
+      const int d = (piece - D / 16) * 16 + lane / 4;
+      loff[p] = (uint32_t)(d * a.ldvt + vswz(d, lane & 3) * 8) * 2u;
+    }
+  }
   // key blocks of the workgroup, and the active sub-range of this wavefront
   const int kv_end = min(S, q0 + BQ);
   const int kv_begin = W > 0 ? max(0, q0 - W + 1) : 0;
@@ -134,15 +180,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, float sca
   const int wb1 = wq0 < S ? min(kb1, wq1 / KB + 1) : kb0;  // empty when the wave has no queries
   auto active = [&](int kb) { return kb >= wb0 && kb < wb1; };
 
-  auto issue_block = [&](int kb) {
-    bf16_t* kl = lds + (kb % ST) * (KSZ + VSZ);
-#pragma unroll
-    for (int p = 0; p < LPW; ++p)
-      load_piece<D>(rk, rv, a.ldk, a.ldvt, kl, kl + KSZ, kb * KB, S, wave + 4 * p, lane);
-  };
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
-    if (kb0 + s < kb1) issue_block(kb0 + s);
+    if (kb0 + s < kb1) load_block<D>(kbase, vbase, a.ldk, a.ldvt, S, (kb0 + s) * KB, lds + s * SLOT, loff, wave, lane);
 
   floatx16_t o[DT][QT];
 #pragma unroll
@@ -155,117 +195,206 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, float sca
     m[qt] = -INFINITY;
     l[qt] = 0.f;
   }
+  floatx16_t sb[2][QT];  // scores of the current block and of the next one
 
-  // Sᵀ of block kb (K from its LDS buffer)
-  auto scores = [&](int kb, floatx16_t (&sc)[QT]) {
-    const bf16_t* K = lds + (kb % ST) * (KSZ + VSZ);
+  // Sᵀ of the block in ring slot `slot` into score buffer `par`
+  auto scores = [&](int slot, int par) __attribute__((always_inline)) {
+    const bf16_t* K = lds + slot * SLOT;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) sc[qt] = floatx16_t{};
+    for (int qt = 0; qt < QT; ++qt) sb[par][qt] = floatx16_t{};
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(K + ln * D + (kswz<D>(ln, 2 * ds + lg) << 3)));
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) sc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qt][ds], sc[qt], 0, 0, 0);
+      for (int qt = 0; qt < QT; ++qt)
+        sb[par][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qt][ds], sb[par][qt], 0, 0, 0);
     }
   };
-
-  floatx16_t sc[QT], sn[QT];
+  // Causal / window / length mask of block kb: lane (ln, lg), register r of q tile qt
+  // is key j0 + 16 lg + r against query wq0 + 32 qt + ln.
+  auto mask = [&](int kb, int par) __attribute__((always_inline)) {
+    const int j0 = kb * KB;
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) sc[qt] = sn[qt] = floatx16_t{};
+    for (int qt = 0; qt < QT; ++qt) {
+      // key j0 + 16 lg + r is visible from query qi iff 0 <= qi - key < window
+      // (window = W if W > 0, else unbounded) and key < S
+      const int qi = wq0 + qt * 32 + ln;
+      const int d0 = qi - (j0 + 16 * lg);  // qi - key for r = 0
+      const int wlim = W > 0 ? W : 0x7FFFFFFF;
+      const int klim = S - (j0 + 16 * lg);  // r < klim <=> key < S
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dd = d0 - r;
+        const bool vis = (unsigned)dd < (unsigned)wlim && r < klim;
+        sb[par][qt][r] = vis ? sb[par][qt][r] : -INFINITY;
+      }
+    }
+  };
+  // Row maxima (scaled to log2 units), and the lazy rescaling: the reference max m of
+  // a query moves only when a block max exceeds it by more than 2^8, so probabilities
+  // stay <= 256 and the O / l rescale (exact powers of exp2) is skipped on most blocks.
+  auto max_and_rescale = [&](int par) __attribute__((always_inline)) {
+    float mx[QT];
+    bool need = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float v = sb[par][qt][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) v = fmaxf(v, sb[par][qt][r]);
+      mx[qt] = max_halves(v) * scale_log2;
+      need |= mx[qt] > m[qt] + 8.f;
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float mnew = mx[qt] > m[qt] + 8.f ? mx[qt] : m[qt];
+        const float corr = mnew == -INFINITY ? 1.f : fast_exp2(m[qt] - mnew);
+        m[qt] = mnew;
+        l[qt] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= corr;
+      }
+    }
+  };
+  // Probabilities p = exp2(s log2e / sqrt(D) - m) as bf16 MFMA B operands. The
+  // normaliser l sums the same bf16 values the value product weights (two per
+  // v_dot2 with ones), so the weights of a query sum to one.
+  auto probs = [&](int par, bf16x8_t (&pf)[QT][2]) __attribute__((always_inline)) {
+    const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float nmo = m[qt] == -INFINITY ? 0.f : -m[qt];
+      uint32_t pk[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pk[i] = pack_bf16x2(fast_exp2(fmaf(sb[par][qt][2 * i], scale_log2, nmo)),
+                            fast_exp2(fmaf(sb[par][qt][2 * i + 1], scale_log2, nmo)));
+      float s = l[qt];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[i]), ones, s, false);
+      l[qt] = s;
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+        pf[qt][mm] = as_bf16x8(u32x4_t{pk[4 * mm], pk[4 * mm + 1], pk[4 * mm + 2], pk[4 * mm + 3]});
+    }
+  };
+  // Oᵀ[d, query] += Vᵀ[d, keys] · Pᵀ[keys, query], the d tiles innermost so that
+  // consecutive MFMAs accumulate into different registers
+  auto pv = [&](int slot, const bf16x8_t (&pf)[QT][2]) __attribute__((always_inline)) {
+    const bf16_t* V = lds + slot * SLOT + KSZ;
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = dt * 32 + ln;
+        const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(V + d * KB + (vswz(d, 2 * lg + mm) << 3)));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qt][mm], o[dt][qt], 0, 0, 0);
+      }
+  };
+  // The same two products from fragments read ahead: all K fragments of a block and all
+  // Vᵀ fragments are read from LDS before the block's softmax, so that no MFMA waits on
+  // the LDS read issued just before it.
+  auto read_k = [&](int slot, bf16x8_t (&kf)[DS]) __attribute__((always_inline)) {
+    const bf16_t* K = lds + slot * SLOT;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+      kf[ds] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(K + ln * D + (kswz<D>(ln, 2 * ds + lg) << 3)));
+  };
+  auto read_v = [&](int slot, bf16x8_t (&vf)[2][DT]) __attribute__((always_inline)) {
+    const bf16_t* V = lds + slot * SLOT + KSZ;
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = dt * 32 + ln;
+        vf[mm][dt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(V + d * KB + (vswz(d, 2 * lg + mm) << 3)));
+      }
+  };
+  auto scores_from = [&](const bf16x8_t (&kf)[DS], int par) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) sb[par][qt] = floatx16_t{};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        sb[par][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[qt][ds], sb[par][qt], 0, 0, 0);
+  };
+  auto pv_from = [&](const bf16x8_t (&vf)[2][DT], const bf16x8_t (&pf)[QT][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[mm][dt], pf[qt][mm], o[dt][qt], 0, 0, 0);
+  };
+
   if (kb0 < kb1) {
     if (kb0 + ST - 2 < kb1) wait_vmcnt<(ST - 2) * LPW>();
     else wait_vmcnt<0>();
   }
   lds_barrier();
-  if (active(kb0)) scores(kb0, sc);
+  if (active(kb0)) scores(0, 0);
 
-  for (int kb = kb0; kb < kb1; ++kb) {
-    if (kb + 1 < kb1) {
-      if (kb + ST - 2 < kb1) wait_vmcnt<(ST - 3) * LPW>();  // block kb + 1 has landed
-      else wait_vmcnt<0>();
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      lds_barrier();  // ... for everyone; and everyone is done with block kb - 1
-      if (kb + ST - 1 < kb1) issue_block(kb + ST - 1);  // refill block kb - 1's buffer
-      if (active(kb + 1)) scores(kb + 1, sn);  // MFMAs that overlap the softmax below
-    }
-    if (active(kb)) {
-      const int j0 = kb * KB;
-      // lane (ln, lg), register r of q tile qt: key j0 + 16 lg + r, query wq0 + 32 qt + ln.
-      // Blocks strictly below the diagonal and inside the window need no mask.
+  for (int kb = kb0; kb < kb1; kb += UNROLL) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int k = kb + u;
+      if (k >= kb1) break;
+      const int slot = u % ST, par = u & 1;
+      const bool has_next = k + 1 < kb1;
+      if (has_next) {
+        if (k + ST - 2 < kb1) wait_vmcnt<(ST - 3) * LPW>();  // block k + 1 has landed
+        else wait_vmcnt<0>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();  // ... for everyone; and everyone is done with block k - 1
+        if (k + ST - 1 < kb1)  // refill block k - 1's slot
+          load_block<D>(kbase, vbase, a.ldk, a.ldvt, S, (k + ST - 1) * KB, lds + (u + ST - 1) % ST * SLOT, loff, wave,
+                        lane);
+      }
+      const bool act = active(k), act1 = has_next && active(k + 1);
+      const int j0 = k * KB;
+      // blocks strictly below the diagonal and inside the window need no mask
       const bool full = j0 + KB - 1 <= wq0 && (W <= 0 || wq1 - j0 < W);
-      float mx[QT];
+      if (act && READ_AHEAD) {
+        bf16x8_t kf[DS], vf[2][DT], pf[QT][2];
+        read_k((u + 1) % ST, kf);
+        read_v(slot, vf);
+        if (!full) mask(k, par);
+        max_and_rescale(par);
+        // one basic block: the next block's score MFMAs interleave with this block's
+        // exponentials (after the wavefront's last block they read a stale slot and
+        // are not used)
+        scores_from(kf, par ^ 1);
+        probs(par, pf);
+        pv_from(vf, pf);
+        // issue order: each score MFMA of the next block followed by a share of the
+        // vector work that makes the first half of P, then the first half's value
+        // MFMAs each followed by a share of the second half's, then the rest
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        if (!full) {
-          // key j0 + 16 lg + r is visible from query qi iff 0 <= qi - key < window
-          // (window = W if W > 0, else unbounded) and key < S
-          const int qi = wq0 + qt * 32 + ln;
-          const int d0 = qi - (j0 + 16 * lg);            // qi - key for r = 0
-          const int wlim = W > 0 ? W : 0x7FFFFFFF;
-          const int klim = S - (j0 + 16 * lg);           // r < klim <=> key < S
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int dd = d0 - r;
-            const bool vis = (unsigned)dd < (unsigned)wlim && r < klim;
-            sc[qt][r] = vis ? sc[qt][r] : -INFINITY;
-          }
+        for (int i = 0; i < DS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 24 / DS, 0);
         }
-        float v = sc[qt][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) v = fmaxf(v, sc[qt][r]);
-        mx[qt] = v;
-      }
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 32, 64)) * scale_log2;
-      // Lazy rescaling: the reference max m of a query moves only when a block max
-      // exceeds it by more than 2^8, so probabilities stay <= 256 and the O / l
-      // rescale (exact powers of exp2) is skipped on most blocks.
-      bool need = false;
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) need |= mx[qt] > m[qt] + 8.f;
-      if (__any(need)) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const float mnew = mx[qt] > m[qt] + 8.f ? mx[qt] : m[qt];
-          const float corr = mnew == -INFINITY ? 1.f : fast_exp2(m[qt] - mnew);
-          m[qt] = mnew;
-          l[qt] *= corr;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= corr;
+        for (int i = 0; i < DT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 26 / DT, 0);
         }
-      }
-      bf16x8_t pf[QT][2];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float mo = m[qt] == -INFINITY ? 0.f : m[qt];
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(sc[qt][r], scale_log2, -mo));
-        float ps = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ps += p[r];
-        l[qt] += ps;
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
-          pf[qt][mm] = as_bf16x8(u32x4_t{pack_bf16x2(p[8 * mm + 0], p[8 * mm + 1]), pack_bf16x2(p[8 * mm + 2], p[8 * mm + 3]),
-                                         pack_bf16x2(p[8 * mm + 4], p[8 * mm + 5]), pack_bf16x2(p[8 * mm + 6], p[8 * mm + 7])});
-      }
-      // Oᵀ[d, query] += Vᵀ[d, keys] · Pᵀ[keys, query]
-      const bf16_t* V = lds + (kb % ST) * (KSZ + VSZ) + KSZ;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 32 + ln;
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(V + d * KB + (vswz(d, 2 * lg + mm) << 3)));
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-            o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qt][mm], o[dt][qt], 0, 0, 0);
-        }
+        __builtin_amdgcn_sched_group_barrier(0x008, DT, 0);
+      } else if (act) {
+        if (!full) mask(k, par);
+        max_and_rescale(par);
+        bf16x8_t pf[QT][2];
+        scores((u + 1) % ST, par ^ 1);
+        probs(par, pf);
+        pv(slot, pf);
+      } else if (act1) {
+        scores((u + 1) % ST, par ^ 1);
       }
     }
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) sc[qt] = sn[qt];
   }
 
   // normalise and store: register r of d tile dt is dim 32 dt + 8 (r / 4) + 4 lg + r % 4

@@ -125,7 +125,10 @@ ATTN_CASES = [
     (1, 1, 4, 2, 64, 0), (2, 9, 9, 3, 64, 0), (1, 100, 4, 4, 64, 0), (1, 257, 8, 2, 128, 0),
     (2, 130, 32, 8, 128, 0), (1, 300, 4, 1, 128, 64), (1, 97, 2, 1, 256, 0), (1, 200, 16, 8, 256, 33),
     (1, 64, 2, 2, 64, 4), (1, 65, 2, 1, 64, 64), (1, 65, 2, 1, 64, 65), (1, 65, 2, 1, 64, 66),
-    (1, 1100, 16, 8, 256, 1024),
+    (1, 1536, 3, 1, 64, 256),
+    (1, 1100, 16, 8, 256, 1024), (1, 2048, 2, 1, 128, 0),
+    # many heads: grids of 512 or more workgroups, as in the large forwards
+    (2, 256, 128, 16, 64, 0), (1, 512, 128, 16, 128, 100), (1, 384, 176, 16, 256, 0),
 ]
 
 
