@@ -64,7 +64,12 @@ def test_route_op_matches_oracle_decisions(fwd, T, E, k, norm):
     np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-7)
 
 
-def _check(cfg, got, ref, band, rows_mask=None, slots=None):
+def _check(cfg, got, ref, band, rows_mask=None, slots=None, argmax=True):
+    """Hidden slots by cosine on the given rows; with argmax, the argmax on those rows
+    under the oracle-side band. Where routing is undecided on some tokens (their k-th and
+    (k+1)-th router logits lie within the bf16 error), the argmax is checked on the
+    decided tokens only: an undecided token may take other experts and its logits are
+    then not comparable."""
     L = cfg.n_layers
     for s in (slots if slots is not None else range(L + 2)):
         g, r = got["hidden"][s], ref["hidden"][s]
@@ -72,6 +77,8 @@ def _check(cfg, got, ref, band, rows_mask=None, slots=None):
             g, r = g[rows_mask], r[rows_mask]
         c = cosine(g, r)
         assert c >= COS_MIN, f"{cfg.name}: slot {s} cosine {c}"
+    if not argmax:
+        return None, None
     rz, ga, band = ref["logits"], got["argmax"], np.asarray(band).reshape(got["argmax"].shape)
     if rows_mask is not None:
         rz, ga, band = rz[rows_mask], ga[rows_mask], band[rows_mask]
@@ -116,7 +123,7 @@ def test_moe_top2_last_layer_on_decided_tokens(fwd):
     assert decided.mean() >= 0.75, (decided.mean(), err)
     L = cfg.n_layers
     # slots before the MoE layer hold every token; from it on, only the decided ones
-    _check(cfg, got, ref, band, slots=range(L))
+    _check(cfg, got, ref, band, slots=range(L), argmax=False)
     pinned, near = _check(cfg, got, ref, band, rows_mask=decided, slots=(L, L + 1))
     _say(f"  {cfg.name}: {int(decided.sum())} of {decided.size} tokens decided (bf16 logit error {err:.2e}), "
          f"argmax pinned {pinned} near-tie {near}")
@@ -217,7 +224,7 @@ def test_moe_multi_tile_segments_and_empty_experts(fwd):
     assert decided.mean() >= 0.75, decided.mean()
     band = oracle_band(ref["logits"], refb["logits"])
     L = cfg.n_layers
-    _check(cfg, got, ref, band, slots=range(L))
+    _check(cfg, got, ref, band, slots=range(L), argmax=False)
     pinned, near = _check(cfg, got, ref, band, rows_mask=decided, slots=(L, L + 1))
     _say(f"  {cfg.name}: argmax pinned {pinned} near-tie {near} on the decided tokens")
     model.close()
@@ -250,6 +257,6 @@ def test_moe_128_experts_top8_full_size(fwd):
     # decided beyond four times the bf16 router-logit error
     assert decided.mean() >= 0.15, decided.mean()
     band = oracle_band(ref["logits"], refb["logits"])
-    _check(cfg, got, ref, band, slots=(0,))
+    _check(cfg, got, ref, band, slots=(0,), argmax=False)
     pinned, near = _check(cfg, got, ref, band, rows_mask=decided, slots=(1, 2))
     _say(f"  {cfg.name}: argmax pinned {pinned} near-tie {near} on the decided tokens")
