@@ -367,6 +367,228 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(DecodeArgs a) {
   }
   if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// ----------------------------------------------------- D = 128, exact group size
+// The same workgroup layout (256 keys, 4 wavefronts x 64 keys, 16 lanes per key
+// holding 8 dims each) with the group size a template constant, so no per-head branch.
+// Scores: v_dot2_f32_bf16 on the bf16 (q, k) pairs (exact products, fp32 sums), then
+// the G per-head partial sums of a key are reduced over its 16 lanes together
+// (head_sums). P·V: two keys at a time, their values for one dim paired by v_perm_b32
+// and weighted by the bf16 probabilities with v_dot2. The probabilities are rounded
+// to bf16 before the chunk sum, so the weights and the normaliser agree.
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+// DPP controls within a row of 16 lanes: exchange across lane bit 0 / bit 1
+// (quad_perm [1,0,3,2] / [2,3,0,1]) and rotations by 4 and 8 lanes (row_ror), which
+// keep bits 0 and 1 of the lane and flip bit 2 / bit 3 respectively.
+template <int BIT>
+__device__ __forceinline__ float dpp_bit(float v) {
+  if constexpr (BIT == 0) return dpp_mov<0xB1>(v);
+  else if constexpr (BIT == 1) return dpp_mov<0x4E>(v);
+  else if constexpr (BIT == 2) return dpp_mov<0x124>(v);
+  else return dpp_mov<0x128>(v);
+}
+// v[0 .. G) are this lane's partial sums of G heads; the key's 16 lanes form one DPP
+// row. For each of the lane bits t < log2(G) in turn, a lane keeps the half of its
+// remaining heads selected by bit t of its index and adds the partner's (the lane
+// with bit t flipped and the same lower bits) partial of that half; the bits from
+// log2(G) to 3 are then summed by exchanges that keep the lower bits. Returns the
+// complete sum of head head_of_lane<G>(sub).
+template <int G, int T = 0>
+__device__ __forceinline__ void halve(float (&v)[G], int sub) {
+  if constexpr ((G >> T) > 1) {
+    constexpr int H = (G >> T) / 2;
+    const bool b = (sub >> T) & 1;
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+      const float keep = b ? v[k + H] : v[k];
+      const float send = b ? v[k] : v[k + H];
+      v[k] = keep + dpp_bit<T>(send);
+    }
+    halve<G, T + 1>(v, sub);
+  }
+}
+template <int G>
+__device__ __forceinline__ float head_sums(float (&v)[G], int sub) {
+  halve<G>(v, sub);
+  constexpr int LB = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  float r = v[0];
+  if constexpr (LB <= 0) r += dpp_bit<0>(r);
+  if constexpr (LB <= 1) r += dpp_bit<1>(r);
+  if constexpr (LB <= 2) r += dpp_bit<2>(r);
+  r += dpp_bit<3>(r);
+  return r;
+}
+template <int G>
+__device__ __forceinline__ int head_of_lane(int sub) {
+  int h = 0;
+#pragma unroll
+  for (int t = 0; (G >> t) > 1; ++t) h += ((sub >> t) & 1) * ((G >> t) / 2);
+  return h;
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void attn_decode_d128_kernel(DecodeArgs a) {
+  constexpr int D = 128, CH = kDecodeChunk, LPK = 16, KPL = 4, NL = 16;
+  constexpr int RS = G * D + 4;  // row stride of the partial outputs (floats)
+  static_assert(CH == 256 && (G == 1 || G == 2 || G == 4 || G == 8), "4 x 64 keys per chunk, G in {1, 2, 4, 8}");
+  __shared__ __align__(16) float ps[CH][G];
+  __shared__ __align__(16) float ored[4 * KPL * RS];
+  __shared__ float stat[2][G];
+  __shared__ int last;
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int sub = lane % LPK, kk = lane / LPK;
+  const int lo = a.window > 0 ? max(0, a.len - a.window) : 0;
+  const int j0 = lo + c * CH, j1 = min(a.len, j0 + CH);
+  const int64_t head = ((int64_t)b * a.Hkv + g) * a.Smax;
+  // keys at or past j1 (including cache rows not written yet) read as zeros
+  const auto krs = make_rsrc(a.kc + head * D, (int64_t)j1 * D * 2);
+  const auto vrs = make_rsrc(a.vc + head * D, (int64_t)j1 * D * 2);
+  auto piece = [&](int i) {  // byte offset of this lane's 16 bytes of piece i
+    return (uint32_t)(j0 + wave * 64 + i * KPL + kk) * (D * 2) + sub * 16;
+  };
+
+  // loads complete in issue order: the query first, then the keys, then the values
+  u32x4_t qv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qv[h] = *reinterpret_cast<const u32x4_t*>(a.q + (int64_t)b * a.ldq + (int64_t)(g * G + h) * D + sub * 8);
+  u32x4_t kv[NL], vv[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) kv[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, piece(i), 0, 0);
+#pragma unroll
+  for (int i = 0; i < NL; ++i) vv[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, piece(i), 0, 0);
+
+  // scores (log2 units), -inf past the last key
+  const int hl = head_of_lane<G>(sub);
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    float sh[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float d = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) d = dot2_bf16(qv[h][w], kv[i][w], d);
+      sh[h] = d;
+    }
+    const float tot = head_sums<G>(sh, sub);
+    const int jl = wave * 64 + i * KPL + kk;
+    if (sub < G) ps[jl][hl] = j0 + jl < j1 ? tot * a.scale_log2 : -INFINITY;
+  }
+  __syncthreads();
+
+  // chunk maximum and sum per head (probabilities rounded to bf16), one wavefront per head
+  for (int h = wave; h < G; h += 4) {
+    float m = -INFINITY;
+    for (int i = lane; i < CH; i += 64) m = fmaxf(m, ps[i][h]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int i = lane; i < CH; i += 64) {
+      const float e = ps[i][h] == -INFINITY ? 0.f : fast_exp2(ps[i][h] - m);
+      const float p = __uint_as_float(pack_bf16x2(e, 0.f) << 16);
+      ps[i][h] = p;
+      l += p;
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      stat[0][h] = m;
+      stat[1][h] = l;
+    }
+  }
+  __syncthreads();
+
+  // P·V, two keys (pieces i, i + 1) per step: acc[h][e] += p_i v_i[e] + p_{i+1} v_{i+1}[e]
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NL; i += 2) {
+    const int ja = wave * 64 + i * KPL + kk, jb = ja + KPL;
+    uint32_t pp[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h)  // both probabilities are bf16 values: their high halves
+      pp[h] = __builtin_amdgcn_perm(__float_as_uint(ps[jb][h]), __float_as_uint(ps[ja][h]), 0x07060302u);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t xl = __builtin_amdgcn_perm(vv[i + 1][w], vv[i][w], 0x05040100u);  // dim 2w of both keys
+      const uint32_t xh = __builtin_amdgcn_perm(vv[i + 1][w], vv[i][w], 0x07060302u);  // dim 2w + 1
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        acc[h][2 * w] = dot2_bf16(pp[h], xl, acc[h][2 * w]);
+        acc[h][2 * w + 1] = dot2_bf16(pp[h], xh, acc[h][2 * w + 1]);
+      }
+    }
+  }
+  float* orow = ored + (wave * KPL + kk) * RS + sub * 8;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    *reinterpret_cast<float4*>(orow + h * D) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+    *reinterpret_cast<float4*>(orow + h * D + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+  }
+  __syncthreads();
+
+  auto put_o = [&](int h, int d, float v) {
+    const int col = (g * G + h) * D + d;
+    Elem<bf16_t>::store(a.o + (a.o_tiled ? tiled_index(b, col, (int)a.ldo) : (int64_t)b * a.ldo + col), v);
+  };
+  constexpr int items = G * D;
+  float* pbase = a.part + ((int64_t)b * a.Hq + g * G) * a.nsplit * (D + 2);  // head g * G + h at h * nsplit * (D + 2)
+  for (int it = tid; it < items; it += 256) {
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4 * KPL; ++r) sum += ored[r * RS + it];
+    const int h = it / D, d = it - h * D;
+    if (a.nsplit == 1) put_o(h, d, sum / stat[1][h]);
+    else store_agent(pbase + ((int64_t)h * a.nsplit + c) * (D + 2) + d, sum);
+  }
+  if (a.nsplit == 1) return;
+  if (tid < G) {
+    store_agent(pbase + ((int64_t)tid * a.nsplit + c) * (D + 2) + D, stat[0][tid]);
+    store_agent(pbase + ((int64_t)tid * a.nsplit + c) * (D + 2) + D + 1, stat[1][tid]);
+  }
+  // the last chunk of this (sequence, kv head) to finish merges all of them
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  unsigned* cnt = a.count + (int64_t)b * a.Hkv + g;
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(a.nsplit - 1);
+  __syncthreads();
+  if (!last) return;
+  // one pass over the chunks in order per (head, dim), rescaling to the running maximum
+  const int ns = a.nsplit;
+  for (int it = tid; it < items; it += 256) {
+    const int h = it / D, d = it - h * D;
+    const float* ph = pbase + (int64_t)h * ns * (D + 2);
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    constexpr int TB = 8;  // chunks loaded per round trip
+    for (int t0 = 0; t0 < ns; t0 += TB) {
+      float ov[TB], mv[TB], lv[TB];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const int t = t0 + u < ns ? t0 + u : t0;  // (surplus loads repeat t0, unused)
+        ov[u] = load_agent(ph + (int64_t)t * (D + 2) + d);
+        mv[u] = load_agent(ph + (int64_t)t * (D + 2) + D);
+        lv[u] = load_agent(ph + (int64_t)t * (D + 2) + D + 1);
+      }
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        if (t0 + u >= ns) break;
+        const float Mn = fmaxf(M, mv[u]);
+        const float r = fast_exp2(M - Mn), e = fast_exp2(mv[u] - Mn);  // (first chunk: r = 0)
+        O = O * r + ov[u] * e;
+        L = L * r + lv[u] * e;
+        M = Mn;
+      }
+    }
+    put_o(h, d, O / L);
+  }
+  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 }  // namespace
 
 namespace {
@@ -388,6 +610,11 @@ hipError_t decode_bf16(const DecodeArgs& a, int B, hipStream_t s) {
   hipLaunchKernelGGL((attn_decode_bf16_kernel<D, GM>), dim3(a.nsplit, a.Hkv, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+template <int G>
+hipError_t decode_d128(const DecodeArgs& a, int B, hipStream_t s) {
+  hipLaunchKernelGGL((attn_decode_d128_kernel<G>), dim3(a.nsplit, a.Hkv, B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 }  // namespace
 
 hipError_t attention_decode(DType dt, const void* q, int64_t ldq, const void* kc, const void* vc, int Smax, int len,
@@ -404,7 +631,14 @@ hipError_t attention_decode(DType dt, const void* q, int64_t ldq, const void* kc
     a.nsplit = (len - lo + kDecodeChunk - 1) / kDecodeChunk;
     switch (D) {
       case 64: return G <= 4 ? decode_bf16<64, 4>(a, B, s) : decode_bf16<64, 8>(a, B, s);
-      case 128: return G <= 4 ? decode_bf16<128, 4>(a, B, s) : decode_bf16<128, 8>(a, B, s);
+      case 128:
+        switch (G) {
+          case 1: return decode_d128<1>(a, B, s);
+          case 2: return decode_d128<2>(a, B, s);
+          case 4: return decode_d128<4>(a, B, s);
+          case 8: return decode_d128<8>(a, B, s);
+        }
+        return G <= 4 ? decode_bf16<128, 4>(a, B, s) : decode_bf16<128, 8>(a, B, s);
       default: return G <= 4 ? decode_bf16<256, 4>(a, B, s) : decode_bf16<256, 8>(a, B, s);
     }
   }

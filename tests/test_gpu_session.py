@@ -205,12 +205,17 @@ def test_session_errors(fwd):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("shape", ["d128_g4", "d256_g2_window", "d64_g8"])
+@pytest.mark.parametrize("shape", ["d128_g4", "d256_g2_window", "d64_g8", "d128_g1", "d128_g2_window", "d128_g8"])
 def test_bf16_decode_head_shapes(fwd, shape):
     """The decode attention's head geometries: 128-wide heads in groups of 4 (Llama-3
     shape), 256-wide heads in pairs with a 64-key window on local layers (Gemma-style),
-    and 64-wide heads in groups of 8; a 300-token prompt spans two key chunks."""
+    64-wide heads in groups of 8, and the other group sizes of the 128-wide kernel (1;
+    2 with a window; 8); a 300-token prompt spans two key chunks."""
     base = {"d128_g4": wl.LLAMA3_8B.replace(n_heads=8, n_kv_heads=2, head_dim=128),
+            "d128_g1": wl.LLAMA3_8B.replace(n_heads=4, n_kv_heads=4, head_dim=128),
+            "d128_g2_window": wl.LLAMA3_8B.replace(n_heads=4, n_kv_heads=2, head_dim=128, sliding_window=64,
+                                                   layer_kind=("local", "global")),
+            "d128_g8": wl.LLAMA3_8B.replace(n_heads=16, n_kv_heads=2, head_dim=128),
             "d256_g2_window": wl.GEMMA3_STYLE.replace(n_heads=4, n_kv_heads=2, head_dim=256, sliding_window=64,
                                                       layer_kind=("local", "global")),
             "d64_g8": wl.SMOLLM2_135M.replace(n_heads=16, n_kv_heads=2, head_dim=64)}[shape]
