@@ -129,6 +129,8 @@ ATTN_CASES = [
     (1, 1100, 16, 8, 256, 1024), (1, 2048, 2, 1, 128, 0),
     # many heads: grids of 512 or more workgroups, as in the large forwards
     (2, 256, 128, 16, 64, 0), (1, 512, 128, 16, 128, 100), (1, 384, 176, 16, 256, 0),
+    # heads x 256-query blocks >= 512: two 32-query tiles per wavefront at D = 64
+    (4, 256, 128, 16, 64, 0), (2, 512, 128, 16, 128, 0), (2, 500, 128, 16, 128, 100),
 ]
 
 
