@@ -20,6 +20,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix (and vector) peak
 PEAK_HBM_GBS = 8000.0
 METRIC = "prefill tokens/s (Llama-3-8B shape, bf16); GEMM MFMA util vs peak"
 
@@ -312,14 +313,15 @@ def forward_flops(cfg, B, S):
 
 
 def configs_leg(fwd, steps, stream):
-    """The other forward configurations at their own shapes: the SmolLM2-shaped model
-    (30 layers, 1 x 512) and the Gemma3-style model (48 layers, 5 local : 1 global,
-    sandwich norms, softcap 30, 1 x 1024): ms per prefill (argmax only), tokens/s and
-    the fraction of the bf16 peak by algorithmic flops."""
+    """The other forward configurations at their own shapes: the tiny fp32 model (2
+    layers, 1 x 16), the SmolLM2-shaped model (30 layers, 1 x 512) and the Gemma3-style
+    model (48 layers, 5 local : 1 global, sandwich norms, softcap 30, 1 x 1024): ms per
+    prefill (argmax only), tokens/s and the fraction of the peak of the computing
+    dtype (fp32 matrix for the tiny model, bf16 otherwise) by algorithmic flops."""
     import torch
     from synth import workloads as wl
     out = {}
-    for cfg in (wl.SMOLLM2_135M, wl.GEMMA3_STYLE):
+    for cfg in (wl.TINY_F32, wl.SMOLLM2_135M, wl.GEMMA3_STYLE):
         B, S = cfg.batch, cfg.seq
         ids = wl.draw_ids(cfg)
         weights = {n: fwd.to_device(wl.draw_weight(cfg, n)) for n in wl.weight_shapes(cfg)}
@@ -341,10 +343,14 @@ def configs_leg(fwd, steps, stream):
         torch.cuda.empty_cache()
         fl = forward_flops(cfg, B, S)
         log(f"{cfg.name}: {ms:.3f} ms per prefill of {B} x {S}")
-        out[cfg.name] = {"batch": B, "seq": S, "ms_per_step": ms, "tokens_per_s": B * S / (ms * 1e-3),
-                         "algorithmic_tflop_per_step": fl / 1e12, "tflops": fl / (ms * 1e-3) / 1e12,
-                         "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                         "outputs": "argmax only"}
+        rec = {"batch": B, "seq": S, "ms_per_step": ms, "tokens_per_s": B * S / (ms * 1e-3),
+               "algorithmic_tflop_per_step": fl / 1e12, "tflops": fl / (ms * 1e-3) / 1e12,
+               "outputs": "argmax only"}
+        if cfg.dtype == "f32":
+            rec["frac_of_f32_peak"] = rec["tflops"] / PEAK_F32_TFLOPS
+        else:
+            rec["frac_of_bf16_peak"] = rec["tflops"] / PEAK_BF16_TFLOPS
+        out[cfg.name] = rec
     return out
 
 

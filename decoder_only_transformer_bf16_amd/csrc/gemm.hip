@@ -1213,17 +1213,22 @@ hipError_t launch_pp64(const void* X, const void* W, int M, int N, int K, const 
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ f32 VALU kernel
-// 64x64 output tile, 256 threads, 4x4 outputs per thread, K slices of 16.
+// ------------------------------------------------------------------ f32 kernel
+// fp32 products on the matrix cores (v_mfma_f32_32x32x2_f32): a 64 x 64 output tile
+// per workgroup, one 32 x 32 quarter per wavefront, K slices of 16 through LDS. The
+// tile returns through LDS so that the epilogue is called with the same (row, column
+// pair) per thread as everywhere else: 4 rows x 2 pairs per thread.
 template <class Epi>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ X, const float* __restrict__ W,
                                                       int M, int N, int K, Epi epi) {
   __shared__ float As[16][64 + 4];
   __shared__ float Bs[16][64 + 4];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  __shared__ float Cs[64][64 + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;  // this wavefront's 32 x 32 quarter of the tile
   const int nTN = (N + 63) / 64;
   const int m0 = (blockIdx.x / nTN) * 64, n0 = (blockIdx.x % nTN) * 64;
-  float acc[4][4] = {};
+  floatx16_t acc = floatx16_t{};
   for (int k0 = 0; k0 < K; k0 += 16) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -1232,20 +1237,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
       Bs[k][r] = (n0 + r < N && k0 + k < K) ? W[(int64_t)(n0 + r) * K + k0 + k] : 0.f;
     }
     __syncthreads();
+    // v_mfma_f32_32x32x2_f32: lane l holds row (A) / column (B) l % 32 at k = l / 32
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[k][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[k][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    for (int kk = 0; kk < 16; kk += 2) {
+      const float av = As[kk + (lane >> 5)][wm * 32 + (lane & 31)];
+      const float bv = Bs[kk + (lane >> 5)][wn * 32 + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
     }
     __syncthreads();
   }
+  // register r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+#pragma unroll
+  for (int r = 0; r < 16; ++r) Cs[wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][wn * 32 + (lane & 31)] = acc[r];
+  __syncthreads();
+  const int tx = tid & 15, ty = tid >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + ty * 4 + i;
@@ -1253,7 +1258,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 #pragma unroll
     for (int jp = 0; jp < 2; ++jp) {
       const int c = n0 + tx * 4 + 2 * jp;
-      epi.pair(row, c, acc[i][2 * jp], acc[i][2 * jp + 1], c < N, c + 1 < N);
+      epi.pair(row, c, Cs[ty * 4 + i][tx * 4 + 2 * jp], Cs[ty * 4 + i][tx * 4 + 2 * jp + 1], c < N, c + 1 < N);
     }
   }
 }
