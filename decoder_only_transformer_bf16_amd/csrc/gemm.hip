@@ -1279,7 +1279,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // re-arms the counter.
 constexpr int kSkUnroll = 8;     // K tiles per wavefront in flight
 constexpr int kSkUnrollNorm = 4; // the same with the normalised X operand (three times the loads)
-constexpr int kSkTarget = 448;   // workgroups a launch aims for (about one resident round)
+// Workgroups a launch aims for: about one resident round when X is normalised on the
+// fly (three times the loads per K tile), half that for a bf16 X, whose splits otherwise
+// spend more on the partial round trip than they save (interleaved decode steps of the
+// Llama shape: O 0.453 -> 0.412 ms and down 0.907 -> 0.856 ms per step at 224; QKV with
+// the fused norm 0.593 -> 0.697 ms, so it keeps 448).
+constexpr int kSkTarget = 448;
 constexpr int kSkMinTiles = 8;   // fewest K tiles per split
 constexpr int kSkWaves = 4;      // wavefronts per workgroup, each on every kSkWaves-th K tile
 
@@ -1291,11 +1296,11 @@ struct kHasSq<E, std::void_t<decltype(&E::template batch_sq<2>)>> : std::true_ty
 struct SkinnyPlan {
   int groups, nsplit, kps;  // 64-column groups, K splits, K tiles per split
 };
-SkinnyPlan skinny_plan(int N, int K) {
+SkinnyPlan skinny_plan(int N, int K, int target) {
   SkinnyPlan p;
   const int KT = K / 32;
   p.groups = (N + 63) / 64;
-  int ns = std::max(1, std::min((kSkTarget + p.groups - 1) / p.groups, KT / kSkMinTiles));
+  int ns = std::max(1, std::min((target + p.groups - 1) / p.groups, KT / kSkMinTiles));
   p.kps = (KT + ns - 1) / ns;
   p.nsplit = (KT + p.kps - 1) / p.kps;
   return p;
@@ -1520,7 +1525,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(XOp xop, con
 template <class XOp, class Epi>
 hipError_t launch_skinny(const XOp& xop, const void* W, int M, int N, int K, const Epi& epi, const SplitK& sk,
                          float* ssq_out, hipStream_t s) {
-  const SkinnyPlan p = skinny_plan(N, K);
+  const SkinnyPlan p = skinny_plan(N, K, std::is_same<XOp, XNorm>::value ? kSkTarget : kSkTarget / 2);
   const int MB = skinny_blocks(M);
   if (p.nsplit > 1 && ((int64_t)p.groups * p.nsplit * 16 * MB * 64 > sk.part_floats || p.groups > sk.count_len))
     return hipErrorInvalidValue;  // workspace sized for fewer rows or outputs
@@ -1628,7 +1633,7 @@ hipError_t gemm_grouped_store(const void* X, const void* W, float* Y, int N, int
 
 int64_t skinny_part_floats(int M, int N, int K) {
   if (M <= 0 || N <= 0 || K < 32) return 0;
-  const SkinnyPlan p = skinny_plan(N, K);
+  const SkinnyPlan p = skinny_plan(N, K, kSkTarget);  // the larger of the two split counts
   return p.nsplit > 1 ? (int64_t)p.groups * p.nsplit * 16 * skinny_blocks(std::min(M, kSkinnyRows)) * 64 : 0;
 }
 int64_t skinny_groups(int N) { return N > 0 ? (N + 63) / 64 : 0; }
