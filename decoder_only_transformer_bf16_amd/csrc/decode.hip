@@ -11,15 +11,18 @@
 // attention_decode is flash-decoding: the visible keys of a sequence are cut into
 // chunks of kDecodeChunk, one workgroup per (chunk, kv head, sequence) computes the
 // scores of all Hq / Hkv query heads that share the kv head, their chunk-local
-// softmax statistics and the chunk's share of P·V, all in fp32, and the chunks are
-// merged by rescaling to a common maximum. The work is HBM-bound: each cached key
-// and value is read once per step.
+// softmax statistics and the chunk's share of P·V, and the chunks are merged by
+// rescaling to a common maximum. The work is HBM-bound: each cached key and value is
+// read once per step.
 //
 // bf16 (at most 8 query heads per kv head): a wavefront reads its 64 keys and values
 // as 1 KiB pieces, D / 8 lanes per key row (16 bytes each), so every load is
 // contiguous; a lane's partial dot products are summed across its key's lanes with
 // DPP moves, and its share of P·V stays in registers until one LDS reduction. The
-// last workgroup of a (sequence, kv head) to finish merges the chunks itself. The
+// last workgroup of a (sequence, kv head) to finish merges the chunks itself. For
+// 128-wide heads in groups of 1, 2, 4 or 8 a kernel with the group size fixed at
+// compile time takes bf16 dot products (v_dot2) for the scores and for P·V, with the
+// probabilities rounded to bf16; the other bf16 shapes accumulate fp32 products. The
 // fp32 configuration (and wider groups) use a plain one-thread-per-key kernel and a
 // separate merge kernel.
 #include <algorithm>
