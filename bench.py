@@ -205,8 +205,9 @@ def moe_leg(fwd, steps, stream):
 
 def gemm_sweep_leg(fwd, stream, calls):
     """The standalone projection Y = X·Wᵀ over the [P, in, out] sweep (bf16 N(0, 1)
-    operands, fp32 output): per shape, the median of `calls` fwd_gemm launches, each
-    bracketed by HIP events on the stream the call runs on; TFLOP/s by algorithmic flops
+    operands, fp32 output): per shape, after ~0.2 s of warm-up calls, the median of
+    `calls` fwd_gemm launches, each bracketed by HIP events on the stream the call runs
+    on; TFLOP/s by algorithmic flops
     2 P in out, against the bf16 peak, and the achieved HBM rate by algorithmic bytes
     2 (P in + out in) + 4 P out."""
     import torch
@@ -218,8 +219,14 @@ def gemm_sweep_leg(fwd, stream, calls):
         del Xh, Wh
         Y = torch.empty((P, N), dtype=torch.float32, device="cuda")
         with torch.cuda.stream(stream):
-            for _ in range(3):
-                fwd.gemm(X, W, Y, stream=stream)
+            # the GPU idles while the operands are drawn on the host: warm up for ~0.2 s of
+            # calls (at least 3), so that the timed calls run at the steady-state clock
+            t0, n = time.perf_counter(), 0
+            while n < 3 or (time.perf_counter() - t0 < 0.2 and n < 5000):
+                for _ in range(8):
+                    fwd.gemm(X, W, Y, stream=stream)
+                n += 8
+                stream.synchronize()
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
             for a, b in ev:
                 a.record(stream)
