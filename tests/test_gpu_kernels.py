@@ -40,7 +40,9 @@ def _say(msg):
 
 # ------------------------------------------------------------------ GEMM
 SMALL_SHAPES = [tuple(s) for s in GOLD["gemm_shapes_P_in_out"]["value"]] + [
-    (1, 64, 96), (7, 576, 960), (300, 576, 576), (513, 1536, 3072), (100, 8, 24), (33, 4104, 200)]
+    (1, 64, 96), (7, 576, 960), (300, 576, 576), (513, 1536, 3072), (100, 8, 24), (33, 4104, 200),
+    # 320 tiles of 256 x 256 on the row-major 64-wide-slice kernel, ragged in rows, columns and K
+    (2000, 96, 10000)]
 
 
 @pytest.mark.parametrize("P,K,N", SMALL_SHAPES)
