@@ -91,7 +91,9 @@ def test_gemm_rejects_bad_arguments(fwd):
 
 # ------------------------------------------------------------------ RMSNorm
 @pytest.mark.parametrize("rows,H,dt", [(1, 64, "f32"), (37, 576, "bf16"), (300, 4096, "bf16"), (5, 3840, "bf16"),
-                                       (16, 64, "f32")])
+                                       (16, 64, "f32"),
+                                       # more rows than the capped grid has wavefronts: grid-stride rows
+                                       (9001, 576, "bf16")])
 def test_rmsnorm_matches_oracle(fwd, rows, H, dt):
     _say(f"rmsnorm rows={rows} H={H} {dt}")
     x = synth.normal(11, f"rms.x.{rows}.{H}", (rows, H), 1.5, "f32")
