@@ -9,7 +9,7 @@
 // problems (K-tiled operands: 32-wide K slices in four LDS stages; row-major ones:
 // 64-wide slices in two), a 128 x 128 software-pipelined kernel for small ones (with an
 // optional split of K over workgroups), and a split-K 16x16x32 kernel for few rows.
-// f32 path: an LDS-tiled VALU kernel (the fp32 configuration is tiny).
+// f32 path: v_mfma_f32_32x32x2_f32 on 64 x 64 tiles through LDS (the fp32 configuration is tiny).
 #include <algorithm>
 #include <mutex>
 #include <type_traits>
@@ -1548,7 +1548,9 @@ hipError_t launch_skinny(const XOp& xop, const void* W, int M, int N, int K, con
 }
 
 // ------------------------------------------------------------------ dispatch
-// The tiled kernels only (256 x 256 ping-pong tiles for large problems, else 128 x 128).
+// The tile kernels (no few-row path): 256 x 256 ping-pong tiles from 256 such tiles up
+// (32-wide slices on K-tiled operands, 64-wide on row-major ones), 128 x 128 tiles from 256
+// of those, 64 x 128 tiles below.
 template <class Epi>
 hipError_t launch_dense(const void* X, const void* W, int M, int N, int K, const Epi& epi, bool tiled, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
