@@ -91,7 +91,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+            raise ImportError(f"{LIB_PATH} is missing: build it with python -m decoder_only_transformer_bf16_amd._build")
         L = ctypes.CDLL(LIB_PATH)
         L.fwd_available.restype = c_i32
         L.fwd_create.argtypes = [ctypes.POINTER(FwdConfig), ctypes.POINTER(FwdWeights), c_vp, ctypes.POINTER(c_vp)]

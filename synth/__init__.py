@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "synth.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 _lib = None
 
-SEED_WEIGHTS = 7          # rand source 7 on the metalgemm page (Theorem 1 verdict)
+SEED_WEIGHTS = 7          # rand source 7 on the metalgemm page (Theorem 1)
 SEED_IDS = 99             # lcg seed 99, same passage
 SEED_GEMM = 0x1234567     # lcg seed 0x1234567, same passage
 WEIGHT_SIGMA = 0.02
