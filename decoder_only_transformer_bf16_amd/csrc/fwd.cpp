@@ -186,7 +186,8 @@ struct Geometry {
     int64_t f = 0;
     for (int64_t c = 1; c <= (T + 127) / 128; ++c) {
       const int M = (int)std::min(128 * c, T);
-      f = std::max({f, fwdk::dense_split_floats(M, (int)H, (int)(Hq * D)), fwdk::dense_split_floats(M, (int)H, (int)F)});
+      f = std::max({f, fwdk::dense_split_floats(M, (int)H, (int)(Hq * D), true),
+                    fwdk::dense_split_floats(M, (int)H, (int)F, true)});
     }
     return f;
   }
@@ -1026,7 +1027,7 @@ int fwd_gemm(const void* X, const void* W, float* Y, int32_t P, int32_t in, int3
   if (int rc = gemm_args(X, W, Y, P, in, out, dtype, &done)) return rc;
   if (done) return FWD_OK;
   const hipStream_t s = (hipStream_t)hip_stream;
-  fwdk::DenseSplit ds{nullptr, dtype == FWD_DTYPE_BF16 ? fwdk::dense_split_floats(P, out, in) : 0};
+  fwdk::DenseSplit ds{nullptr, dtype == FWD_DTYPE_BF16 ? fwdk::dense_split_floats(P, out, in, false) : 0};
   if (ds.part_floats > 0) {  // split partials, stream-ordered: concurrent calls on other streams do not share them
     hipMemPool_t pool = nullptr;
     HIP_TRY(split_pool(&pool));
@@ -1043,7 +1044,7 @@ int fwd_gemm_noalloc(const void* X, const void* W, float* Y, int32_t P, int32_t 
   bool done = false;
   if (int rc = gemm_args(X, W, Y, P, in, out, dtype, &done)) return rc;
   if (done) return FWD_OK;
-  const int64_t need = dtype == FWD_DTYPE_BF16 ? fwdk::dense_split_floats(P, out, in) : 0;
+  const int64_t need = dtype == FWD_DTYPE_BF16 ? fwdk::dense_split_floats(P, out, in, false) : 0;
   if (need > fwdk::kStaticSplitFloats)
     return fail(FWD_E_TOO_LARGE, "this product's split partials need " + std::to_string(need * 4) +
                                      " bytes; the static scratch holds " +

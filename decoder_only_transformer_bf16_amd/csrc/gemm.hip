@@ -826,9 +826,12 @@ struct PPCfg {
   static_assert((STAGES - 2) * LOADS < 64, "vmcnt range");
 };
 
-template <class C, class Epi, bool TILED, bool GROUPED = false>
+// SPLIT: workgroup b takes tile b % tiles over K slices [kps (b / tiles), + kps) and the
+// epilogue (a plain store) writes that range's fp32 partial tile at epi.Y + (b / tiles) M ldy.
+template <class C, class Epi, bool TILED, bool GROUPED = false, bool SPLIT = false>
 __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
-                                                        int M, int N, int K, Epi epi, GroupArgs grp = GroupArgs{}) {
+                                                        int M, int N, int K, Epi epi, GroupArgs grp = GroupArgs{},
+                                                        int kps = 0) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::STAGES, NW = C::NW;
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN, KS = C::KS;
   constexpr int SLICE = (BM + BN) * BK, LA = C::LOADS_A, LT = C::LOADS, FR = TM + TN;
@@ -839,20 +842,28 @@ __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict
   const int group = wave >> 2;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int nTN = (N + BN - 1) / BN;
-  int tm, tn, row0 = 0;
+  static_assert(!(SPLIT && GROUPED) && (!SPLIT || C::RS == 0), "split ranges: plain tiles, buffer->LDS route");
+  int tm, tn, row0 = 0, kt0 = 0;
   if constexpr (GROUPED) {
     if (!group_tile(grp, blockIdx.x, nTN, tm, tn, row0, M)) return;
     X += (int64_t)row0 * K;
     W += (int64_t)group_expert(grp, blockIdx.x / nTN) * grp.w_stride;
   } else {
-    tile_coords(blockIdx.x, (M + BM - 1) / BM, nTN, tm, tn);
+    int pid = blockIdx.x;
+    if constexpr (SPLIT) {
+      const int tiles = ((M + BM - 1) / BM) * nTN, sp = pid / tiles;
+      pid -= sp * tiles;
+      kt0 = sp * kps;
+      epi.Y += (int64_t)sp * M * epi.ldy;
+    }
+    tile_coords(pid, (M + BM - 1) / BM, nTN, tm, tn);
   }
   const int m0 = tm * BM, n0 = tn * BN;
   // (K-tiled operands are read in whole 16-row tiles: rows are padded to 16)
   const int mr = TILED ? (M + 15) / 16 * 16 : M, nr = TILED ? (N + 15) / 16 * 16 : N;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(X + (int64_t)m0 * K, (int64_t)min(BM, mr - m0) * K * 2);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + (int64_t)n0 * K, (int64_t)min(BN, nr - n0) * K * 2);
-  const int nk = (K + BK - 1) / BK;
+  const int nk = SPLIT ? min((K + BK - 1) / BK - kt0, kps) : (K + BK - 1) / BK;  // slices of this workgroup
   auto issue_load = [&](int p, bf16_t* buf, int k0) {
     if (p < LA) load_block<BK, TILED>(ra, buf, K, k0, wave + p * NW, lane);
     else load_block<BK, TILED>(rb, buf + BM * BK, K, k0, wave + (p - LA) * NW, lane);
@@ -909,7 +920,7 @@ __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict
     for (int q = 0; q < ST - 1; ++q)
       if (q < nk)
 #pragma unroll
-        for (int p = 0; p < LT; ++p) issue_load(p, lds + q * SLICE, q * BK);
+        for (int p = 0; p < LT; ++p) issue_load(p, lds + q * SLICE, (kt0 + q) * BK);
     if (nk >= ST - 1) wait_vmcnt<(ST - 2) * LT>();  // slice 0 has landed
     else wait_vmcnt<0>();
     lds_barrier();
@@ -922,7 +933,7 @@ __global__ __launch_bounds__(C::NT) void gemm_pp_kernel(const bf16_t* __restrict
       if (refill) {
         bf16_t* fill = lds + ((s + ST - 1) % ST) * SLICE;
 #pragma unroll
-        for (int p = 0; p < LT; ++p) issue_load(p, fill, (s + ST - 1) * BK);
+        for (int p = 0; p < LT; ++p) issue_load(p, fill, (kt0 + s + ST - 1) * BK);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // fragments in registers, buffer s % ST read
       if (group == 1) {  // this barrier ends an odd step: slice s + 1 must have landed
@@ -1183,6 +1194,7 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict
 // nsplit ranges of kps 32-wide K slices each (nsplit = 1: no split).
 struct DenseSplitPlan {
   int nsplit, kps;
+  bool big = false;  // ranges of 256 x 256 ping-pong tiles (K-tiled operands), else of 128 x 128 tiles
 };
 DenseSplitPlan split_ranges(int K, int ns) {
   const int nk = (K + 31) / 32;
@@ -1198,6 +1210,20 @@ hipError_t launch_split(const void* X, const void* W, int M, int N, int K, float
   const int tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
   hipLaunchKernelGGL((gemm_bf16_kernel<C, EpiStore<32>, TILED, true>), dim3(tiles * p.nsplit), dim3(C::NT), 0, s,
                      (const bf16_t*)X, (const bf16_t*)W, M, N, K, EpiStore<32>{part, N, 0.f}, p.kps);
+  const int64_t work = ((N & 3) == 0 && (ldy & 3) == 0) ? (int64_t)M * N / 4 : (int64_t)M * N;
+  const int blocks = (int)std::min<int64_t>((work + 255) / 256, 4096);
+  hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, (const float*)part, p.nsplit, M, N, Y, ldy,
+                     cap);
+  return hipGetLastError();
+}
+
+// The same over ranges of 256 x 256 ping-pong tiles (K-tiled operands).
+hipError_t launch_split_pp(const void* X, const void* W, int M, int N, int K, float* Y, int64_t ldy, float cap,
+                           float* part, const DenseSplitPlan& p, hipStream_t s) {
+  const int tiles = ((M + CfgBig::BM - 1) / CfgBig::BM) * ((N + CfgBig::BN - 1) / CfgBig::BN);
+  hipLaunchKernelGGL((gemm_pp_kernel<CfgBig, EpiStore<32>, true, false, true>), dim3(tiles * p.nsplit),
+                     dim3(CfgBig::NT), 0, s, (const bf16_t*)X, (const bf16_t*)W, M, N, K, EpiStore<32>{part, N, 0.f},
+                     GroupArgs{}, p.kps);
   const int64_t work = ((N & 3) == 0 && (ldy & 3) == 0) ? (int64_t)M * N / 4 : (int64_t)M * N;
   const int blocks = (int)std::min<int64_t>((work + 255) / 256, 4096);
   hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, (const float*)part, p.nsplit, M, N, Y, ldy,
@@ -1650,12 +1676,22 @@ namespace {
 // ranges on 64 x 128 tiles, less than the standalone product's stream-ordered
 // allocation of the partials costs (about 15 us per call).
 constexpr int kCUs = 256;
-DenseSplitPlan dense_split_plan(int M, int N, int K) {
+DenseSplitPlan dense_split_plan(int M, int N, int K, bool tiled) {
   const DenseSplitPlan none{1, 0};
   if (M <= 0 || N <= 0 || K <= 0) return none;
   const int64_t small = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
   const int nk = (K + 31) / 32;
   if (small >= 256 || nk < 256) return none;
+  const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  if (tiled && big >= 16) {
+    // About one round of 256 x 256 tiles over the ranges, each range at least 64 slices
+    // (the Gemma3-style down product, 1024 x 3840 over K 15360: 60 tiles x 4 ranges,
+    // 6.88 -> 5.60 ms over its 48 layers against 2 ranges of 128 x 128 tiles,
+    // interleaved in one process)
+    DenseSplitPlan p = split_ranges(K, (int)std::max<int64_t>(2, std::min<int64_t>(kCUs / big, nk / 64)));
+    p.big = true;
+    return p;
+  }
   const int ns = (int)std::min<int64_t>(std::max<int64_t>((2 * kCUs + small / 2) / small, 2), nk / 128);
   return split_ranges(K, ns);
 }
@@ -1684,8 +1720,8 @@ hipError_t static_split_scratch(float** ptr) {
   return hipSuccess;
 }
 
-int64_t dense_split_floats(int M, int N, int K) {
-  const DenseSplitPlan p = dense_split_plan(M, N, K);
+int64_t dense_split_floats(int M, int N, int K, bool tiled) {
+  const DenseSplitPlan p = dense_split_plan(M, N, K, tiled);
   return p.nsplit > 1 ? (int64_t)p.nsplit * M * N : 0;
 }
 
@@ -1693,10 +1729,11 @@ hipError_t gemm_store(DType dt, const void* X, const void* W, float* Y, int64_t 
                       float softcap, bool tiled, hipStream_t s, const SplitK* sk, const RowNormX* nx,
                       const DenseSplit* ds) {
   if (dt == DType::BF16 && ds && !nx && !(tiled && sk && M <= kSkinnyRows) && M > 0 && N > 0) {
-    const DenseSplitPlan p = dense_split_plan(M, N, K);
+    const DenseSplitPlan p = dense_split_plan(M, N, K, tiled);
     if (p.nsplit > 1) {
       if (tiled && K % 32) return hipErrorInvalidValue;
       if ((int64_t)p.nsplit * M * N > ds->part_floats || !ds->part) return hipErrorInvalidValue;
+      if (p.big) return launch_split_pp(X, W, M, N, K, Y, ldy, softcap, ds->part, p, s);
       return tiled ? launch_split<CfgSmall, true>(X, W, M, N, K, Y, ldy, softcap, ds->part, p, s)
                    : launch_split<CfgSmall, false>(X, W, M, N, K, Y, ldy, softcap, ds->part, p, s);
     }

@@ -43,12 +43,14 @@ struct RowNormX {
 };
 // Products with few output tiles and a long K are cut into K ranges whose fp32 partial
 // tiles a second launch adds in range order (deterministic) when `ds` holds room for
-// dense_split_floats(M, N, K) partials (bf16 only; 0 floats: the product is not split).
+// dense_split_floats(M, N, K, tiled) partials (bf16 only; 0 floats: the product is not
+// split). The plan depends on the operand layout: K-tiled products may take ranges of
+// 256 x 256 tiles, row-major ones take 128 x 128 tiles.
 struct DenseSplit {
   float* part;
   int64_t part_floats;
 };
-int64_t dense_split_floats(int M, int N, int K);
+int64_t dense_split_floats(int M, int N, int K, bool tiled);
 // For callers that cannot allocate: a static device array of kStaticSplitFloats floats
 // that serves as the split-K partial buffer. static_split_scratch gives its address on
 // the current device (looked up once per device). Calls that use it concurrently on one

@@ -127,6 +127,20 @@ def test_bf16_window_sandwich_small(fwd):
     model.close()
 
 
+def test_sandwich_split_products_on_large_tiles(fwd):
+    """Sandwich down products of 500 x 2048 over K = 8192: 16 tiles of 256 x 256, cut into
+    4 K ranges on the ping-pong kernel and added in range order."""
+    cfg = wl.SMOLLM2_135M.replace(n_layers=2, hidden=2048, n_heads=16, n_kv_heads=4, head_dim=128, ffn=8192,
+                                  vocab=4096, norm_placement="sandwich", seq=500, name="sandwich-2L-split")
+    _say("forward bf16 2-layer sandwich, down product split over K on 256 x 256 tiles, 1x500")
+    ids = wl.draw_ids(cfg)
+    model, got, ref = run_pair(fwd, cfg, ids)
+    check_parity(cfg, got, ref)
+    again = model.prefill(ids, logits=True, hidden=False, argmax=True)
+    assert np.array_equal(again["logits"].cpu().numpy(), got["logits"])  # ranges added in a fixed order
+    model.close()
+
+
 def test_batch_rows_independent_and_bitwise(fwd):
     cfg = wl.SMOLLM2_135M.replace(n_layers=4, batch=3, seq=80, name="smol-4L-batch")
     _say("forward bf16 batch independence 3x80")
