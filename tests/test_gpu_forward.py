@@ -128,9 +128,10 @@ def test_bf16_window_sandwich_small(fwd):
 
 
 def test_sandwich_split_products_on_large_tiles(fwd):
-    """Sandwich down products of 500 x 2048 over K = 8192: 16 tiles of 256 x 256, cut into
-    4 K ranges on the ping-pong kernel and added in range order."""
-    cfg = wl.SMOLLM2_135M.replace(n_layers=2, hidden=2048, n_heads=16, n_kv_heads=4, head_dim=128, ffn=8192,
+    """Sandwich down products of 500 x 2048 over K = 9024 (282 slices of 32): 16 tiles of
+    256 x 256, cut into K ranges of 71, 71, 71 and 69 slices on the ping-pong kernel and
+    added in range order."""
+    cfg = wl.SMOLLM2_135M.replace(n_layers=2, hidden=2048, n_heads=16, n_kv_heads=4, head_dim=128, ffn=9024,
                                   vocab=4096, norm_placement="sandwich", seq=500, name="sandwich-2L-split")
     _say("forward bf16 2-layer sandwich, down product split over K on 256 x 256 tiles, 1x500")
     ids = wl.draw_ids(cfg)
