@@ -282,3 +282,26 @@ def test_qwen3moe_hybrid_dense_sparse(hf, k, norm):
     if k > 1:
         assert _compare(cfg.replace(moe_norm_topk=not norm), w, ids, logits, hidden)[0] > TEETH
     assert _compare(cfg.replace(n_experts_per_tok=k + 1), w, ids, logits, hidden)[0] > TEETH
+
+
+def test_greedy_matches_hf_generate(hf):
+    """The oracle's greedy continuation (repeated cacheless forwards) against HF's
+    greedy generate, which runs through HF's own key/value cache."""
+    torch, _ = hf
+    cfg = BASE.replace(seq=8)
+    # value, output and FFN matrices 10x larger: at N(0, 0.02^2) the embedding dominates
+    # the residual stream and every row would just repeat its last token
+    w = {n: a * np.float32(10.0) if n.rsplit(".", 1)[-1] in ("wv", "wo", "w_gate", "w_up", "w_down") else a
+         for n, a in _weights(cfg).items()}
+    ids = wl.draw_ids(cfg)
+    model = _build(hf, "LlamaForCausalLM", "LlamaConfig", _llama_state(cfg, w), **_geometry(cfg),
+                   head_dim=cfg.head_dim, hidden_act="silu",
+                   rope_parameters={"rope_type": "default", "rope_theta": cfg.rope_theta})
+    toks, logits = oracle.greedy(cfg, w, ids, 6)
+    top2 = np.sort(logits, axis=-1)[..., -2:]
+    assert np.min(top2[..., 1] - top2[..., 0]) > 1e-4            # no near tie at any step
+    assert len(np.unique(toks)) > 6                              # a continuation, not a repeated token
+    with torch.no_grad():
+        out = model.generate(torch.from_numpy(np.asarray(ids, np.int64)), max_new_tokens=6, do_sample=False,
+                             pad_token_id=0, eos_token_id=None)
+    assert np.array_equal(out[:, ids.shape[1]:].numpy(), toks)
