@@ -305,3 +305,20 @@ def test_greedy_matches_hf_generate(hf):
         out = model.generate(torch.from_numpy(np.asarray(ids, np.int64)), max_new_tokens=6, do_sample=False,
                              pad_token_id=0, eos_token_id=None)
     assert np.array_equal(out[:, ids.shape[1]:].numpy(), toks)
+
+
+def test_llama_family_at_the_smollm2_shape(hf):
+    """The SmolLM2-135M-shaped config itself (30 layers, hidden 576, 9 / 3 heads of 64,
+    FFN 1536, vocab 49152), with its own bf16 synthetic weights widened to float32 as
+    the oracle reads them, over 1 x 24 tokens."""
+    cfg = wl.SMOLLM2_135M.replace(seq=24)
+    w = {n: np.asarray(wl.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a, np.float32)
+         for n, a in wl.draw_all(cfg).items()}
+    ids = wl.draw_ids(cfg)
+    model = _build(hf, "LlamaForCausalLM", "LlamaConfig", _llama_state(cfg, w), **_geometry(cfg),
+                   head_dim=cfg.head_dim, hidden_act="silu",
+                   rope_parameters={"rope_type": "default", "rope_theta": cfg.rope_theta})
+    logits, hidden = _run(hf, model, ids)
+    err, o = _compare(cfg, w, ids, logits, hidden)
+    assert err < TOL, err
+    assert np.array_equal(o["argmax"], np.argmax(logits, axis=-1))
